@@ -1,0 +1,271 @@
+"""Plain, slow fp64 CPU oracle of the speculative-decoding verify pass.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module.  It shares
+no code with the HIP library (no kernels, headers, helpers or tables) and never
+imports it; the only module both sides use is the seeded input generator, which
+holds none of the method's arithmetic.
+
+What it computes, and the passages it follows (pages quoted by title):
+
+* "mlx-dspark" wiki summary, section "Architecture", first bullet: each round
+  runs the target forward over the anchor plus m draft tokens in one pass,
+  compares the draft with the target's own logits and commits the longest
+  accepted prefix; greedy output equals plain decoding, and temperature > 0 is
+  an exact sample through the Leviathan/Chen rule min(1, p/q).
+* Same page, "Key techniques" (auto-calibration bullet): a round commits
+  1 + sum p^i tokens in expectation, i.e. the accepted drafts plus one token of
+  the target's own; "Design decisions": a miss costs a plain one-token forward.
+* Same page, "Key techniques" (custom kernels bullet): the verify kernel
+  dequantises each weight group once and reuses it for every row -- the
+  arithmetic is the plain dequantise-then-matmul below.
+* "mlx-dspark 0.7.0" project page, "How it works": the output matches plain
+  decoding except where rounding breaks a tie; with temperature > 0 the
+  committed tokens are an exact sample of the target at temperature T.
+* "mlx-dspark releases", v0.0.2 notes: the sampling path was validated to give
+  exactly the target's output distribution.
+
+Readings where the pages are silent (quantisation format, packing, tie rule,
+the extra committed token, strictness of the accept test, residual with zero
+mass, inverse-CDF rule) are listed in the design notes and restated at each
+function below.
+
+Every function works in float64 on exactly the values the storage formats hold
+(bf16 activations, fp16 scales/biases, integer codes), so the matmul result is
+exact up to fp64 rounding (relative error of order K * 2**-53).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 64
+
+
+# ------------------------------------------------------------------ decoders
+def decode_fp16(bits) -> np.ndarray:
+    """IEEE binary16 bit patterns -> float64 (exact)."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def decode_bf16(bits) -> np.ndarray:
+    """bfloat16 bit patterns -> float64 (exact): the upper half of a float32."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):     # signalling-NaN patterns widen to NaN
+        return u.view(np.float32).astype(np.float64)
+
+
+# ------------------------------------------------------------- O1: unpacking
+def unpack_codes(codes, bits: int, k: int) -> np.ndarray:
+    """Integer codes ``[N][K]`` from packed words ``uint32[N][K*bits/32]``.
+
+    Reading of the (unstated) packing: LSB-first, 32/bits codes per word, so
+    code k of a row sits in word k // (32/bits) at bit offset
+    bits * (k mod 32/bits).
+    """
+    if bits not in (4, 8):
+        raise ValueError("unpack_codes: bits must be 4 or 8")
+    per = 32 // bits
+    words = np.asarray(codes, dtype=np.uint32)
+    n = words.shape[0]
+    if words.shape[1] * per != k:
+        raise ValueError("unpack_codes: packed width does not match K")
+    mask = np.uint32((1 << bits) - 1)
+    q = np.empty((n, k), dtype=np.int64)
+    for slot in range(per):
+        q[:, slot::per] = (words >> np.uint32(bits * slot)) & mask
+    return q
+
+
+# --------------------------------------------------------------- O2: dequant
+def dequantize(codes, scales, biases, bits: int, n: int, k: int) -> np.ndarray:
+    """Weight matrix ``W[N][K]`` in float64.
+
+    Affine group quantisation (reading of "quantized" / "weight group" in the
+    wiki summary's "Key techniques"): w[n,k] = s[n, k//64] * q[n,k] + b[n, k//64]
+    with fp16 scale s and bias b per 64-wide group along K.  ``bits == 16`` is
+    the unquantised bf16 control: ``codes`` holds bf16 bit patterns [N][K].
+    """
+    if bits == 16:
+        return decode_bf16(codes).reshape(n, k)
+    if k % GROUP:
+        raise ValueError("dequantize: K must be a multiple of 64")
+    q = unpack_codes(codes, bits, k).astype(np.float64)
+    s = decode_fp16(scales).reshape(n, k // GROUP)
+    b = decode_fp16(biases).reshape(n, k // GROUP)
+    g = np.arange(k) // GROUP
+    return s[:, g] * q + b[:, g]
+
+
+# ---------------------------------------------------------------- O3: linear
+def qlinear(x_bf16, codes, scales, biases, bits: int, n: int, k: int) -> np.ndarray:
+    """Verify-pass projection y[M][N] = x[M][K] . W[N][K]^T in float64.
+
+    The M rows are the anchor plus the drafts ("mlx-dspark" wiki summary,
+    "Architecture"): every row goes through the same dequantised weights.
+    """
+    x = decode_bf16(x_bf16)
+    x = x.reshape(-1, k)
+    w = dequantize(codes, scales, biases, bits, n, k)
+    return x @ w.T
+
+
+# ------------------------------------------------------ O4: argmax and margin
+def argmax_lowest(z) -> tuple[np.ndarray, np.ndarray]:
+    """Per-row argmax with the lowest index on ties, and the top-2 margin.
+
+    The target's greedy token is the argmax of its own logits.  The project page
+    ("mlx-dspark 0.7.0", "How it works") allows the output to differ from plain
+    decoding only where floating-point rounding breaks a tie, and leaves the tie
+    rule open -- the reading taken is the lowest index.  A NaN counts as
+    the maximum (the first NaN wins), so a row holding a NaN never reports a
+    finite token silently.
+
+    margin[m] = z[m, t] - max over v != t of z[m, v]  (NaN if the row holds a
+    NaN; +inf when V == 1).
+    """
+    z = np.asarray(z, dtype=np.float64)
+    t = np.argmax(z, axis=1)
+    rows = np.arange(z.shape[0])
+    top = z[rows, t]
+    if z.shape[1] == 1:
+        return t.astype(np.int32), np.full(z.shape[0], np.inf)
+    rest = z.copy()
+    rest[rows, t] = -np.inf
+    margin = top - rest.max(axis=1)
+    margin[np.isnan(z).any(axis=1)] = np.nan
+    return t.astype(np.int32), margin
+
+
+def lmhead_argmax(h_bf16, codes, scales, biases, bits: int, v: int, hdim: int):
+    """Target logits z[M][V] = h . W_lm^T, their argmax and top-2 margin."""
+    z = qlinear(h_bf16, codes, scales, biases, bits, v, hdim)
+    t, margin = argmax_lowest(z)
+    return z, t, margin
+
+
+# -------------------------------------------------------- O5: greedy accept
+def accept_greedy(target_ids, draft_ids) -> tuple[np.ndarray, np.ndarray]:
+    """Longest accepted prefix plus the target's own token, per request.
+
+    target_ids ``[B][M]``: row j's greedy token (row 0 reads the anchor, row j
+    reads draft j-1).  draft_ids ``[B][M-1]``.  Draft j is accepted while it
+    equals row j's token; at the first mismatch (or after all M-1 drafts) the
+    target's token of that row is committed ("Architecture": commit the longest
+    accepted prefix; "Key techniques": 1 + sum p^i tokens per round).
+
+    Returns accept_len ``[B]`` = number of committed tokens (accepted drafts
+    + 1, so 1..M) and committed ``[B][M]`` padded with -1.
+    """
+    t = np.atleast_2d(np.asarray(target_ids, dtype=np.int64))
+    d = np.atleast_2d(np.asarray(draft_ids, dtype=np.int64))
+    bsz, m_rows = t.shape
+    if d.shape != (bsz, m_rows - 1):
+        raise ValueError("accept_greedy: draft_ids must be [B][M-1]")
+    accept_len = np.zeros(bsz, dtype=np.int32)
+    committed = np.full((bsz, m_rows), -1, dtype=np.int32)
+    for b in range(bsz):
+        a = 0
+        while a < m_rows - 1 and d[b, a] == t[b, a]:
+            a += 1
+        committed[b, :a] = d[b, :a]
+        committed[b, a] = t[b, a]
+        accept_len[b] = a + 1
+    return accept_len, committed
+
+
+def sequential_greedy(target_ids, draft_ids) -> list[int]:
+    """What plain one-token-at-a-time greedy decoding emits from the same rows.
+
+    Decoding emits row j's token; row j+1 was computed on input d_j, so it is
+    a valid next step only while the emitted token equals d_j.  Emission stops
+    after the first token that differs from its draft, or after the last row.
+    Independent formulation of the invariant "greedy output equals plain
+    decoding" ("Architecture", "How it works").
+    """
+    t = list(np.asarray(target_ids, dtype=np.int64).ravel())
+    d = list(np.asarray(draft_ids, dtype=np.int64).ravel())
+    out = []
+    for j, tok in enumerate(t):
+        out.append(int(tok))
+        if j == len(t) - 1 or tok != d[j]:
+            break
+    return out
+
+
+# ---------------------------------------------------- O6: stochastic accept
+def softmax_t(z, temperature: float) -> np.ndarray:
+    """p = softmax(z / T) in float64 with max-subtraction (one row)."""
+    a = np.asarray(z, dtype=np.float64) / float(temperature)
+    a = a - a.max()
+    e = np.exp(a)
+    return e / e.sum()
+
+
+def inverse_cdf(weights, threshold: float) -> int:
+    """Index-order inverse CDF on non-negative weights.
+
+    Reading: inclusive prefix sums C_v in index order; the sample is the first
+    v with C_v > threshold (threshold = u * total).  If rounding leaves no such
+    v, the last v with positive weight is taken.
+    """
+    w = np.asarray(weights, dtype=np.float64)
+    c = np.cumsum(w)
+    hit = np.nonzero(c > threshold)[0]
+    if hit.size:
+        return int(hit[0])
+    pos = np.nonzero(w > 0)[0]
+    return int(pos[-1]) if pos.size else w.size - 1
+
+
+def accept_sample(logits, q, draft_ids, uniforms, temperature: float):
+    """Leviathan/Chen speculative sampling over one verify block.
+
+    logits ``[M][V]`` (row j is the target's distribution after input j),
+    q ``[M-1][V]`` the drafter's distributions, draft_ids ``[M-1]``, uniforms
+    ``[M]``: u_j decides draft j, u_{M-1} is the single final draw.
+
+    p_j = softmax(z_j / T).  For j = 0 .. M-2: accept d_j iff
+    u_j * q_j(d_j) < p_j(d_j)  (equals u_j < min(1, p/q) for q > 0; q(d) = 0
+    with p(d) > 0 accepts).  At the first reject j, sample from the residual
+    r = max(0, p_j - q_j) with threshold u_{M-1} * sum(r); if the residual has no
+    mass (possible only through rounding), sample from p_j instead.  If every
+    draft is accepted, sample the bonus token from p_{M-1}
+    ("Architecture": exact sample via min(1, p/q); "How it works": exact sample
+    from the target at temperature T; v0.0.2 release notes: validated to equal
+    the target's distribution).
+
+    Data faults -- T <= 0 or non-finite, a non-finite logit, a non-finite or
+    negative q, a uniform outside [0, 1), a draft id outside [0, V) -- return
+    accept_len = -1 and all -1 committed ids.
+
+    Returns (accept_len = committed count 1..M, committed ``[M]`` padded -1).
+    """
+    z = np.asarray(logits, dtype=np.float64)
+    m_rows, v = z.shape
+    qq = np.asarray(q, dtype=np.float64).reshape(m_rows - 1, v)
+    d = np.asarray(draft_ids, dtype=np.int64).ravel()
+    u = np.asarray(uniforms, dtype=np.float64).ravel()
+    committed = np.full(m_rows, -1, dtype=np.int32)
+    bad = (not np.isfinite(temperature) or temperature <= 0
+           or not np.isfinite(z).all()
+           or not np.isfinite(qq).all() or (qq < 0).any()
+           or not np.isfinite(u).all() or (u < 0).any() or (u >= 1).any()
+           or (d < 0).any() or (d >= v).any())
+    if bad:
+        return -1, committed
+    final_u = u[m_rows - 1]
+    for j in range(m_rows - 1):
+        p = softmax_t(z[j], temperature)
+        if u[j] * qq[j, d[j]] < p[d[j]]:
+            committed[j] = d[j]
+            continue
+        r = np.maximum(0.0, p - qq[j])
+        mass = r.sum()
+        if not mass > 0:
+            r = p
+            mass = p.sum()
+        committed[j] = inverse_cdf(r, final_u * mass)
+        return j + 1, committed
+    p = softmax_t(z[m_rows - 1], temperature)
+    committed[m_rows - 1] = inverse_cdf(p, final_u * p.sum())
+    return m_rows, committed

@@ -1,0 +1,188 @@
+"""Pins for the oracle's dequantise-then-matmul (O2/O3) and argmax (O4).
+
+* exact rational arithmetic (fractions.Fraction) on tiny shapes, from values
+  decoded by the bit-field decoder, not by the oracle's decoders;
+* s = 1, b = 0 reduces to an integer matmul, exact in int64;
+* bits = 16 reduces to numpy's matmul of the bf16 values;
+* all-ones activations give sum over groups of (s * sum q + 64 b);
+* hand-worked cases from tests/golden;
+* argmax: brute force with many ties, NaN rows, and the margin.
+Non-square shapes (M != N != K) make a transposed operand fail.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from speculative_decoding_verify_dspk_amd import inputs
+from fieldcodec import decode_fields as _decode_fields
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")
+
+
+def _exact_linear(x_bits, w):
+    """y = x . W^T with Fractions (and sum |terms|); values from the bit-field decoder."""
+    m, k = x_bits.shape
+    x = [[Fraction(_decode_fields(int(b), 8, 7)) for b in row] for row in x_bits]
+    q = w.codes_u8.astype(int)
+    s = [[Fraction(_decode_fields(int(b), 5, 10)) for b in row] for row in w.scales]
+    bb = [[Fraction(_decode_fields(int(b), 5, 10)) for b in row] for row in w.biases]
+    y, yabs = [], []
+    for i in range(m):
+        row, rabs = [], []
+        for n in range(w.n):
+            acc, aabs = Fraction(0), Fraction(0)
+            for kk in range(k):
+                g = kk // 64
+                term = x[i][kk] * (s[n][g] * int(q[n, kk]) + bb[n][g])
+                acc += term
+                aabs += abs(term)
+            row.append(acc)
+            rabs.append(aabs)
+        y.append(row)
+        yabs.append(rabs)
+    return y, yabs
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_qlinear_exact_rational(bits):
+    m, n, k = 2, 3, 192
+    w = inputs.make_qweight(n, k, bits, "exact-pin")
+    x = inputs.make_activations(m, k, "exact-pin")
+    got = oracle.qlinear(x, w.codes, w.scales, w.biases, bits, n, k)
+    ref, ref_abs = _exact_linear(x, w)
+    for i in range(m):
+        for j in range(n):
+            # dequantise (one rounding), product and a K-term sum in fp64:
+            # |error| <= (K + 2) * 2^-53 * sum_k |x_k w_k| (standard bound)
+            assert abs(Fraction(got[i, j]) - ref[i][j]) <= Fraction(k + 2, 2 ** 53) * ref_abs[i][j], (i, j)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_qlinear_integer_reduction(bits):
+    """s = 1, b = 0 and small-integer x: the product is an exact integer matmul."""
+    m, n, k = 5, 7, 256
+    g = np.random.default_rng(11)
+    codes = g.integers(0, 1 << bits, size=(n, k), dtype=np.uint8)
+    xi = g.integers(-8, 9, size=(m, k))
+    x_bits = inputs.f32_to_bf16_bits(xi.astype(np.float32))
+    one = np.full((n, k // 64), 0x3C00, np.uint16)   # fp16 1.0
+    zero = np.zeros((n, k // 64), np.uint16)
+    y = oracle.qlinear(x_bits, inputs.pack_codes(codes, bits), one, zero, bits, n, k)
+    assert np.array_equal(y, (xi.astype(np.int64) @ codes.astype(np.int64).T).astype(np.float64))
+
+
+def test_qlinear_bf16_control_is_plain_matmul():
+    m, n, k = 3, 5, 128
+    w = inputs.make_qweight(n, k, 16, "bf16-pin")
+    x = inputs.make_activations(m, k, "bf16-pin")
+    wf = inputs.bf16_bits_to_f32(w.codes).astype(np.float64)
+    xf = inputs.bf16_bits_to_f32(x).astype(np.float64)
+    y = oracle.qlinear(x, w.codes, None, None, 16, n, k)
+    assert np.allclose(y, np.matmul(xf, wf.T), rtol=1e-13, atol=1e-12)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_qlinear_all_ones(bits):
+    n, k = 9, 320
+    w = inputs.make_qweight(n, k, bits, "ones-pin")
+    x = np.full((1, k), 0x3F80, np.uint16)   # bf16 1.0
+    y = oracle.qlinear(x, w.codes, w.scales, w.biases, bits, n, k)[0]
+    q = w.codes_u8.astype(np.int64).reshape(n, k // 64, 64).sum(axis=2)
+    s = np.array([[_decode_fields(int(b), 5, 10) for b in r] for r in w.scales])
+    b = np.array([[_decode_fields(int(v), 5, 10) for v in r] for r in w.biases])
+    expect = (s * q + 64 * b).sum(axis=1)
+    assert np.allclose(y, expect, rtol=1e-14, atol=1e-12)
+
+
+def _golden_weight(case):
+    n, k, bits = case["n"], case["k"], case["bits"]
+    kk = np.arange(k)
+    if case["codes"].startswith("row 0"):
+        codes = np.stack([kk, 255 - kk]).astype(np.uint8)
+    else:
+        codes = np.tile(kk % 16, (n, 1)).astype(np.uint8)
+    s = inputs.f32_to_fp16_bits(np.array(case["scales"], np.float32))
+    b = inputs.f32_to_fp16_bits(np.array(case["biases"], np.float32))
+    return inputs.pack_codes(codes, bits), s, b
+
+
+def test_qlinear_golden_hand_cases():
+    cases = json.load(open(GOLDEN))["qlinear"]
+    # case 0: one row of ones
+    c = cases[0]
+    words, s, b = _golden_weight(c)
+    x = np.full((1, c["k"]), 0x3F80, np.uint16)
+    y = oracle.qlinear(x, words, s, b, c["bits"], c["n"], c["k"])
+    assert np.array_equal(y, np.array(c["expected_y"]))
+    # case 1: two rows with group-dependent values
+    c = cases[1]
+    words, s, b = _golden_weight(c)
+    k = c["k"]
+    xr0 = np.where(np.arange(k) < 64, 1.0, 0.5).astype(np.float32)
+    xr1 = -np.ones(k, np.float32)
+    x = inputs.f32_to_bf16_bits(np.stack([xr0, xr1]))
+    y = oracle.qlinear(x, words, s, b, c["bits"], c["n"], c["k"])
+    assert np.array_equal(y, np.array(c["expected_y"]))
+
+
+def test_qlinear_group_index_is_along_k():
+    """A scale on group 1 only must change only the contribution of k in [64, 128)."""
+    n, k = 2, 256
+    codes = np.ones((n, k), np.uint8)
+    s = np.full((n, k // 64), 0x3C00, np.uint16)
+    s[:, 1] = 0x4000   # 2.0
+    zero = np.zeros((n, k // 64), np.uint16)
+    x = np.zeros((1, k), np.float32)
+    x[0, 70] = 1.0
+    y = oracle.qlinear(inputs.f32_to_bf16_bits(x), inputs.pack_codes(codes, 8), s, zero, 8, n, k)
+    assert np.array_equal(y, [[2.0, 2.0]])
+    x[0, 70] = 0.0
+    x[0, 1] = 1.0
+    y = oracle.qlinear(inputs.f32_to_bf16_bits(x), inputs.pack_codes(codes, 8), s, zero, 8, n, k)
+    assert np.array_equal(y, [[1.0, 1.0]])
+
+
+# ------------------------------------------------------------------ argmax
+def _brute_argmax(row):
+    best = 0
+    for v in range(1, len(row)):
+        if np.isnan(row[best]):
+            break
+        if np.isnan(row[v]) or row[v] > row[best]:
+            best = v
+    return best
+
+
+def test_argmax_brute_force_with_ties():
+    g = np.random.default_rng(5)
+    z = g.integers(-3, 4, size=(400, 9)).astype(np.float64)   # many ties
+    t, margin = oracle.argmax_lowest(z)
+    for i, row in enumerate(z):
+        b = _brute_argmax(row)
+        assert t[i] == b
+        others = [row[v] for v in range(len(row)) if v != b]
+        assert margin[i] == row[b] - max(others)
+
+
+def test_argmax_nan_and_golden():
+    z = np.array([[1.0, np.nan, 5.0, np.nan]])
+    t, margin = oracle.argmax_lowest(z)
+    assert t[0] == 1 and np.isnan(margin[0])
+    for c in json.load(open(GOLDEN))["argmax"]:
+        t, margin = oracle.argmax_lowest(np.array([c["z"]]))
+        assert t[0] == c["t"]
+        assert margin[0] == (np.inf if c["margin"] == "inf" else c["margin"])
+
+
+def test_lmhead_argmax_consistent():
+    w = inputs.make_qweight(300, 128, 8, "lmhead-pin")
+    h = inputs.make_activations(4, 128, "lmhead-pin")
+    z, t, margin = oracle.lmhead_argmax(h, w.codes, w.scales, w.biases, 8, 300, 128)
+    assert z.shape == (4, 300)
+    for i in range(4):
+        assert t[i] == _brute_argmax(z[i])
+        assert margin[i] > 0
