@@ -1,0 +1,209 @@
+"""Benchmark of the verify pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config qwen3-4b]
+
+Workload (default): one Qwen3-4B-shaped decoder layer (q 4096x2560, k/v
+1024x2560, o 2560x4096, gate/up 9728x2560, down 2560x9728) plus the
+151936x2560 vocabulary head, 8-bit affine group-64 weights, bf16 N(0,1) rows,
+greedy acceptance of drafts that match the target's token with probability
+0.7 per position.  One step = one verify round at each width
+M = 1, 2, 4, 6, 8, 12, 16 (the verify-cost curve); each round is
+  4 projection launches + head/argmax + greedy accept + one D2H copy and sync.
+
+Printed: one JSON line with the whole-job weight-GB/s (weight bytes of every
+round / wall time), the per-width curve t(M)/t(1), the roofline of the
+dominant kernel (the vocabulary head), and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+SWEEP = (1, 2, 4, 6, 8, 12, 16)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="qwen3-4b", choices=["qwen3-4b", "dense-27b", "ornith-9b"])
+    ap.add_argument("--bits", type=int, default=8)
+    ap.add_argument("--copies", type=int, default=3, help="rotating weight copies (defeat the 256 MB MALL)")
+    ap.add_argument("--sweep", default=",".join(map(str, SWEEP)))
+    ap.add_argument("--layers", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-s", type=float, default=20.0)
+    return ap.parse_args()
+
+
+def cpu_baseline(model: str, bits: int, m: int, budget_s: float):
+    """The oracle, as it stands, on one verify round of the same workload:
+    every projection of one layer at width m, then as many 8192-entry slices
+    of the vocabulary head as fit the time budget.  Reported in weight-GB/s."""
+    import oracle
+    from speculative_decoding_verify_dspk_amd import inputs
+    shapes = inputs.LAYER_SHAPES[model]
+    threads = len(os.sched_getaffinity(0))
+    done_bytes, t_total = 0, 0.0
+    projs = inputs.layer_projections(model)
+    acts = {}
+    for name, n, k, src in projs:
+        w = inputs.make_qweight(n, k, bits, "cpu-baseline", model, name, keep_codes=False)
+        x = acts.setdefault((src, k), inputs.make_activations(m, k, "cpu-baseline", src))
+        t0 = time.perf_counter()
+        oracle.qlinear(x, w.codes, w.scales, w.biases, bits, n, k)
+        t_total += time.perf_counter() - t0
+        done_bytes += inputs.weight_bytes(n, k, bits)
+    v, h = shapes["vocab"], shapes["hidden"]
+    hx = inputs.make_activations(m, h, "cpu-baseline", "h")
+    slices = 0
+    sl = 8192
+    while t_total < budget_s and slices * sl < v:
+        n = min(sl, v - slices * sl)
+        w = inputs.make_qweight(n, h, bits, "cpu-baseline", "head", slices, keep_codes=False)
+        t0 = time.perf_counter()
+        z = oracle.qlinear(hx, w.codes, w.scales, w.biases, bits, n, h)
+        oracle.argmax_lowest(z)
+        t_total += time.perf_counter() - t0
+        done_bytes += inputs.weight_bytes(n, h, bits)
+        slices += 1
+    return {"value": round(done_bytes / t_total / 1e9, 4), "unit": "weight-GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"one {model} layer (7 projections) + {slices} x {sl}-row slices of the {v}x{h} head, "
+                      f"{bits}-bit, M={m}; {done_bytes / 1e6:.1f} MB of weights in {t_total:.1f} s "
+                      f"(numpy fp64, {threads} threads)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only (the verify pass is not sharded); "
+              "use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from speculative_decoding_verify_dspk_amd import binding, inputs
+    from speculative_decoding_verify_dspk_amd.verify_round import VerifyStack
+
+    binding.lib()   # fail loudly if the HIP library is missing
+    sweep = [int(s) for s in args.sweep.split(",")]
+    max_m = max(sweep)
+    stack = VerifyStack(args.config, args.layers, args.bits, max_m, copies=args.copies)
+    stream = torch.cuda.current_stream()
+    V = stack.vocab
+
+    # untimed pre-pass: target ids per width, then drafts with a 0.7 match rate
+    drafts, acc = {}, {}
+    for m in sweep:
+        stack.launch_head(m, 0, stream=stream)
+        t = stack.argmax[:m].cpu().numpy()[None, :]
+        d = inputs.drafts_match_rate(t, 0.7, V, "bench", args.config, m) if m > 1 else np.zeros((1, 0), np.int32)
+        drafts[m] = torch.from_numpy(np.ascontiguousarray(d, dtype=np.int32)).cuda() if m > 1 else None
+        acc[m] = (torch.empty((1,), dtype=torch.int32, device="cuda"),
+                  torch.empty((1, m), dtype=torch.int32, device="cuda"))
+    host_len = torch.empty((1,), dtype=torch.int32).pin_memory()
+    host_com = torch.empty((1, max_m), dtype=torch.int32).pin_memory()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
+    rounds = {m: 0 for m in sweep}
+
+    def run_round(m: int, copy: int, record: list | None):
+        e = [ev() for _ in range(4)] if record is not None else None
+        if e: e[0].record(stream)
+        stack.launch_layers(m, copy, stream)
+        if e: e[1].record(stream)
+        stack.launch_head(m, copy, stream=stream)
+        if e: e[2].record(stream)
+        binding.accept_greedy(stack.argmax, drafts[m], 1, m, acc[m][0], acc[m][1], stream)
+        host_len.copy_(acc[m][0], non_blocking=True)
+        host_com[:, :m].copy_(acc[m][1], non_blocking=True)
+        if e: e[3].record(stream)
+        stream.synchronize()       # the round's one device sync
+        if record is not None:
+            record.append((m, e))
+
+    step_copy = 0
+    for _ in range(args.warmup):
+        for m in sweep:
+            run_round(m, step_copy % args.copies, None)
+            step_copy += 1
+
+    records = []
+    committed = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for m in sweep:
+            run_round(m, step_copy % args.copies, records)
+            committed += int(host_len[0])
+            step_copy += 1
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    layer_b = stack.layer_weight_bytes() * args.layers
+    head_b = stack.head_weight_bytes()
+    round_b = layer_b + head_b
+    n_rounds = args.steps * len(sweep)
+    value = round_b * n_rounds / wall / 1e9
+
+    # per-width device times from the events (median over steps)
+    curve = {}
+    head_ms_all, head_bytes_all = [], []
+    for m in sweep:
+        rs = [e for (mm, e) in records if mm == m]
+        t_round = np.median([e[0].elapsed_time(e[3]) for e in rs])
+        t_layer = np.median([e[0].elapsed_time(e[1]) for e in rs])
+        t_head = [e[1].elapsed_time(e[2]) for e in rs]
+        head_ms_all += t_head
+        head_bytes_all += [head_b + m * stack.hidden * 2 + m * 4] * len(t_head)
+        curve[m] = {"round_us": round(float(t_round) * 1e3, 2), "layer_us": round(float(t_layer) * 1e3, 2),
+                    "head_us": round(float(np.median(t_head)) * 1e3, 2),
+                    "weight_GBps": round(round_b / (t_round * 1e-3) / 1e9, 1),
+                    "hbm_frac": round(round_b / (t_round * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    t1 = curve[sweep[0]]["round_us"]
+    for m in sweep:
+        curve[m]["t_over_t1"] = round(curve[m]["round_us"] / t1, 4)
+
+    head_avg_s = float(np.mean(head_ms_all)) * 1e-3
+    head_bytes = float(np.mean(head_bytes_all))
+    achieved = head_bytes / head_avg_s / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "qgemm_kernel<8,1,4,true> (vocabulary head + argmax)",
+                "avg_launch_us": round(head_avg_s * 1e6, 2), "bytes_per_launch": int(head_bytes)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.config, args.bits, 8, args.cpu_sample_s)
+
+    out = {
+        "metric": "verify weight-GB/s & % HBM peak vs width M=1..16; t(M)/t(1) cost curve",
+        "value": round(value, 1), "unit": "weight-GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.config} layer x{args.layers} + lm_head {V}x{stack.hidden}, "
+                               f"{args.bits}-bit g64, greedy alpha=0.7, one round per M in {sweep}",
+                   "widths": sweep, "weight_bytes_per_round": round_b, "rotating_copies": args.copies},
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "t16_over_t1": curve[sweep[-1]]["t_over_t1"],
+        "curve": curve,
+        "rounds_per_s": round(n_rounds / wall, 1),
+        "rows_per_s": round(sum(sweep) * args.steps / wall, 1),
+        "committed_tokens_per_round": round(committed / n_rounds, 3),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "device": torch.cuda.get_device_name(0), "host": platform.node(),
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,209 @@
+/*
+ * dspk.h -- C ABI of the MI355X (gfx950) verify pass of lossless speculative
+ * decoding.
+ *
+ * One verify round, as the "mlx-dspark" wiki summary describes it (section
+ * "Architecture", first bullet): the target model runs once over the anchor
+ * token plus m draft tokens, the drafts are compared with the target's own
+ * logits, and the longest accepted prefix is committed.  Greedy rounds give
+ * exactly what plain decoding gives; with temperature > 0 the Leviathan/Chen
+ * rule min(1, p/q) makes the committed tokens an exact sample of the target.
+ *
+ * The library computes the data-parallel part of that round:
+ *   dspk_qgemm_verify   - every projection of the target over the M = m + 1
+ *                         rows, through affine group-quantised weights;
+ *   dspk_lmhead_argmax  - the vocabulary projection fused with the row argmax;
+ *   dspk_accept_greedy  - longest matching prefix plus the target's token;
+ *   dspk_accept_sample  - min(1, p/q) acceptance with residual resampling.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every data pointer is DEVICE memory (hipMalloc / torch) owned by the
+ *   caller.  The library never allocates, frees or synchronises; every call
+ *   only enqueues kernels on `stream` (a hipStream_t, NULL = default stream)
+ *   and returns.  Results are valid once the stream reaches that point.
+ * - Return value: DSPK_OK (0) on success, a negative DSPK_E* code otherwise;
+ *   dspk_last_error() then holds a message (thread-local).  Nothing is
+ *   enqueued when a call fails its argument checks.  There is no fallback
+ *   path and no clamping of bad arguments.
+ * - Faults that depend on data values (non-finite logits, bad uniforms, draft
+ *   ids out of range) cannot be seen on the host without a sync; the
+ *   acceptance kernels report them on the device (accept_len = -1).
+ * - Calls that share a workspace must be ordered on one stream.
+ */
+#ifndef DSPK_H
+#define DSPK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSPK_OK            0
+#define DSPK_EINVAL      (-1) /* null / misaligned pointer, bad size or stride  */
+#define DSPK_EUNSUPPORTED (-2) /* valid request outside what the kernels handle */
+#define DSPK_EDEVICE     (-3) /* HIP launch error                              */
+
+#define DSPK_F32  0           /* y / logits element type: float32              */
+#define DSPK_BF16 1           /* y element type: bfloat16 (round to nearest even) */
+
+#define DSPK_GROUP     64     /* quantisation group width along K              */
+#define DSPK_MAX_ROWS  32     /* largest M (anchor + drafts, or B requests x rows) */
+#define DSPK_MAX_GROUPED 4    /* most weights in one grouped call              */
+
+/*
+ * One weight matrix W[n][k] (out features x in features).
+ *
+ * bits 4 or 8 -- affine group quantisation, w[r][c] = s[r][c/64] * q[r][c] +
+ *   b[r][c/64], the plain reading of the pages' "quantised" target weights
+ *   with per-group parameters ("mlx-dspark" wiki summary, "Key techniques",
+ *   custom kernels bullet):
+ *     codes  : uint32[n][k*bits/32], codes packed LSB-first (code c of a row
+ *              sits in word c/(32/bits) at bit bits*(c mod 32/bits)),
+ *              unsigned 0 .. 2^bits-1;
+ *     scales : IEEE binary16 [n][k/64], row-major;
+ *     biases : IEEE binary16 [n][k/64], row-major.
+ * bits 16 -- unquantised bfloat16 control: codes = bf16[n][k], scales and
+ *   biases must be NULL.
+ * group must be 64; k must be a multiple of 64; codes must be 16-byte
+ * aligned; scales/biases 4-byte aligned.  The struct itself is host memory.
+ */
+typedef struct dspk_qweight {
+    int32_t n;
+    int32_t k;
+    int32_t bits;
+    int32_t group;
+    const void *codes;
+    const uint16_t *scales;
+    const uint16_t *biases;
+} dspk_qweight;
+
+/* Library version: major*10000 + minor*100 + patch. */
+int dspk_version(void);
+
+/* Message for the last non-zero return on this thread ("" if none). */
+const char *dspk_last_error(void);
+
+/*
+ * Workspace for dspk_qgemm_verify: bytes needed for a weight of n x k read by
+ * m rows (0 when the kernel needs none).  The first 256 bytes... are split-K
+ * counters: the workspace must be zero-filled before its FIRST use; every
+ * completed call leaves it zero-filled again, so it can be reused as is.
+ */
+size_t dspk_qgemm_workspace_bytes(int32_t n, int32_t k, int32_t m);
+
+/*
+ * Verify-pass projection: y[i][c] = sum_r x[i][r] * w[c][r] for the M rows
+ * i < m (anchor plus drafts), fp32 accumulation.  Each weight group is read
+ * from HBM and dequantised once per call and reused for all M rows -- the
+ * pages' point that verifying m extra rows must not re-read the weights per
+ * row ("mlx-dspark" wiki summary, "Key techniques", custom kernels bullet;
+ * the 1-bit counter-example in "mlx-dspark 0.7.0", "PrismML Bonsai 27B").
+ *
+ *   w         : weight descriptor (see dspk_qweight).
+ *   x         : bf16 activations [m][ldx], ldx >= k, ldx % 8 == 0, 16-byte aligned.
+ *   m         : rows, 1 .. DSPK_MAX_ROWS.
+ *   y         : output [m][ldy], element type y_dtype (DSPK_F32 | DSPK_BF16),
+ *               ldy >= n; 4-byte aligned.
+ *   workspace : >= dspk_qgemm_workspace_bytes(n, k, m) bytes (may be NULL when
+ *               that is 0), 256-byte aligned, zero-filled before first use.
+ * Errors: DSPK_EINVAL (null or misaligned pointer, n < 1, k % 64, ldx/ldy,
+ * m out of 1..32, workspace too small), DSPK_EUNSUPPORTED (bits not in
+ * {4, 8, 16}, group != 64), DSPK_EDEVICE.
+ */
+int dspk_qgemm_verify(const dspk_qweight *w, const uint16_t *x, int64_t ldx, int32_t m,
+                      void *y, int32_t y_dtype, int64_t ldy,
+                      void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Grouped form for weights that read the same rows (q/k/v, gate/up): one
+ * launch for `count` (1 .. DSPK_MAX_GROUPED) weights with equal k and bits.
+ * y[g] is the output of w[g] with leading dimension ldy[g].  The workspace is
+ * the sum of dspk_qgemm_workspace_bytes over the weights.  Same results,
+ * bit for bit, as `count` separate dspk_qgemm_verify calls.
+ */
+int dspk_qgemm_verify_grouped(int32_t count, const dspk_qweight *w,
+                              const uint16_t *x, int64_t ldx, int32_t m,
+                              void *const *y, int32_t y_dtype, const int64_t *ldy,
+                              void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace for dspk_lmhead_argmax (zero-filled before first use, left zeroed). */
+size_t dspk_lmhead_workspace_bytes(int32_t v, int32_t m);
+
+/*
+ * Target logits and greedy tokens: z[i][c] = sum_r h[i][r] * w_lm[c][r] over
+ * the vocabulary c < v = w->n, and argmax[i] = the smallest c with z[i][c]
+ * equal to the row maximum (a NaN counts as the maximum).  These are the
+ * target's own tokens that the drafts are compared with ("mlx-dspark" wiki
+ * summary, "Architecture").  The tie rule is the reading taken where the
+ * project page leaves ties to floating-point rounding.
+ *
+ *   w         : vocabulary head, same format as dspk_qgemm_verify, k <= 8192.
+ *   h         : bf16 [m][ldh] final hidden rows (16-byte aligned, ldh % 8 == 0).
+ *   argmax    : int32 [m] output.
+ *   logits    : float32 [m][ldl] output, or NULL to skip writing logits.
+ *   workspace : >= dspk_lmhead_workspace_bytes(v, m), 256-byte aligned,
+ *               zero-filled before first use.
+ * The result is deterministic (independent of workgroup order).
+ */
+int dspk_lmhead_argmax(const dspk_qweight *w, const uint16_t *h, int64_t ldh, int32_t m,
+                       int32_t *argmax, float *logits, int64_t ldl,
+                       void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Greedy acceptance for b requests of m_rows rows each ("mlx-dspark" wiki
+ * summary, "Architecture": commit the longest accepted prefix; "Key
+ * techniques": a round commits 1 + sum p^i tokens, i.e. always the target's
+ * own token after the accepted drafts).
+ *
+ *   target_ids : int32 [b][m_rows]   row j's greedy token (from dspk_lmhead_argmax)
+ *   draft_ids  : int32 [b][m_rows-1] draft j is compared with row j
+ *   accept_len : int32 [b] output, committed tokens per request (1 .. m_rows)
+ *   committed  : int32 [b][m_rows] output: accepted drafts, then the target's
+ *                token of the first mismatching row (or the last row), then -1.
+ * b >= 1, 1 <= m_rows <= DSPK_MAX_ROWS.  A target id < 0 (an argmax that
+ * could not be formed) makes that request's accept_len -1.
+ */
+int dspk_accept_greedy(const int32_t *target_ids, const int32_t *draft_ids,
+                       int32_t b, int32_t m_rows,
+                       int32_t *accept_len, int32_t *committed, void *stream);
+
+/* Workspace for dspk_accept_sample (zero-filled before first use, left zeroed). */
+size_t dspk_sample_workspace_bytes(int32_t v, int32_t m_rows);
+
+/*
+ * Stochastic acceptance (Leviathan/Chen; "mlx-dspark" wiki summary,
+ * "Architecture"; "mlx-dspark 0.7.0", "How it works": an exact sample of the
+ * target at temperature T).  p_j = softmax(z_j / T).  For j = 0 .. m_rows-2
+ * draft j is accepted iff u_j * q_j(d_j) < p_j(d_j); at the first reject the
+ * token is drawn from norm(max(0, p_j - q_j)) (from p_j if that has no mass)
+ * with u_{m_rows-1}; if all drafts pass, the bonus token is drawn from
+ * p_{m_rows-1} with u_{m_rows-1}.  Draws are index-order inverse CDFs: the
+ * first c whose inclusive prefix sum exceeds u * total.
+ *
+ *   logits   : float32 [m_rows][ldz] target logits (v columns used)
+ *   q        : float32 [m_rows-1][ldq] draft distributions (used as given)
+ *   draft_ids: int32 [m_rows-1]
+ *   uniforms : float32 [m_rows]: u_j for draft j, the last one for the final draw
+ *   temperature > 0 and finite.
+ *   accept_len : int32 [1] output (committed count, 1 .. m_rows; -1 on a data
+ *                fault: non-finite logit, non-finite or negative q, uniform
+ *                outside [0, 1), draft id outside [0, v));
+ *   committed  : int32 [m_rows] output, padded with -1 (all -1 on a fault).
+ *   workspace  : >= dspk_sample_workspace_bytes(v, m_rows), 256-byte aligned,
+ *                zero-filled before first use.
+ * 2 <= m_rows <= DSPK_MAX_ROWS, v >= 1.
+ */
+int dspk_accept_sample(const float *logits, int64_t ldz,
+                       const float *q, int64_t ldq, const int32_t *draft_ids,
+                       const float *uniforms, int32_t m_rows, int32_t v, float temperature,
+                       int32_t *accept_len, int32_t *committed,
+                       void *workspace, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPK_H */

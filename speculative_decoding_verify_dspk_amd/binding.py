@@ -1,0 +1,196 @@
+"""Thin ctypes binding of libdspk.so (argument marshalling only).
+
+Every function takes torch tensors that live in HIP device memory, passes their
+addresses and sizes to the C entry point of the same name, and raises
+``DspkError`` on a non-zero return.  No arithmetic of the verify pass happens
+here; the library must be built (``python -m
+speculative_decoding_verify_dspk_amd.build``) -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from ctypes import c_float, c_int32, c_int64, c_size_t, c_void_p
+
+import numpy as np
+
+from . import inputs
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdspk.so")
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "dspk.h")
+
+DSPK_F32, DSPK_BF16 = 0, 1
+MAX_ROWS = 32
+MAX_GROUPED = 4
+
+
+class DspkError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"dspk error {code}: {msg}")
+        self.code = code
+
+
+class QWeightDesc(ctypes.Structure):
+    _fields_ = [("n", c_int32), ("k", c_int32), ("bits", c_int32), ("group", c_int32),
+                ("codes", c_void_p), ("scales", c_void_p), ("biases", c_void_p)]
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdspk.so once; raise if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m speculative_decoding_verify_dspk_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    sig = {
+        "dspk_version": (c_int32, []),
+        "dspk_last_error": (ctypes.c_char_p, []),
+        "dspk_qgemm_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
+        "dspk_qgemm_verify": (c_int32, [P(QWeightDesc), c_void_p, c_int64, c_int32, c_void_p, c_int32,
+                                        c_int64, c_void_p, c_size_t, c_void_p]),
+        "dspk_qgemm_verify_grouped": (c_int32, [c_int32, P(QWeightDesc), c_void_p, c_int64, c_int32,
+                                                P(c_void_p), c_int32, P(c_int64), c_void_p, c_size_t,
+                                                c_void_p]),
+        "dspk_lmhead_workspace_bytes": (c_size_t, [c_int32, c_int32]),
+        "dspk_lmhead_argmax": (c_int32, [P(QWeightDesc), c_void_p, c_int64, c_int32, c_void_p, c_void_p,
+                                         c_int64, c_void_p, c_size_t, c_void_p]),
+        "dspk_accept_greedy": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
+                                         c_void_p]),
+        "dspk_sample_workspace_bytes": (c_size_t, [c_int32, c_int32]),
+        "dspk_accept_sample": (c_int32, [c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_void_p, c_int32,
+                                         c_int32, c_float, c_void_p, c_void_p, c_void_p, c_size_t,
+                                         c_void_p]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _LIB = L
+    return L
+
+
+def header_symbols() -> list[str]:
+    """Names of the functions include/dspk.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(dspk_[a-z_0-9]+)\s*\(", text)))
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise DspkError(rc, lib().dspk_last_error().decode())
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _rows(t, name: str) -> int:
+    """Leading dimension of a row-major 2-D tensor (unit column stride)."""
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name}: expected a 2-D tensor with unit column stride")
+    return t.stride(0)
+
+
+# ---------------------------------------------------------------- weights
+class DeviceQWeight:
+    """A weight matrix in device memory plus its C descriptor."""
+
+    def __init__(self, n: int, k: int, bits: int, codes, scales=None, biases=None):
+        self.n, self.k, self.bits = n, k, bits
+        self.codes, self.scales, self.biases = codes, scales, biases
+        self.desc = QWeightDesc(n, k, bits, 64, codes.data_ptr(),
+                                None if scales is None else scales.data_ptr(),
+                                None if biases is None else biases.data_ptr())
+
+    @classmethod
+    def upload(cls, w: inputs.QWeight, device="cuda"):
+        import torch
+        codes = torch.from_numpy(np.ascontiguousarray(w.codes.view(np.int32) if w.bits != 16
+                                                      else w.codes.view(np.int16))).to(device)
+        sc = bi = None
+        if w.bits != 16:
+            sc = torch.from_numpy(np.ascontiguousarray(w.scales.view(np.int16))).to(device)
+            bi = torch.from_numpy(np.ascontiguousarray(w.biases.view(np.int16))).to(device)
+        return cls(w.n, w.k, w.bits, codes, sc, bi)
+
+    @property
+    def nbytes(self) -> int:
+        b = self.codes.numel() * self.codes.element_size()
+        if self.scales is not None:
+            b += 2 * self.scales.numel() * self.scales.element_size()
+        return b
+
+
+# ------------------------------------------------------------ entry points
+def version() -> int:
+    return lib().dspk_version()
+
+
+def qgemm_workspace_bytes(n: int, k: int, m: int) -> int:
+    return lib().dspk_qgemm_workspace_bytes(n, k, m)
+
+
+def lmhead_workspace_bytes(v: int, m: int) -> int:
+    return lib().dspk_lmhead_workspace_bytes(v, m)
+
+
+def sample_workspace_bytes(v: int, m_rows: int) -> int:
+    return lib().dspk_sample_workspace_bytes(v, m_rows)
+
+
+def alloc_workspace(nbytes: int, device="cuda"):
+    """Zero-filled workspace (the library keeps it zeroed between calls)."""
+    import torch
+    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def qgemm_verify(w: DeviceQWeight, x, m: int, y, workspace=None, stream=None) -> None:
+    ldx, ldy = _rows(x, "x"), _rows(y, "y")
+    dt = DSPK_BF16 if y.element_size() == 2 else DSPK_F32
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    _check(lib().dspk_qgemm_verify(ctypes.byref(w.desc), x.data_ptr(), ldx, m, y.data_ptr(), dt, ldy,
+                                   _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def qgemm_verify_grouped(ws: list, x, m: int, ys: list, workspace=None, stream=None) -> None:
+    cnt = len(ws)
+    descs = (QWeightDesc * cnt)(*[w.desc for w in ws])
+    yptr = (c_void_p * cnt)(*[y.data_ptr() for y in ys])
+    ldy = (c_int64 * cnt)(*[_rows(y, "y") for y in ys])
+    dt = DSPK_BF16 if ys[0].element_size() == 2 else DSPK_F32
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    _check(lib().dspk_qgemm_verify_grouped(cnt, descs, x.data_ptr(), _rows(x, "x"), m, yptr, dt, ldy,
+                                           _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def lmhead_argmax(w: DeviceQWeight, h, m: int, argmax, logits=None, workspace=None, stream=None) -> None:
+    ldl = 0 if logits is None else _rows(logits, "logits")
+    _check(lib().dspk_lmhead_argmax(ctypes.byref(w.desc), h.data_ptr(), _rows(h, "h"), m, argmax.data_ptr(),
+                                    _ptr(logits), ldl, _ptr(workspace),
+                                    0 if workspace is None else workspace.numel(), _stream(stream)))
+
+
+def accept_greedy(target_ids, draft_ids, b: int, m_rows: int, accept_len, committed, stream=None) -> None:
+    _check(lib().dspk_accept_greedy(target_ids.data_ptr(), _ptr(draft_ids), b, m_rows, accept_len.data_ptr(),
+                                    committed.data_ptr(), _stream(stream)))
+
+
+def accept_sample(logits, q, draft_ids, uniforms, m_rows: int, v: int, temperature: float, accept_len,
+                  committed, workspace=None, stream=None) -> None:
+    _check(lib().dspk_accept_sample(logits.data_ptr(), _rows(logits, "logits"), q.data_ptr(), _rows(q, "q"),
+                                    draft_ids.data_ptr(), uniforms.data_ptr(), m_rows, v, float(temperature),
+                                    accept_len.data_ptr(), committed.data_ptr(), _ptr(workspace),
+                                    0 if workspace is None else workspace.numel(), _stream(stream)))

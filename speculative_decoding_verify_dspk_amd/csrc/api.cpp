@@ -1,0 +1,240 @@
+// C ABI of the verify-pass library: argument checks, work planning and
+// launches.  Every entry point validates everything it can see on the host
+// before enqueuing anything; nothing here allocates, frees or synchronises.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/dspk.h"
+#include "dspk_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok() {
+    g_err.clear();
+    return DSPK_OK;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_weight(const dspk_qweight *w, const char *who) {
+    if (w == nullptr) return fail(DSPK_EINVAL, "%s: weight descriptor is NULL", who);
+    if (w->bits != 4 && w->bits != 8 && w->bits != 16)
+        return fail(DSPK_EUNSUPPORTED, "%s: bits=%d (supported: 4, 8, 16)", who, w->bits);
+    if (w->group != DSPK_GROUP) return fail(DSPK_EUNSUPPORTED, "%s: group=%d (must be 64)", who, w->group);
+    if (w->n < 1) return fail(DSPK_EINVAL, "%s: n=%d must be >= 1", who, w->n);
+    if (w->k < DSPK_GROUP || w->k % DSPK_GROUP)
+        return fail(DSPK_EINVAL, "%s: k=%d must be a positive multiple of 64", who, w->k);
+    if (w->codes == nullptr || !aligned(w->codes, 16))
+        return fail(DSPK_EINVAL, "%s: codes must be a non-NULL 16-byte aligned device pointer", who);
+    if (w->bits == 16) {
+        if (w->scales != nullptr || w->biases != nullptr)
+            return fail(DSPK_EINVAL, "%s: bf16 weights take no scales or biases", who);
+    } else {
+        if (w->scales == nullptr || w->biases == nullptr)
+            return fail(DSPK_EINVAL, "%s: scales and biases are required for bits=%d", who, w->bits);
+        if (!aligned(w->scales, 4) || !aligned(w->biases, 4))
+            return fail(DSPK_EINVAL, "%s: scales and biases must be 4-byte aligned", who);
+    }
+    return DSPK_OK;
+}
+
+int check_rows(const uint16_t *x, int64_t ldx, int32_t m, int32_t k, const char *who) {
+    if (m < 1 || m > DSPK_MAX_ROWS) return fail(DSPK_EINVAL, "%s: m=%d out of 1..%d", who, m, DSPK_MAX_ROWS);
+    if (x == nullptr || !aligned(x, 16))
+        return fail(DSPK_EINVAL, "%s: activations must be a non-NULL 16-byte aligned device pointer", who);
+    if (ldx < k || ldx % 8) return fail(DSPK_EINVAL, "%s: ldx=%lld must be >= k=%d and a multiple of 8", who,
+                                        (long long)ldx, k);
+    return DSPK_OK;
+}
+
+int launch_result(hipError_t e, const char *who) {
+    if (e != hipSuccess) return fail(DSPK_EDEVICE, "%s: launch failed: %s", who, hipGetErrorString(e));
+    return ok();
+}
+
+int qgemm_common(int32_t count, const dspk_qweight *w, const uint16_t *x, int64_t ldx, int32_t m,
+                 void *const *y, int32_t y_dtype, const int64_t *ldy, void *workspace, size_t ws_bytes,
+                 void *stream, const char *who) {
+    if (count < 1 || count > DSPK_MAX_GROUPED)
+        return fail(DSPK_EINVAL, "%s: count=%d out of 1..%d", who, count, DSPK_MAX_GROUPED);
+    if (w == nullptr || y == nullptr || ldy == nullptr) return fail(DSPK_EINVAL, "%s: NULL array argument", who);
+    if (y_dtype != DSPK_F32 && y_dtype != DSPK_BF16)
+        return fail(DSPK_EINVAL, "%s: y_dtype=%d (DSPK_F32 or DSPK_BF16)", who, y_dtype);
+    for (int i = 0; i < count; ++i) {
+        int rc = check_weight(&w[i], who);
+        if (rc) return rc;
+        if (w[i].k != w[0].k || w[i].bits != w[0].bits)
+            return fail(DSPK_EINVAL, "%s: grouped weights must share k and bits", who);
+        if (y[i] == nullptr || !aligned(y[i], 4)) return fail(DSPK_EINVAL, "%s: y[%d] NULL or misaligned", who, i);
+        if (ldy[i] < w[i].n) return fail(DSPK_EINVAL, "%s: ldy[%d]=%lld < n=%d", who, i, (long long)ldy[i], w[i].n);
+    }
+    int rc = check_rows(x, ldx, m, w[0].k, who);
+    if (rc) return rc;
+
+    dspk::GemmLaunch L{};
+    L.x = x;
+    L.ldx = ldx;
+    L.count = count;
+    L.m = m;
+    L.y_bf16 = y_dtype == DSPK_BF16;
+    size_t need = 0;
+    int grid = 0;
+    for (int i = 0; i < count; ++i) {
+        const dspk::GemmPlan pl = dspk::plan_gemm(w[i].n, w[i].k, m, w[i].bits, false);
+        dspk::GemmProblem &P = L.p[i];
+        P.codes = w[i].codes;
+        P.scales = w[i].scales;
+        P.biases = w[i].biases;
+        P.y = y[i];
+        P.ldy = ldy[i];
+        P.n = w[i].n;
+        P.k = w[i].k;
+        P.ncb = pl.ncb;
+        P.splits = pl.splits;
+        P.wave_groups = pl.wave_groups;
+        P.wg_begin = grid;
+        if (pl.ws_bytes) {
+            char *base = (char *)workspace + need;
+            P.counters = (uint32_t *)base;
+            P.partial = (float *)(base + ((size_t)pl.ncb * 4 + 255) / 256 * 256);
+        }
+        need += pl.ws_bytes;
+        grid += pl.ncb * pl.splits;
+    }
+    if (need > 0) {
+        if (workspace == nullptr || !aligned(workspace, 256))
+            return fail(DSPK_EINVAL, "%s: workspace of %zu bytes required (256-byte aligned)", who, need);
+        if (ws_bytes < need) return fail(DSPK_EINVAL, "%s: workspace %zu bytes < %zu required", who, ws_bytes, need);
+    }
+    return launch_result(dspk::launch_qgemm(L, w[0].bits, grid, (hipStream_t)stream), who);
+}
+
+}  // namespace
+
+extern "C" {
+
+int dspk_version(void) { return 100; }
+
+const char *dspk_last_error(void) { return g_err.c_str(); }
+
+size_t dspk_qgemm_workspace_bytes(int32_t n, int32_t k, int32_t m) {
+    if (n < 1 || k < DSPK_GROUP || k % DSPK_GROUP || m < 1 || m > DSPK_MAX_ROWS) return 0;
+    return dspk::plan_gemm(n, k, m, 8, false).ws_bytes;
+}
+
+int dspk_qgemm_verify(const dspk_qweight *w, const uint16_t *x, int64_t ldx, int32_t m, void *y,
+                      int32_t y_dtype, int64_t ldy, void *workspace, size_t ws_bytes, void *stream) {
+    void *ys[1] = {y};
+    int64_t lds[1] = {ldy};
+    return qgemm_common(1, w, x, ldx, m, ys, y_dtype, lds, workspace, ws_bytes, stream, "dspk_qgemm_verify");
+}
+
+int dspk_qgemm_verify_grouped(int32_t count, const dspk_qweight *w, const uint16_t *x, int64_t ldx, int32_t m,
+                              void *const *y, int32_t y_dtype, const int64_t *ldy, void *workspace,
+                              size_t ws_bytes, void *stream) {
+    return qgemm_common(count, w, x, ldx, m, y, y_dtype, ldy, workspace, ws_bytes, stream,
+                        "dspk_qgemm_verify_grouped");
+}
+
+size_t dspk_lmhead_workspace_bytes(int32_t v, int32_t m) {
+    (void)v;
+    (void)m;
+    return 512;   // keys [32] x 8 bytes, then the arrival counter
+}
+
+int dspk_lmhead_argmax(const dspk_qweight *w, const uint16_t *h, int64_t ldh, int32_t m, int32_t *argmax,
+                       float *logits, int64_t ldl, void *workspace, size_t ws_bytes, void *stream) {
+    const char *who = "dspk_lmhead_argmax";
+    int rc = check_weight(w, who);
+    if (rc) return rc;
+    if (w->k > dspk::kMaxWGGroups * 64)
+        return fail(DSPK_EUNSUPPORTED, "%s: k=%d above the supported %d", who, w->k, dspk::kMaxWGGroups * 64);
+    rc = check_rows(h, ldh, m, w->k, who);
+    if (rc) return rc;
+    if (argmax == nullptr || !aligned(argmax, 4)) return fail(DSPK_EINVAL, "%s: argmax NULL or misaligned", who);
+    if (logits != nullptr && (!aligned(logits, 4) || ldl < w->n))
+        return fail(DSPK_EINVAL, "%s: logits misaligned or ldl=%lld < v=%d", who, (long long)ldl, w->n);
+    if (workspace == nullptr || !aligned(workspace, 256) || ws_bytes < dspk_lmhead_workspace_bytes(w->n, m))
+        return fail(DSPK_EINVAL, "%s: workspace of %zu bytes required (256-byte aligned)", who,
+                    dspk_lmhead_workspace_bytes(w->n, m));
+    const dspk::GemmPlan pl = dspk::plan_gemm(w->n, w->k, m, w->bits, true);
+    dspk::GemmLaunch L{};
+    L.x = h;
+    L.ldx = ldh;
+    L.count = 1;
+    L.m = m;
+    L.argmax = argmax;
+    L.logits = logits;
+    L.ldl = ldl;
+    L.keys = (unsigned long long *)workspace;
+    L.done = (uint32_t *)((char *)workspace + 256);
+    dspk::GemmProblem &P = L.p[0];
+    P.codes = w->codes;
+    P.scales = w->scales;
+    P.biases = w->biases;
+    P.n = w->n;
+    P.k = w->k;
+    P.ncb = pl.ncb;
+    P.splits = 1;
+    P.wave_groups = pl.wave_groups;
+    P.wg_begin = 0;
+    return launch_result(dspk::launch_lmhead(L, w->bits, pl.ncb, (hipStream_t)stream), who);
+}
+
+int dspk_accept_greedy(const int32_t *target_ids, const int32_t *draft_ids, int32_t b, int32_t m_rows,
+                       int32_t *accept_len, int32_t *committed, void *stream) {
+    const char *who = "dspk_accept_greedy";
+    if (b < 1) return fail(DSPK_EINVAL, "%s: b=%d must be >= 1", who, b);
+    if (m_rows < 1 || m_rows > DSPK_MAX_ROWS)
+        return fail(DSPK_EINVAL, "%s: m_rows=%d out of 1..%d", who, m_rows, DSPK_MAX_ROWS);
+    if (target_ids == nullptr || accept_len == nullptr || committed == nullptr)
+        return fail(DSPK_EINVAL, "%s: NULL pointer", who);
+    if (m_rows > 1 && draft_ids == nullptr) return fail(DSPK_EINVAL, "%s: draft_ids is NULL", who);
+    return launch_result(
+        dspk::launch_accept_greedy(target_ids, draft_ids, b, m_rows, accept_len, committed, (hipStream_t)stream),
+        who);
+}
+
+size_t dspk_sample_workspace_bytes(int32_t v, int32_t m_rows) {
+    if (v < 1 || m_rows < 1) return 0;
+    return dspk::sample_workspace_bytes(v, m_rows);
+}
+
+int dspk_accept_sample(const float *logits, int64_t ldz, const float *q, int64_t ldq, const int32_t *draft_ids,
+                       const float *uniforms, int32_t m_rows, int32_t v, float temperature, int32_t *accept_len,
+                       int32_t *committed, void *workspace, size_t ws_bytes, void *stream) {
+    const char *who = "dspk_accept_sample";
+    if (m_rows < 2 || m_rows > DSPK_MAX_ROWS)
+        return fail(DSPK_EINVAL, "%s: m_rows=%d out of 2..%d", who, m_rows, DSPK_MAX_ROWS);
+    if (v < 1) return fail(DSPK_EINVAL, "%s: v=%d must be >= 1", who, v);
+    if (!(temperature > 0.f) || !isfinite(temperature))
+        return fail(DSPK_EINVAL, "%s: temperature must be finite and > 0", who);
+    if (logits == nullptr || q == nullptr || draft_ids == nullptr || uniforms == nullptr || accept_len == nullptr ||
+        committed == nullptr)
+        return fail(DSPK_EINVAL, "%s: NULL pointer", who);
+    if (!aligned(logits, 4) || !aligned(q, 4)) return fail(DSPK_EINVAL, "%s: misaligned logits or q", who);
+    if (ldz < v || ldq < v) return fail(DSPK_EINVAL, "%s: ldz/ldq must be >= v", who);
+    const size_t need = dspk_sample_workspace_bytes(v, m_rows);
+    if (workspace == nullptr || !aligned(workspace, 256) || ws_bytes < need)
+        return fail(DSPK_EINVAL, "%s: workspace of %zu bytes required (256-byte aligned)", who, need);
+    return launch_result(dspk::launch_accept_sample(logits, ldz, q, ldq, draft_ids, uniforms, m_rows, v, temperature,
+                                                    accept_len, committed, workspace, (hipStream_t)stream),
+                         who);
+}
+
+}  // extern "C"

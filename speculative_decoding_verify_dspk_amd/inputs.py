@@ -229,3 +229,38 @@ def weight_bytes(n: int, k: int, bits: int) -> int:
     if bits == 16:
         return n * k * 2
     return n * k * bits // 8 + 2 * 2 * n * (k // GROUP)
+
+
+# ------------------------------------------------- device-side bulk generators
+def device_generator(*labels):
+    """torch CUDA generator seeded from labels (for multi-GB weight stacks)."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed_of(*labels) & ((1 << 63) - 1))
+    return g
+
+
+def make_qweight_device(n: int, k: int, bits: int, *labels):
+    """Same distributions as ``make_qweight``, drawn on the GPU with torch's
+    generator: uniform random 32-bit words are exactly LSB-first packed words of
+    independent uniform codes; scales U(0.001, 0.01) and biases N(0, 0.1) are
+    rounded to fp16; the bf16 control is N(0.7, 0.45).  Returns
+    (codes, scales, biases) device tensors (int32 / int16 / int16 bit patterns)."""
+    import torch
+    g = device_generator(*labels, n, k, bits)
+    if bits == 16:
+        w = torch.empty((n, k), dtype=torch.float32, device="cuda").normal_(0.7, 0.45, generator=g)
+        return w.to(torch.bfloat16).view(torch.int16), None, None
+    words = torch.randint(-(1 << 31), 1 << 31, (n, k * bits // 32), dtype=torch.int64, device="cuda",
+                          generator=g).to(torch.int32)
+    sc = torch.empty((n, k // GROUP), dtype=torch.float32, device="cuda").uniform_(0.001, 0.01, generator=g)
+    bi = torch.empty((n, k // GROUP), dtype=torch.float32, device="cuda").normal_(0.0, 0.1, generator=g)
+    return words, sc.to(torch.float16).view(torch.int16), bi.to(torch.float16).view(torch.int16)
+
+
+def make_activations_device(m: int, k: int, *labels):
+    """bf16 N(0, 1) rows ``[M][K]`` on the GPU (int16 bit patterns)."""
+    import torch
+    g = device_generator(*labels, m, k, "act")
+    x = torch.empty((m, k), dtype=torch.float32, device="cuda").normal_(0.0, 1.0, generator=g)
+    return x.to(torch.bfloat16).view(torch.int16)

@@ -1,0 +1,102 @@
+"""One verify round on the GPU, composed from the C-ABI calls.
+
+A round ("mlx-dspark" wiki summary, "Architecture"): every projection of the
+target over the M rows (anchor + drafts, or B requests x rows), the vocabulary
+head with the row argmax (or logits for sampling), the acceptance step, and one
+device-to-host copy of the round's result ("mlx-dspark releases", v0.2.0 notes:
+one device sync per round).
+
+Weights and activations are seeded synthetic tensors of the workload's shapes
+(``inputs.LAYER_SHAPES``).  Each decoder layer contributes four launches, as a
+real layer's dependencies allow: q/k/v grouped (they read the same rows), o,
+gate/up grouped, down.  The four inputs of a layer are independent N(0, 1)
+rows; attention, norms and the activation function are outside this path.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+from . import binding, inputs
+
+
+@dataclass
+class Layer:
+    qkv: list
+    o: binding.DeviceQWeight
+    gateup: list
+    down: binding.DeviceQWeight
+
+
+@dataclass
+class VerifyStack:
+    model: str
+    n_layers: int
+    bits: int
+    max_m: int
+    copies: int = 1
+    seed: str = "stack"
+    layers: list = field(default_factory=list)   # [copy][layer] -> Layer
+    heads: list = field(default_factory=list)    # [copy] -> DeviceQWeight
+
+    def __post_init__(self):
+        import torch
+        s = inputs.LAYER_SHAPES[self.model]
+        self.hidden, self.qdim, self.kvdim, self.inter, self.vocab = (s["hidden"], s["q"], s["kv"], s["inter"],
+                                                                      s["vocab"])
+        H, Q, KV, F, V = self.hidden, self.qdim, self.kvdim, self.inter, self.vocab
+
+        def mk(n, k, *lab):
+            c, sc, bi = inputs.make_qweight_device(n, k, self.bits, self.model, self.seed, *lab)
+            return binding.DeviceQWeight(n, k, self.bits, c, sc, bi)
+
+        for cp in range(self.copies):
+            ls = []
+            for li in range(self.n_layers):
+                ls.append(Layer(qkv=[mk(Q, H, cp, li, "q"), mk(KV, H, cp, li, "k"), mk(KV, H, cp, li, "v")],
+                                o=mk(H, Q, cp, li, "o"),
+                                gateup=[mk(F, H, cp, li, "gate"), mk(F, H, cp, li, "up")],
+                                down=mk(H, F, cp, li, "down")))
+            self.layers.append(ls)
+            self.heads.append(mk(V, H, cp, "lm_head"))
+        M = self.max_m
+        act = lambda k, name: inputs.make_activations_device(M, k, self.model, self.seed, name)
+        self.x_attn, self.x_o, self.x_mlp, self.x_down = act(H, "attn_in"), act(Q, "o_in"), act(H, "mlp_in"), \
+            act(F, "down_in")
+        self.h = act(H, "final_h")
+        f32 = dict(dtype=torch.float32, device="cuda")
+        self.y_qkv = [torch.empty((M, Q), **f32), torch.empty((M, KV), **f32), torch.empty((M, KV), **f32)]
+        self.y_o = torch.empty((M, H), **f32)
+        self.y_gu = [torch.empty((M, F), **f32), torch.empty((M, F), **f32)]
+        self.y_down = torch.empty((M, H), **f32)
+        self.argmax = torch.empty((M,), dtype=torch.int32, device="cuda")
+        self.logits = torch.empty((M, V), **f32)
+        # one workspace per launch shape (their split-K layouts differ)
+        wsb = binding.qgemm_workspace_bytes
+        self.ws_qkv = binding.alloc_workspace(wsb(Q, H, M) + 2 * wsb(KV, H, M))
+        self.ws_o = binding.alloc_workspace(wsb(H, Q, M))
+        self.ws_gu = binding.alloc_workspace(2 * wsb(F, H, M))
+        self.ws_down = binding.alloc_workspace(wsb(H, F, M))
+        self.ws_head = binding.alloc_workspace(binding.lmhead_workspace_bytes(V, M))
+
+    # ------------------------------------------------------------------ sizes
+    def layer_weight_bytes(self) -> int:
+        L = self.layers[0][0]
+        return sum(w.nbytes for w in L.qkv + [L.o] + L.gateup + [L.down])
+
+    def head_weight_bytes(self) -> int:
+        return self.heads[0].nbytes
+
+    def round_weight_bytes(self) -> int:
+        return self.n_layers * self.layer_weight_bytes() + self.head_weight_bytes()
+
+    # ---------------------------------------------------------------- launches
+    def launch_layers(self, m: int, copy: int = 0, stream=None) -> None:
+        for L in self.layers[copy]:
+            binding.qgemm_verify_grouped(L.qkv, self.x_attn, m, self.y_qkv, self.ws_qkv, stream)
+            binding.qgemm_verify(L.o, self.x_o, m, self.y_o, self.ws_o, stream)
+            binding.qgemm_verify_grouped(L.gateup, self.x_mlp, m, self.y_gu, self.ws_gu, stream)
+            binding.qgemm_verify(L.down, self.x_down, m, self.y_down, self.ws_down, stream)
+
+    def launch_head(self, m: int, copy: int = 0, want_logits: bool = False, stream=None) -> None:
+        binding.lmhead_argmax(self.heads[copy], self.h, m, self.argmax, self.logits if want_logits else None,
+                              self.ws_head, stream)

@@ -1,0 +1,105 @@
+"""Helpers for the GPU parity tests: upload seeded host inputs, call the HIP
+path through the C ABI binding, and compare with the oracle."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from speculative_decoding_verify_dspk_amd import binding, inputs
+
+# Contract tolerance on logits / projections: per-row normwise relative error.
+RTOL = 2e-3
+# Rows whose oracle top-2 margin is below this may legitimately pick either token.
+NEAR_TIE = 1e-3
+
+
+def torch():
+    import torch as t
+    return t
+
+
+def dev_u16(a: np.ndarray):
+    """uint16 host array -> int16 device tensor with the same bits."""
+    t = torch()
+    return t.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+
+def dev_i32(a: np.ndarray):
+    t = torch()
+    return t.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def dev_f32(a: np.ndarray):
+    t = torch()
+    return t.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def run_qgemm(w: inputs.QWeight, x_bits: np.ndarray, m: int, out_bf16: bool = False, dw=None):
+    t = torch()
+    dw = dw or binding.DeviceQWeight.upload(w)
+    x = dev_u16(x_bits)
+    y = t.empty((m, w.n), dtype=t.int16 if out_bf16 else t.float32, device="cuda")
+    ws = binding.alloc_workspace(binding.qgemm_workspace_bytes(w.n, w.k, m))
+    binding.qgemm_verify(dw, x, m, y, ws)
+    t.cuda.synchronize()
+    r = y.cpu().numpy()
+    return r.view(np.uint16) if out_bf16 else r
+
+
+def run_lmhead(w: inputs.QWeight, h_bits: np.ndarray, m: int, want_logits: bool = True, dw=None):
+    t = torch()
+    dw = dw or binding.DeviceQWeight.upload(w)
+    h = dev_u16(h_bits)
+    am = t.full((m,), -7, dtype=t.int32, device="cuda")
+    z = t.empty((m, w.n), dtype=t.float32, device="cuda") if want_logits else None
+    ws = binding.alloc_workspace(binding.lmhead_workspace_bytes(w.n, m))
+    binding.lmhead_argmax(dw, h, m, am, z, ws)
+    t.cuda.synchronize()
+    return am.cpu().numpy(), (z.cpu().numpy() if want_logits else None)
+
+
+def rowwise_rel_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """max_v |got - ref| / max_v |ref| per row."""
+    num = np.abs(got.astype(np.float64) - ref).max(axis=1)
+    den = np.maximum(np.abs(ref).max(axis=1), 1e-300)
+    return num / den
+
+
+def assert_rows_close(got, ref, rtol=RTOL, what=""):
+    err = rowwise_rel_err(got, ref)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    assert (err <= rtol).all(), f"{what}: worst row normwise error {err.max():.3e} > {rtol}"
+    return err.max()
+
+
+def oracle_columns(w: inputs.QWeight, x_bits: np.ndarray, cols: np.ndarray) -> np.ndarray:
+    """Oracle outputs for a subset of output columns (rows of W), one slice at a time."""
+    cols = np.asarray(cols)
+    if w.bits == 16:
+        return oracle.qlinear(x_bits, w.codes[cols], None, None, 16, len(cols), w.k)
+    return oracle.qlinear(x_bits, w.codes[cols], w.scales[cols], w.biases[cols], w.bits, len(cols), w.k)
+
+
+def oracle_logits_chunked(w: inputs.QWeight, h_bits: np.ndarray, chunk: int = 16384) -> np.ndarray:
+    """Full oracle logits, computed over vocabulary slices to bound host memory."""
+    out = np.empty((h_bits.shape[0], w.n))
+    for s in range(0, w.n, chunk):
+        out[:, s:s + chunk] = oracle_columns(w, h_bits, np.arange(s, min(w.n, s + chunk)))
+    return out
+
+
+def assert_argmax_parity(got_ids, z_ref, what=""):
+    """Bit-exact ids except rows whose oracle top-2 margin is below NEAR_TIE."""
+    t_ref, margin = oracle.argmax_lowest(z_ref)
+    near = ~(margin >= NEAR_TIE)
+    got_ids = np.asarray(got_ids)
+    bad = (got_ids != t_ref) & ~near
+    assert not bad.any(), f"{what}: argmax mismatch rows {np.nonzero(bad)[0]} got {got_ids[bad]} want {t_ref[bad]}"
+    # near-tie rows: any token within NEAR_TIE of the row maximum is a valid pick
+    for i in np.nonzero(near)[0]:
+        top = z_ref[i, t_ref[i]]
+        assert 0 <= got_ids[i] < z_ref.shape[1], f"{what}: row {i} id out of range"
+        assert np.isnan(top) or z_ref[i, got_ids[i]] >= top - NEAR_TIE, f"{what}: row {i} near-tie pick invalid"
+    if near.any():
+        print(f"[{what}] near-tie rows (margin < {NEAR_TIE}): {np.nonzero(near)[0].tolist()}")
+    return t_ref, near

@@ -1,0 +1,145 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+* libdspk.so loads and exports every function include/dspk.h declares;
+* argument validation rejects bad calls before touching the device, with the
+  documented error code and a message;
+* the oracle and the HIP path share no code: neither imports the other.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from speculative_decoding_verify_dspk_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+EINVAL, EUNSUPPORTED = -1, -2
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from speculative_decoding_verify_dspk_amd import build
+        build.build()
+    return binding.lib()
+
+
+def test_exports_every_header_symbol(lib):
+    names = binding.header_symbols()
+    assert len(names) >= 10
+    for name in names:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (dspk_\w+)", out))
+    assert set(names) <= exported
+    assert lib.dspk_version() >= 100
+
+
+def _desc(n=64, k=128, bits=8, group=64, codes=0x10000, scales=0x20000, biases=0x30000):
+    return binding.QWeightDesc(n, k, bits, group, codes, scales, biases)
+
+
+# pointers below are never dereferenced: every call fails validation first
+X, Y, WS = 0x40000, 0x50000, 0x60000
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (dict(bits=3), EUNSUPPORTED), (dict(bits=2), EUNSUPPORTED), (dict(group=32), EUNSUPPORTED),
+    (dict(k=100), EINVAL), (dict(k=0), EINVAL), (dict(n=0), EINVAL),
+    (dict(codes=0), EINVAL), (dict(codes=0x10004), EINVAL), (dict(scales=0), EINVAL),
+    (dict(bits=16), EINVAL),   # bf16 weights must not carry scales/biases
+])
+def test_qgemm_rejects_bad_weight(lib, mutate, code):
+    d = _desc(**mutate)
+    rc = lib.dspk_qgemm_verify(ctypes.byref(d), X, 128, 4, Y, 0, 64, WS, 1 << 20, None)
+    assert rc == code
+    assert lib.dspk_last_error().decode().startswith("dspk_qgemm_verify")
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(m=0), EINVAL), (dict(m=33), EINVAL), (dict(ldx=120), EINVAL), (dict(ldx=132), EINVAL),
+    (dict(x=0), EINVAL), (dict(x=X + 8), EINVAL), (dict(ldy=32), EINVAL), (dict(dt=7), EINVAL),
+    (dict(y=0), EINVAL),
+])
+def test_qgemm_rejects_bad_rows(lib, args, code):
+    a = dict(x=X, ldx=128, m=4, y=Y, dt=0, ldy=64)
+    a.update(args)
+    d = _desc()
+    rc = lib.dspk_qgemm_verify(ctypes.byref(d), a["x"], a["ldx"], a["m"], a["y"], a["dt"], a["ldy"],
+                               WS, 1 << 20, None)
+    assert rc == code
+
+
+def test_qgemm_workspace_contract(lib):
+    # a short-K weight runs in one split: no workspace; a long-K, narrow one needs one
+    assert lib.dspk_qgemm_workspace_bytes(151936, 2560, 16) == 0
+    need = lib.dspk_qgemm_workspace_bytes(1024, 9728, 16)
+    assert need > 0 and need % 256 == 0
+    d = _desc(n=1024, k=9728)
+    rc = lib.dspk_qgemm_verify(ctypes.byref(d), X, 9728, 16, Y, 0, 1024, WS, need - 256, None)
+    assert rc == EINVAL and "workspace" in lib.dspk_last_error().decode()
+    rc = lib.dspk_qgemm_verify(ctypes.byref(d), X, 9728, 16, Y, 0, 1024, WS + 16, need, None)
+    assert rc == EINVAL
+
+
+def test_grouped_rejects_mismatch(lib):
+    ds = (binding.QWeightDesc * 2)(_desc(k=128), _desc(k=256))
+    ys = (ctypes.c_void_p * 2)(Y, Y)
+    ld = (ctypes.c_int64 * 2)(64, 64)
+    assert lib.dspk_qgemm_verify_grouped(2, ds, X, 256, 4, ys, 0, ld, WS, 1 << 20, None) == EINVAL
+    assert lib.dspk_qgemm_verify_grouped(0, ds, X, 256, 4, ys, 0, ld, WS, 1 << 20, None) == EINVAL
+    assert lib.dspk_qgemm_verify_grouped(5, ds, X, 256, 4, ys, 0, ld, WS, 1 << 20, None) == EINVAL
+
+
+def test_lmhead_rejects(lib):
+    d = _desc(n=1000, k=128)
+    assert lib.dspk_lmhead_argmax(ctypes.byref(d), X, 128, 4, Y, None, 0, None, 0, None) == EINVAL
+    assert lib.dspk_lmhead_argmax(ctypes.byref(d), X, 128, 4, Y, Y, 999, WS, 4096, None) == EINVAL
+    big = _desc(n=1000, k=8192 + 64)
+    assert lib.dspk_lmhead_argmax(ctypes.byref(big), X, 8256, 4, Y, None, 0, WS, 4096, None) == EUNSUPPORTED
+    assert lib.dspk_lmhead_argmax(ctypes.byref(d), X, 128, 40, Y, None, 0, WS, 4096, None) == EINVAL
+
+
+def test_accept_rejects(lib):
+    assert lib.dspk_accept_greedy(X, X, 0, 4, Y, Y, None) == EINVAL
+    assert lib.dspk_accept_greedy(X, X, 1, 33, Y, Y, None) == EINVAL
+    assert lib.dspk_accept_greedy(X, None, 1, 4, Y, Y, None) == EINVAL
+    need = lib.dspk_sample_workspace_bytes(151936, 17)
+    assert need > 0
+    ok = dict(z=X, ldz=1000, q=X, ldq=1000, d=X, u=X, rows=4, v=1000, T=1.0, ws=WS, wsb=need)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return lib.dspk_accept_sample(a["z"], a["ldz"], a["q"], a["ldq"], a["d"], a["u"], a["rows"], a["v"],
+                                      a["T"], Y, Y, a["ws"], a["wsb"], None)
+    assert call(T=0.0) == EINVAL
+    assert call(T=float("nan")) == EINVAL
+    assert call(T=float("inf")) == EINVAL
+    assert call(rows=1) == EINVAL
+    assert call(rows=33) == EINVAL
+    assert call(ldz=999) == EINVAL
+    assert call(wsb=16) == EINVAL
+    assert call(z=X + 2) == EINVAL
+
+
+def _imports(path):
+    src = open(path).read()
+    return set(re.findall(r"^\s*(?:from|import)\s+([\w\.]+)", src, re.M))
+
+
+def test_oracle_and_hip_path_are_independent():
+    pkg = os.path.join(ROOT, "speculative_decoding_verify_dspk_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            p = os.path.join(dirpath, f)
+            if f.endswith(".py"):
+                assert not any(m.split(".")[0] == "oracle" for m in _imports(p)), p
+            if f.endswith((".hip", ".cpp", ".h")):
+                assert "oracle" not in open(p).read().lower(), p
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith(".py"):
+            mods = _imports(os.path.join(ROOT, "oracle", f))
+            assert not any(m.startswith("speculative_decoding_verify_dspk_amd") for m in mods), f

@@ -1,0 +1,173 @@
+"""GPU parity of dspk_accept_greedy and dspk_accept_sample.
+
+Greedy: bit-exact against the oracle.  Sampling: the GPU and the oracle get
+the same fp32 logits, q, drafts and uniforms; committed ids and lengths must be
+equal except where a decision sits within the exemption band of fp32 versus
+fp64 arithmetic (an accept test with |u q(d) - p(d)| < 1e-5 max(q, p), or a
+final draw whose threshold lies within 1e-5 of the mass total of a CDF
+boundary).  Exempt cases are reported.  Also: the pages' hand cases, data
+faults, and a chi-square test of the GPU's committed-token distribution.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+from scipy import stats
+
+import oracle
+from speculative_decoding_verify_dspk_amd import binding, inputs
+from gpuutil import dev_f32, dev_i32, torch
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")
+
+
+def gpu_greedy(t, d):
+    tt = torch()
+    b, m_rows = t.shape
+    al = tt.full((b,), -9, dtype=tt.int32, device="cuda")
+    com = tt.full((b, m_rows), -9, dtype=tt.int32, device="cuda")
+    dd = dev_i32(d.reshape(b, m_rows - 1)) if m_rows > 1 else None
+    binding.accept_greedy(dev_i32(t), dd, b, m_rows, al, com)
+    tt.cuda.synchronize()
+    return al.cpu().numpy(), com.cpu().numpy()
+
+
+@pytest.mark.parametrize("b,m_rows", [(1, 1), (1, 2), (1, 6), (4, 6), (64, 17), (100, 32), (3, 24)])
+def test_greedy_matches_oracle(b, m_rows):
+    g = np.random.default_rng(b * 100 + m_rows)
+    v = 50
+    t = g.integers(0, v, size=(b, m_rows)).astype(np.int32)
+    d = inputs.drafts_match_rate(t, 0.7, v, "greedy-gpu", b, m_rows) if m_rows > 1 else np.zeros((b, 0), np.int32)
+    al, com = gpu_greedy(t, d)
+    ral, rcom = oracle.accept_greedy(t, d)
+    assert np.array_equal(al, ral)
+    assert np.array_equal(com, rcom)
+
+
+def test_greedy_golden():
+    for c in json.load(open(GOLDEN))["greedy"]:
+        t = np.array([c["t"]], np.int32)
+        d = np.array(c["d"], np.int32).reshape(1, len(c["t"]) - 1)
+        al, com = gpu_greedy(t, d)
+        assert al[0] == c["accept_len"] and list(com[0]) == c["committed"], c
+
+
+def gpu_sample(z, q, d, u, T):
+    tt = torch()
+    m_rows, v = z.shape
+    al = tt.full((1,), -9, dtype=tt.int32, device="cuda")
+    com = tt.full((m_rows,), -9, dtype=tt.int32, device="cuda")
+    ws = binding.alloc_workspace(binding.sample_workspace_bytes(v, m_rows))
+    binding.accept_sample(dev_f32(z), dev_f32(q.reshape(m_rows - 1, v)), dev_i32(d), dev_f32(u), m_rows, v, T,
+                          al, com, ws)
+    tt.cuda.synchronize()
+    assert int(ws[:256].count_nonzero()) == 0, "arrival counter not reset"
+    return int(al.cpu()[0]), com.cpu().numpy()
+
+
+def exempt(z, q, d, u, T, band=1e-5):
+    """Decisions of the oracle's run that sit within the fp32/fp64 band."""
+    z = np.asarray(z, np.float64)
+    m_rows = z.shape[0]
+    alen, com = oracle.accept_sample(z, q, d, u, T)
+    if alen < 0:
+        return False
+    for j in range(min(alen, m_rows - 1)):
+        p = oracle.softmax_t(z[j], T)
+        lhs, rhs = u[j] * q[j, d[j]], p[d[j]]
+        if abs(lhs - rhs) < band * max(q[j, d[j]], p[d[j]], 1e-30):
+            return True
+    jr = alen - 1
+    p = oracle.softmax_t(z[jr], T)
+    wts = np.maximum(0.0, p - q[jr]) if (jr < m_rows - 1 and com[jr] != d[jr]) else p
+    if wts.sum() <= 0:
+        wts = p
+    thr = u[m_rows - 1] * wts.sum()
+    c = np.cumsum(wts)
+    return bool((np.abs(c - thr) < band * wts.sum()).any())
+
+
+def _softmax(a, T):
+    a = np.asarray(a, np.float64) / T
+    e = np.exp(a - a.max())
+    return e / e.sum()
+
+
+def make_block(g, v, m_rows, T, spread=2.0, noise=1.0, match=0.5):
+    z = (g.normal(0, spread, size=(m_rows, v))).astype(np.float32)
+    q = np.empty((m_rows - 1, v), np.float32)
+    d = np.empty(m_rows - 1, np.int32)
+    for j in range(m_rows - 1):
+        # a drafter that is sometimes close to the target, sometimes not
+        zq = z[j] + g.normal(0, noise if g.random() < match else 4 * noise, size=v)
+        q[j] = _softmax(zq, T).astype(np.float32)
+        d[j] = g.choice(v, p=q[j].astype(np.float64) / q[j].sum())
+    u = inputs.make_uniforms(m_rows, "blk", int(g.integers(1 << 30)))
+    return z, q, d, u
+
+
+@pytest.mark.parametrize("v,m_rows,T", [(8, 2, 1.0), (8, 4, 0.7), (64, 6, 1.0), (1000, 17, 1.5),
+                                        (5000, 3, 1.0), (4097, 32, 0.9), (151936, 17, 1.0)])
+def test_sample_matches_oracle(v, m_rows, T):
+    g = np.random.default_rng(v + m_rows)
+    trials = 40 if v < 100000 else 6
+    n_exempt = 0
+    for i in range(trials):
+        z, q, d, u = make_block(g, v, m_rows, T)
+        al, com = gpu_sample(z, q, d, u, T)
+        ral, rcom = oracle.accept_sample(z.astype(np.float64), q, d, u, T)
+        if al != ral or not np.array_equal(com, rcom):
+            assert exempt(z, q.astype(np.float64), d, u.astype(np.float64), T), \
+                f"trial {i}: gpu ({al}, {com}) != oracle ({ral}, {rcom})"
+            n_exempt += 1
+    print(f"v={v} m_rows={m_rows}: {n_exempt} exempt of {trials}")
+    assert n_exempt <= max(1, trials // 10)
+
+
+def test_sample_golden_hand_cases():
+    for c in json.load(open(GOLDEN))["sample"]:
+        if not (c["T"] > 0):
+            continue            # temperature is validated on the host (DSPK_EINVAL)
+        z = np.array(c["z"], np.float32)
+        q = np.array(c["q"], np.float32)
+        d = np.array(c["d"], np.int32)
+        u = np.array(c["u"], np.float32)
+        al, com = gpu_sample(z, q, d, u, c["T"])
+        assert al == c["accept_len"] and list(com) == c["committed"], (c, al, com)
+
+
+@pytest.mark.parametrize("fault", ["z_nan", "z_inf", "q_neg", "q_nan", "u_one", "u_neg", "d_big", "d_neg"])
+def test_sample_faults(fault):
+    g = np.random.default_rng(3)
+    z, q, d, u = make_block(g, 9000, 5, 1.0)
+    if fault == "z_nan": z[4, 8999] = np.nan
+    if fault == "z_inf": z[0, 5] = -np.inf
+    if fault == "q_neg": q[3, 4500] = -1e-7
+    if fault == "q_nan": q[1, 0] = np.nan
+    if fault == "u_one": u[4] = 1.0
+    if fault == "u_neg": u[0] = -0.25
+    if fault == "d_big": d[2] = 9000
+    if fault == "d_neg": d[0] = -3
+    al, com = gpu_sample(z, q, d, u, 1.0)
+    ral, rcom = oracle.accept_sample(z.astype(np.float64), q, d, u, 1.0)
+    assert al == ral == -1
+    assert (com == -1).all() and (rcom == -1).all()
+
+
+def test_sample_distribution_chi2():
+    """Committed first token over many seeded GPU rounds follows p_0 exactly."""
+    g = np.random.default_rng(11)
+    v, m_rows, T, trials = 8, 3, 1.0, 6000
+    z = g.normal(0, 1.0, size=(m_rows, v)).astype(np.float32)
+    q = np.stack([_softmax(g.normal(0, 1.0, size=v), T) for _ in range(m_rows - 1)]).astype(np.float32)
+    p0 = _softmax(z[0], T)
+    counts = np.zeros(v)
+    for i in range(trials):
+        d = np.array([g.choice(v, p=q[j].astype(np.float64) / q[j].sum()) for j in range(m_rows - 1)], np.int32)
+        u = (g.integers(0, 1 << 24, size=m_rows) / float(1 << 24)).astype(np.float32)
+        al, com = gpu_sample(z, q, d, u, T)
+        counts[com[0]] += 1
+    chi = stats.chisquare(counts, p0 * trials)
+    assert chi.pvalue > 1e-3, chi
