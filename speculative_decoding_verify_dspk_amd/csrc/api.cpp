@@ -95,7 +95,7 @@ int qgemm_common(int32_t count, const dspk_qweight *w, const uint16_t *x, int64_
     size_t need = 0;
     int grid = 0;
     for (int i = 0; i < count; ++i) {
-        const dspk::GemmPlan pl = dspk::plan_gemm(w[i].n, w[i].k, m, w[i].bits, false);
+        const dspk::GemmPlan pl = dspk::plan_gemm(w[i].n, w[i].k, m, false);
         dspk::GemmProblem &P = L.p[i];
         P.codes = w[i].codes;
         P.scales = w[i].scales;
@@ -104,17 +104,17 @@ int qgemm_common(int32_t count, const dspk_qweight *w, const uint16_t *x, int64_
         P.ldy = ldy[i];
         P.n = w[i].n;
         P.k = w[i].k;
-        P.ncb = pl.ncb;
+        P.ncg = pl.ncg;
         P.splits = pl.splits;
-        P.wave_groups = pl.wave_groups;
+        P.split_groups = pl.split_groups;
         P.wg_begin = grid;
         if (pl.ws_bytes) {
             char *base = (char *)workspace + need;
             P.counters = (uint32_t *)base;
-            P.partial = (float *)(base + ((size_t)pl.ncb * 4 + 255) / 256 * 256);
+            P.partial = (float *)(base + ((size_t)pl.ncg * 4 + 255) / 256 * 256);
         }
         need += pl.ws_bytes;
-        grid += pl.ncb * pl.splits;
+        grid += pl.ncg * pl.splits;
     }
     if (need > 0) {
         if (workspace == nullptr || !aligned(workspace, 256))
@@ -134,7 +134,7 @@ const char *dspk_last_error(void) { return g_err.c_str(); }
 
 size_t dspk_qgemm_workspace_bytes(int32_t n, int32_t k, int32_t m) {
     if (n < 1 || k < DSPK_GROUP || k % DSPK_GROUP || m < 1 || m > DSPK_MAX_ROWS) return 0;
-    return dspk::plan_gemm(n, k, m, 8, false).ws_bytes;
+    return dspk::plan_gemm(n, k, m, false).ws_bytes;
 }
 
 int dspk_qgemm_verify(const dspk_qweight *w, const uint16_t *x, int64_t ldx, int32_t m, void *y,
@@ -152,9 +152,9 @@ int dspk_qgemm_verify_grouped(int32_t count, const dspk_qweight *w, const uint16
 }
 
 size_t dspk_lmhead_workspace_bytes(int32_t v, int32_t m) {
-    (void)v;
     (void)m;
-    return 512;   // keys [32] x 8 bytes, then the arrival counter
+    if (v < 1) return 0;
+    return dspk::lmhead_workspace_bytes(v);   // arrival counter, then per-workgroup row maxima
 }
 
 int dspk_lmhead_argmax(const dspk_qweight *w, const uint16_t *h, int64_t ldh, int32_t m, int32_t *argmax,
@@ -162,8 +162,6 @@ int dspk_lmhead_argmax(const dspk_qweight *w, const uint16_t *h, int64_t ldh, in
     const char *who = "dspk_lmhead_argmax";
     int rc = check_weight(w, who);
     if (rc) return rc;
-    if (w->k > dspk::kMaxWGGroups * 64)
-        return fail(DSPK_EUNSUPPORTED, "%s: k=%d above the supported %d", who, w->k, dspk::kMaxWGGroups * 64);
     rc = check_rows(h, ldh, m, w->k, who);
     if (rc) return rc;
     if (argmax == nullptr || !aligned(argmax, 4)) return fail(DSPK_EINVAL, "%s: argmax NULL or misaligned", who);
@@ -172,7 +170,7 @@ int dspk_lmhead_argmax(const dspk_qweight *w, const uint16_t *h, int64_t ldh, in
     if (workspace == nullptr || !aligned(workspace, 256) || ws_bytes < dspk_lmhead_workspace_bytes(w->n, m))
         return fail(DSPK_EINVAL, "%s: workspace of %zu bytes required (256-byte aligned)", who,
                     dspk_lmhead_workspace_bytes(w->n, m));
-    const dspk::GemmPlan pl = dspk::plan_gemm(w->n, w->k, m, w->bits, true);
+    const dspk::GemmPlan pl = dspk::plan_gemm(w->n, w->k, m, true);
     dspk::GemmLaunch L{};
     L.x = h;
     L.ldx = ldh;
@@ -181,19 +179,19 @@ int dspk_lmhead_argmax(const dspk_qweight *w, const uint16_t *h, int64_t ldh, in
     L.argmax = argmax;
     L.logits = logits;
     L.ldl = ldl;
-    L.keys = (unsigned long long *)workspace;
-    L.done = (uint32_t *)((char *)workspace + 256);
+    L.done = (uint32_t *)workspace;
+    L.keys = (unsigned long long *)((char *)workspace + 256);
     dspk::GemmProblem &P = L.p[0];
     P.codes = w->codes;
     P.scales = w->scales;
     P.biases = w->biases;
     P.n = w->n;
     P.k = w->k;
-    P.ncb = pl.ncb;
+    P.ncg = pl.ncg;
     P.splits = 1;
-    P.wave_groups = pl.wave_groups;
+    P.split_groups = pl.split_groups;
     P.wg_begin = 0;
-    return launch_result(dspk::launch_lmhead(L, w->bits, pl.ncb, (hipStream_t)stream), who);
+    return launch_result(dspk::launch_lmhead(L, w->bits, pl.ncg, (hipStream_t)stream), who);
 }
 
 int dspk_accept_greedy(const int32_t *target_ids, const int32_t *draft_ids, int32_t b, int32_t m_rows,

@@ -20,10 +20,16 @@
 // * M rows pad to 16 (MT = 1) or 32 (MT = 2) MFMA rows; the weight fragment is
 //   converted once and multiplied into every row tile, so the weight bytes per
 //   call do not depend on M.
-// * Four waves of a workgroup take consecutive K ranges of one 64-column block
-//   and add their partial sums in LDS in wave order.  Long K is split across
-//   workgroups; the last workgroup to arrive adds the partials in split order,
-//   so results do not depend on scheduling.
+// * A wave owns 64 output columns over one K range and streams it start to
+//   end; the four waves of a workgroup take neighbouring column blocks of the
+//   same K range, so their activation loads are served by the CU's L1.  Each
+//   wave stages the fp16 scale/bias pairs of its columns in its own LDS slice.
+// * When a weight has too few columns to fill the GPU, K is split across
+//   workgroups: each split publishes fp32 partial sums with device-coherent
+//   stores and the last workgroup of a column group to arrive adds them in
+//   split order, so results do not depend on scheduling.  No cache flush is
+//   needed: the partials and the arrival counter only move through
+//   device-scope atomic accesses.
 #include "dspk_internal.h"
 
 namespace dspk {
@@ -35,8 +41,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int NT = kTilesPerWave;
-constexpr int kSbStride = kBlockCols + 1;       // padded LDS row (dwords) of the scale/bias table
-constexpr int kSmemDwords = kMaxWGGroups * kSbStride;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -110,12 +114,49 @@ struct Slot {
     u32x4 a[MT][2];
 };
 
-// One wave: 64 columns [n0, n0+64) x groups [g0, g0+ng) of one weight, all rows.
+__device__ __forceinline__ void wait_vm_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ void store_agent(float *p, float v) {
+    __hip_atomic_store((uint32_t *)p, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float *p) {
+    return __uint_as_float(__hip_atomic_load((uint32_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Scale/bias pairs of this wave's 64 columns for groups [gc0, gc0 + gcn) into
+// its LDS slice: sb[g][col] = s | b << 16.  Lane = column.
+__device__ __forceinline__ void stage_sb(const GemmProblem &P, int n0, int G, int gc0, int gcn, bool vec,
+                                         uint32_t *sb, int lane) {
+    const int n = min(n0 + lane, P.n - 1);
+    const uint16_t *srow = P.scales + (int64_t)n * G + gc0;
+    const uint16_t *brow = P.biases + (int64_t)n * G + gc0;
+    if (vec) {   // 16-byte loads: 8 groups per load (rows and chunk starts are 16-byte aligned)
+        u32x4 sv[kSbChunk / 8], bv[kSbChunk / 8];
+#pragma unroll
+        for (int i = 0; i < kSbChunk / 8; ++i)
+            if (8 * i < gcn) {
+                sv[i] = *(const u32x4 *)(srow + 8 * i);
+                bv[i] = *(const u32x4 *)(brow + 8 * i);
+            }
+#pragma unroll
+        for (int i = 0; i < kSbChunk / 8; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (8 * i + e < gcn)
+                    sb[(8 * i + e) * kBlockCols + lane] =
+                        __builtin_amdgcn_perm(bv[i][e >> 1], sv[i][e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+    } else {
+        for (int g = 0; g < gcn; ++g) sb[g * kBlockCols + lane] = (uint32_t)srow[g] | ((uint32_t)brow[g] << 16);
+    }
+}
+
+// One wave: columns [n0, n0 + 64) x groups [g0, g1) of one weight, all rows.
 template <int BITS, int MT, int PF>
-__device__ __forceinline__ void wave_gemm(const GemmProblem &P, const uint16_t *__restrict__ x,
-                                          int64_t ldx, int M, int n0, int g0, int ng, int lg0,
-                                          const uint32_t *sb, int lane, f32x4 (&y)[NT][MT]) {
+__device__ __forceinline__ void wave_unit(const GemmProblem &P, bool sb_vec, const uint16_t *__restrict__ x,
+                                          int64_t ldx, int M, int n0, int g0, int g1, uint32_t *sb, int lane,
+                                          f32x4 (&y)[NT][MT]) {
     const int c = lane & 15, j = lane >> 4;
+    const int G = P.k >> 6;
     constexpr int GDW = 64 * BITS / 32;     // dwords per group of one weight row
     constexpr int LDW = GDW / 4;            // dwords per lane per group (4 lanes share a row)
     const int64_t row_dw = (int64_t)P.k * BITS / 32;
@@ -195,7 +236,7 @@ __device__ __forceinline__ void wave_gemm(const GemmProblem &P, const uint16_t *
                     b0 = codes4_to_bf16(s.b[t][0][0]);
                     b1 = codes4_to_bf16(s.b[t][0][1]);
                 }
-                const uint32_t sbv = sb[lg * kSbStride + 16 * t + c];
+                const uint32_t sbv = sb[lg * kBlockCols + 16 * t + c];
                 const float sc = h2f(sbv & 0xffffu);
                 float bi = h2f(sbv >> 16);
                 if constexpr (BITS == 4) bi = fmaf(-128.f, sc, bi);   // codes carry +128
@@ -211,35 +252,46 @@ __device__ __forceinline__ void wave_gemm(const GemmProblem &P, const uint16_t *
         }
     };
 
-    Slot<BITS, MT> buf[PF];
+    for (int gc0 = g0; gc0 < g1; gc0 += kSbChunk) {
+        const int ng = min(kSbChunk, g1 - gc0);
+        // Ring of PF slots, each consumed in place and then refilled with the
+        // group PF ahead; the first PF groups are requested before the
+        // scale/bias staging so their latency overlaps it.
+        Slot<BITS, MT> buf[PF];
 #pragma unroll
-    for (int p = 0; p < PF; ++p)
-        if (p < ng) load(buf[p], g0 + p);
-    int gi = 0;
-    for (; gi + 2 * PF <= ng; gi += PF) {
+        for (int p = 0; p < PF; ++p)
+            if (p < ng) load(buf[p], gc0 + p);
+        if constexpr (BITS != 16) stage_sb(P, n0, G, gc0, ng, sb_vec, sb, lane);
+        int gi = 0;
+        for (; gi + 2 * PF <= ng; gi += PF) {
 #pragma unroll
-        for (int p = 0; p < PF; ++p) {
-            const Slot<BITS, MT> cur = buf[p];
-            load(buf[p], g0 + gi + p + PF);
-            compute(cur, lg0 + gi + p);
+            for (int p = 0; p < PF; ++p) {
+                compute(buf[p], gi + p);
+                load(buf[p], gc0 + gi + p + PF);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-    }
-    for (; gi < ng; gi += PF) {
+        for (; gi < ng; gi += PF) {
 #pragma unroll
-        for (int p = 0; p < PF; ++p) {
-            if (gi + p < ng) {
-                const Slot<BITS, MT> cur = buf[p];
-                if (gi + p + PF < ng) load(buf[p], g0 + gi + p + PF);
-                compute(cur, lg0 + gi + p);
+            for (int p = 0; p < PF; ++p) {
+                if (gi + p < ng) {
+                    compute(buf[p], gi + p);
+                    if (gi + p + PF < ng) load(buf[p], gc0 + gi + p + PF);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
 }
 
+// M <= 16 fits three waves per SIMD (12 per CU) without spills; two row tiles need two.
 template <int BITS, int MT, int PF, bool ARGMAX>
-__global__ __launch_bounds__(256) void qgemm_kernel(const GemmLaunch L) {
-    __shared__ uint32_t smem[kSmemDwords];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+__global__ __launch_bounds__(256, MT == 1 ? 3 : 2) void qgemm_kernel(const GemmLaunch L) {
+    __shared__ uint32_t sb_all[kWavesPerWG][kSbChunk * kBlockCols];
+    __shared__ unsigned long long red[kWavesPerWG][kMaxRows];
+    __shared__ int s_last;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar loop control
     const int bid = blockIdx.x;
     int pi = 0;
 #pragma unroll
@@ -248,66 +300,27 @@ __global__ __launch_bounds__(256) void qgemm_kernel(const GemmLaunch L) {
     const GemmProblem &P = L.p[pi];
 
     const int local = bid - P.wg_begin;
-    const int cb = local / P.splits, split = local - cb * P.splits;
-    const int n0 = cb * kBlockCols;
+    const int S = P.splits;
+    const int cg = local / S, split = local - cg * S;
+    const int n0 = cg * kWGCols + w * kBlockCols;
+    const int M = L.m, N = P.n;
+    const bool active = n0 < N;
     const int G = P.k >> 6;
-    const int wg_groups = P.wave_groups * kWavesPerWG;
-    const int wg_g0 = split * wg_groups;
-    const int wg_g1 = min(G, wg_g0 + wg_groups);
-    const int g0 = min(wg_g1, wg_g0 + w * P.wave_groups);
-    const int g1 = min(wg_g1, g0 + P.wave_groups);
-
-    if constexpr (BITS != 16) {
-        // scale/bias table of this workgroup: smem[g][col] = s | b << 16
-        const int wgn = wg_g1 - wg_g0;
-        for (int idx = tid; idx < kBlockCols * wgn; idx += 256) {
-            const int col = idx / wgn, g = idx - col * wgn;
-            const int n = min(n0 + col, P.n - 1);
-            const int64_t off = (int64_t)n * G + wg_g0 + g;
-            smem[g * kSbStride + col] = (uint32_t)P.scales[off] | ((uint32_t)P.biases[off] << 16);
-        }
-        __syncthreads();
-    }
+    const int g0 = split * P.split_groups;
+    const int g1 = min(G, g0 + P.split_groups);
+    const bool sb_vec = ((G & 7) == 0) && ((P.split_groups & 7) == 0) &&
+                        ((((uintptr_t)P.scales | (uintptr_t)P.biases) & 15) == 0);
 
     f32x4 y[NT][MT];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) y[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    wave_gemm<BITS, MT, PF>(P, L.x, L.ldx, L.m, n0, g0, g1 - g0, g0 - wg_g0, smem, lane, y);
+    if (active) wave_unit<BITS, MT, PF>(P, sb_vec, L.x, L.ldx, M, n0, g0, g1, sb_all[w], lane, y);
 
-    // waves 1..3 hand their partial sums to wave 0, which adds them in wave order
-    __syncthreads();
-    float *red = (float *)smem;
     const int c = lane & 15, j = lane >> 4;
-    constexpr int RROWS = 16 * MT;
-    if (w > 0) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    red[((w - 1) * RROWS + 16 * mt + 4 * j + r) * kBlockCols + 16 * t + c] = y[t][mt][r];
-    }
-    __syncthreads();
-    if (w != 0) return;
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float v = y[t][mt][r];
-#pragma unroll
-                for (int q = 0; q < kWavesPerWG - 1; ++q)
-                    v += red[(q * RROWS + 16 * mt + 4 * j + r) * kBlockCols + 16 * t + c];
-                y[t][mt][r] = v;
-            }
-
-    const int M = L.m, N = P.n;
     if constexpr (ARGMAX) {
-        // fused argmax over this block's 64 columns, then across workgroups
+        // best (value, column) per row over this wave's 64 columns ...
         unsigned long long best[MT][4];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -336,23 +349,61 @@ __global__ __launch_bounds__(256) void qgemm_kernel(const GemmLaunch L) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = 16 * mt + 4 * j + r;
-                    if (m < M) atomicMax(&L.keys[m], best[mt][r]);
-                }
+                for (int r = 0; r < 4; ++r) red[w][16 * mt + 4 * j + r] = best[mt][r];
         }
-        __threadfence();
-        uint32_t ticket = 0;
-        if (lane == 0) ticket = atomicAdd(L.done, 1u);
-        ticket = __shfl(ticket, 0);
-        if (ticket == gridDim.x - 1) {
-            __threadfence();
-            if (lane < M) {
-                const unsigned long long k = atomicExch(&L.keys[lane], 0ull);
-                L.argmax[lane] = (int32_t)(0xffffffffu - (uint32_t)(k & 0xffffffffull));
+        __syncthreads();
+        // ... then over the workgroup, published for the last workgroup to combine
+        if (tid < M) {
+            unsigned long long b = red[0][tid];
+#pragma unroll
+            for (int q = 1; q < kWavesPerWG; ++q) b = red[q][tid] > b ? red[q][tid] : b;
+            __hip_atomic_store(&L.keys[(int64_t)bid * kMaxRows + tid], b, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+        wait_vm_stores();
+        __syncthreads();
+        if (tid == 0)
+            s_last = __hip_atomic_fetch_add(L.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                     gridDim.x - 1;
+        __syncthreads();
+        if (!s_last) return;
+        // last workgroup: maximum over all workgroups' keys, 8 rows at a time
+        const int nwg = gridDim.x;
+        for (int m0 = 0; m0 < M; m0 += 8) {
+            unsigned long long b8[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) b8[i] = 0ull;
+            for (int g = tid; g < nwg; g += 256) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    if (m0 + i < M) {
+                        const unsigned long long k = __hip_atomic_load(&L.keys[(int64_t)g * kMaxRows + m0 + i],
+                                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        b8[i] = k > b8[i] ? k : b8[i];
+                    }
             }
-            if (lane == 0) atomicExch(L.done, 0u);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const unsigned long long o = __shfl_xor(b8[i], off);
+                    b8[i] = o > b8[i] ? o : b8[i];
+                }
+            }
+            __syncthreads();
+            if (lane == 0) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) red[w][i] = b8[i];
+            }
+            __syncthreads();
+            if (tid < 8 && m0 + tid < M) {
+                unsigned long long b = red[0][tid];
+#pragma unroll
+                for (int q = 1; q < kWavesPerWG; ++q) b = red[q][tid] > b ? red[q][tid] : b;
+                L.argmax[m0 + tid] = (int32_t)(0xffffffffu - (uint32_t)(b & 0xffffffffull));
+            }
         }
+        if (tid == 0) __hip_atomic_store(L.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
         auto store = [&](int m, int n, float v) {
             if (L.y_bf16)
@@ -360,7 +411,8 @@ __global__ __launch_bounds__(256) void qgemm_kernel(const GemmLaunch L) {
             else
                 ((float *)P.y)[(int64_t)m * P.ldy + n] = v;
         };
-        if (P.splits == 1) {
+        if (S == 1) {
+            if (!active) return;
 #pragma unroll
             for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -372,45 +424,50 @@ __global__ __launch_bounds__(256) void qgemm_kernel(const GemmLaunch L) {
                     }
             return;
         }
-        // split K: publish this split's partial sums, the last arrival adds all splits in order
+        // split K: publish this split's partial sums; the last arrival adds all splits in order
         const int64_t plane = (int64_t)M * N;
+        if (active) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+            for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+                for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = 16 * mt + 4 * j + r, n = n0 + 16 * t + c;
-                    if (m < M && n < N) P.partial[split * plane + (int64_t)m * N + n] = y[t][mt][r];
-                }
-        __threadfence();
-        uint32_t ticket = 0;
-        if (lane == 0) ticket = atomicAdd(&P.counters[cb], 1u);
-        ticket = __shfl(ticket, 0);
-        if (ticket != (uint32_t)P.splits - 1) return;
-        __threadfence();
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = 16 * mt + 4 * j + r, n = n0 + 16 * t + c;
-                    if (m < M && n < N) {
-                        const float *p = P.partial + (int64_t)m * N + n;
-                        float v = p[0];
-                        for (int s = 1; s < P.splits; ++s) v += p[s * plane];
-                        store(m, n, v);
+                    for (int r = 0; r < 4; ++r) {
+                        const int m = 16 * mt + 4 * j + r, n = n0 + 16 * t + c;
+                        if (m < M && n < N) store_agent(P.partial + split * plane + (int64_t)m * N + n, y[t][mt][r]);
                     }
-                }
-        if (lane == 0) atomicExch(&P.counters[cb], 0u);
+        }
+        wait_vm_stores();
+        __syncthreads();
+        if (tid == 0)
+            s_last = __hip_atomic_fetch_add(&P.counters[cg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                     (uint32_t)S - 1;
+        __syncthreads();
+        if (!s_last) return;
+        if (active) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int m = 16 * mt + 4 * j + r, n = n0 + 16 * t + c;
+                        if (m < M && n < N) {
+                            const float *p = P.partial + (int64_t)m * N + n;
+                            float v = load_agent(p);
+                            for (int s2 = 1; s2 < S; ++s2) v += load_agent(p + s2 * plane);
+                            store(m, n, v);
+                        }
+                    }
+        }
+        if (tid == 0) __hip_atomic_store(&P.counters[cg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
 template <int BITS, bool ARGMAX>
 hipError_t launch_bits(const GemmLaunch &L, int grid, hipStream_t s) {
     if (L.m <= 16)
-        hipLaunchKernelGGL((qgemm_kernel<BITS, 1, 4, ARGMAX>), dim3(grid), dim3(256), 0, s, L);
+        hipLaunchKernelGGL((qgemm_kernel<BITS, 1, 3, ARGMAX>), dim3(grid), dim3(256), 0, s, L);
     else
         hipLaunchKernelGGL((qgemm_kernel<BITS, 2, 3, ARGMAX>), dim3(grid), dim3(256), 0, s, L);
     return hipGetLastError();
@@ -428,34 +485,43 @@ hipError_t launch_any(const GemmLaunch &L, int bits, int grid, hipStream_t s) {
 
 }  // namespace
 
-// Work split: aim for about kTargetWaves waves in flight (8 per CU on 256 CUs),
-// each streaming at least kMinWaveGroups groups so prologue and reduction stay
-// small next to the weight stream.
-constexpr int kTargetWaves = 2048;
-constexpr int kMinWaveGroups = 4;
+// Work split.  A weight with few columns is split along K so that about
+// kTargetWaves waves stream it, each over at least kMinSplitGroups groups
+// (multiples of 8 groups keep the scale/bias rows 16-byte aligned).
+#ifndef DSPK_TARGET_WAVES
+#define DSPK_TARGET_WAVES 2048
+#endif
+#ifndef DSPK_MIN_SPLIT_GROUPS
+#define DSPK_MIN_SPLIT_GROUPS 16
+#endif
+constexpr int kTargetWaves = DSPK_TARGET_WAVES;
+constexpr int kMinSplitGroups = DSPK_MIN_SPLIT_GROUPS;
 
-GemmPlan plan_gemm(int32_t n, int32_t k, int32_t m, int32_t bits, bool force_single_split) {
-    (void)bits;
+GemmPlan plan_gemm(int32_t n, int32_t k, int32_t m, bool single_split) {
     GemmPlan p{};
     const int G = k / 64;
-    p.ncb = (n + kBlockCols - 1) / kBlockCols;
-    int parts = (kTargetWaves + p.ncb - 1) / p.ncb;
-    parts = max(parts, min(kWavesPerWG, G));
-    parts = min(parts, G);
-    int wg = (G + parts - 1) / parts;
-    wg = max(wg, min(kMinWaveGroups, (G + kWavesPerWG - 1) / kWavesPerWG));
-    wg = min(wg, kMaxWGGroups / kWavesPerWG);
-    if (force_single_split) wg = (G + kWavesPerWG - 1) / kWavesPerWG;
-    parts = (G + wg - 1) / wg;
-    p.wave_groups = wg;
-    p.splits = (parts + kWavesPerWG - 1) / kWavesPerWG;
+    p.ncg = (n + kWGCols - 1) / kWGCols;
+    const int wave_cols = (n + kBlockCols - 1) / kBlockCols;
+    int splits = 1;
+    if (!single_split) {
+        splits = (kTargetWaves + wave_cols - 1) / wave_cols;
+        splits = max(1, min(splits, G / kMinSplitGroups));
+    }
+    int sg = (G + splits - 1) / splits;
+    if (splits > 1) sg = (sg + 7) / 8 * 8;
+    p.split_groups = sg;
+    p.splits = (G + sg - 1) / sg;
     p.ws_bytes = 0;
     if (p.splits > 1) {
-        const size_t ctr = ((size_t)p.ncb * 4 + 255) / 256 * 256;
-        p.ws_bytes = ctr + (size_t)p.splits * m * n * 4;
-        p.ws_bytes = (p.ws_bytes + 255) / 256 * 256;
+        const size_t ctr = ((size_t)p.ncg * 4 + 255) / 256 * 256;
+        p.ws_bytes = ctr + ((size_t)p.splits * m * n * 4 + 255) / 256 * 256;
     }
     return p;
+}
+
+size_t lmhead_workspace_bytes(int32_t v) {
+    const size_t nwg = ((size_t)v + kWGCols - 1) / kWGCols;
+    return 256 + nwg * kMaxRows * 8;
 }
 
 hipError_t launch_qgemm(const GemmLaunch &L, int bits, int grid, hipStream_t s) {

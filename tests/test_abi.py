@@ -97,9 +97,10 @@ def test_lmhead_rejects(lib):
     d = _desc(n=1000, k=128)
     assert lib.dspk_lmhead_argmax(ctypes.byref(d), X, 128, 4, Y, None, 0, None, 0, None) == EINVAL
     assert lib.dspk_lmhead_argmax(ctypes.byref(d), X, 128, 4, Y, Y, 999, WS, 4096, None) == EINVAL
-    big = _desc(n=1000, k=8192 + 64)
-    assert lib.dspk_lmhead_argmax(ctypes.byref(big), X, 8256, 4, Y, None, 0, WS, 4096, None) == EUNSUPPORTED
-    assert lib.dspk_lmhead_argmax(ctypes.byref(d), X, 128, 40, Y, None, 0, WS, 4096, None) == EINVAL
+    need = lib.dspk_lmhead_workspace_bytes(1000, 4)
+    assert need >= 256 + 4 * 32 * 8
+    assert lib.dspk_lmhead_argmax(ctypes.byref(d), X, 128, 4, Y, None, 0, WS, need - 8, None) == EINVAL
+    assert lib.dspk_lmhead_argmax(ctypes.byref(d), X, 128, 40, Y, None, 0, WS, 1 << 20, None) == EINVAL
 
 
 def test_accept_rejects(lib):

@@ -103,7 +103,8 @@ def make_block(g, v, m_rows, T, spread=2.0, noise=1.0, match=0.5):
         # a drafter that is sometimes close to the target, sometimes not
         zq = z[j] + g.normal(0, noise if g.random() < match else 4 * noise, size=v)
         q[j] = _softmax(zq, T).astype(np.float32)
-        d[j] = g.choice(v, p=q[j].astype(np.float64) / q[j].sum())
+        pj = q[j].astype(np.float64)
+        d[j] = g.choice(v, p=pj / pj.sum())
     u = inputs.make_uniforms(m_rows, "blk", int(g.integers(1 << 30)))
     return z, q, d, u
 
@@ -165,7 +166,8 @@ def test_sample_distribution_chi2():
     p0 = _softmax(z[0], T)
     counts = np.zeros(v)
     for i in range(trials):
-        d = np.array([g.choice(v, p=q[j].astype(np.float64) / q[j].sum()) for j in range(m_rows - 1)], np.int32)
+        d = np.array([g.choice(v, p=q[j].astype(np.float64) / q[j].astype(np.float64).sum())
+                      for j in range(m_rows - 1)], np.int32)
         u = (g.integers(0, 1 << 24, size=m_rows) / float(1 << 24)).astype(np.float32)
         al, com = gpu_sample(z, q, d, u, T)
         counts[com[0]] += 1

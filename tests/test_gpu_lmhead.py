@@ -79,7 +79,7 @@ def test_lmhead_deterministic_and_workspace_reuse():
         binding.lmhead_argmax(dw, x, m, am, z, ws)
         runs.append((am, z))
     t.cuda.synchronize()
-    assert int(ws.count_nonzero()) == 0, "workspace not left zero-filled"
+    assert int(ws[:256].count_nonzero()) == 0, "arrival counter not reset"
     for am, z in runs[1:]:
         assert t.equal(am, runs[0][0]) and t.equal(z, runs[0][1])
 
