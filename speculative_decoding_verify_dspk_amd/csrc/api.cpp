@@ -86,16 +86,28 @@ int qgemm_common(int32_t count, const dspk_qweight *w, const uint16_t *x, int64_
     int rc = check_rows(x, ldx, m, w[0].k, who);
     if (rc) return rc;
 
+    int32_t ns[DSPK_MAX_GROUPED];
+    for (int i = 0; i < count; ++i) ns[i] = w[i].n;
+    const dspk::GemmPlan pl = dspk::plan_gemm(count, ns, w[0].k, m, w[0].bits, false);
+    if (workspace == nullptr || !aligned(workspace, 256))
+        return fail(DSPK_EINVAL, "%s: workspace of %zu bytes required (256-byte aligned)", who, pl.ws_bytes);
+    if (ws_bytes < pl.ws_bytes)
+        return fail(DSPK_EINVAL, "%s: workspace %zu bytes < %zu required", who, ws_bytes, pl.ws_bytes);
+
     dspk::GemmLaunch L{};
     L.x = x;
     L.ldx = ldx;
     L.count = count;
     L.m = m;
     L.y_bf16 = y_dtype == DSPK_BF16;
-    size_t need = 0;
-    int grid = 0;
+    L.units = pl.units;
+    L.total_cg = pl.total_cg;
+    L.counters = (uint32_t *)((char *)workspace + pl.off_counters);
+    L.partial = (float *)((char *)workspace + pl.off_partial);
+    const int gs = dspk::stage_groups(w[0].bits, m);
+    const int nst = (w[0].k / 64 + gs - 1) / gs;
+    int u = 0, cg = 0;
     for (int i = 0; i < count; ++i) {
-        const dspk::GemmPlan pl = dspk::plan_gemm(w[i].n, w[i].k, m, false);
         dspk::GemmProblem &P = L.p[i];
         P.codes = w[i].codes;
         P.scales = w[i].scales;
@@ -104,24 +116,14 @@ int qgemm_common(int32_t count, const dspk_qweight *w, const uint16_t *x, int64_
         P.ldy = ldy[i];
         P.n = w[i].n;
         P.k = w[i].k;
-        P.ncg = pl.ncg;
-        P.splits = pl.splits;
-        P.split_groups = pl.split_groups;
-        P.wg_begin = grid;
-        if (pl.ws_bytes) {
-            char *base = (char *)workspace + need;
-            P.counters = (uint32_t *)base;
-            P.partial = (float *)(base + ((size_t)pl.ncg * 4 + 255) / 256 * 256);
-        }
-        need += pl.ws_bytes;
-        grid += pl.ncg * pl.splits;
+        P.ncg = (w[i].n + dspk::kBlockCols - 1) / dspk::kBlockCols;
+        P.nst = nst;
+        P.u_begin = u;
+        P.cg_begin = cg;
+        u += P.ncg * nst;
+        cg += P.ncg;
     }
-    if (need > 0) {
-        if (workspace == nullptr || !aligned(workspace, 256))
-            return fail(DSPK_EINVAL, "%s: workspace of %zu bytes required (256-byte aligned)", who, need);
-        if (ws_bytes < need) return fail(DSPK_EINVAL, "%s: workspace %zu bytes < %zu required", who, ws_bytes, need);
-    }
-    return launch_result(dspk::launch_qgemm(L, w[0].bits, grid, (hipStream_t)stream), who);
+    return launch_result(dspk::launch_qgemm(L, w[0].bits, pl.grid, (hipStream_t)stream), who);
 }
 
 }  // namespace
@@ -134,7 +136,12 @@ const char *dspk_last_error(void) { return g_err.c_str(); }
 
 size_t dspk_qgemm_workspace_bytes(int32_t n, int32_t k, int32_t m) {
     if (n < 1 || k < DSPK_GROUP || k % DSPK_GROUP || m < 1 || m > DSPK_MAX_ROWS) return 0;
-    return dspk::plan_gemm(n, k, m, false).ws_bytes;
+    size_t most = 0;
+    for (int bits : {4, 8, 16}) {   // the plan depends on the format only through the stage depth
+        const size_t b = dspk::plan_gemm(1, &n, k, m, bits, false).ws_bytes;
+        most = b > most ? b : most;
+    }
+    return most;
 }
 
 int dspk_qgemm_verify(const dspk_qweight *w, const uint16_t *x, int64_t ldx, int32_t m, void *y,
@@ -152,9 +159,9 @@ int dspk_qgemm_verify_grouped(int32_t count, const dspk_qweight *w, const uint16
 }
 
 size_t dspk_lmhead_workspace_bytes(int32_t v, int32_t m) {
-    (void)m;
-    if (v < 1) return 0;
-    return dspk::lmhead_workspace_bytes(v);   // arrival counter, then per-workgroup row maxima
+    if (v < 1 || m < 1 || m > DSPK_MAX_ROWS) return 0;
+    // the largest plan over hidden sizes: one workgroup per CU holds partial sums
+    return dspk::plan_gemm(1, &v, 1 << 20, m, 8, true).ws_bytes;
 }
 
 int dspk_lmhead_argmax(const dspk_qweight *w, const uint16_t *h, int64_t ldh, int32_t m, int32_t *argmax,
@@ -170,28 +177,35 @@ int dspk_lmhead_argmax(const dspk_qweight *w, const uint16_t *h, int64_t ldh, in
     if (workspace == nullptr || !aligned(workspace, 256) || ws_bytes < dspk_lmhead_workspace_bytes(w->n, m))
         return fail(DSPK_EINVAL, "%s: workspace of %zu bytes required (256-byte aligned)", who,
                     dspk_lmhead_workspace_bytes(w->n, m));
-    const dspk::GemmPlan pl = dspk::plan_gemm(w->n, w->k, m, true);
+    const dspk::GemmPlan pl = dspk::plan_gemm(1, &w->n, w->k, m, w->bits, true);
+    if (ws_bytes < pl.ws_bytes)
+        return fail(DSPK_EINVAL, "%s: workspace %zu bytes < %zu required", who, ws_bytes, pl.ws_bytes);
     dspk::GemmLaunch L{};
     L.x = h;
     L.ldx = ldh;
     L.count = 1;
     L.m = m;
+    L.units = pl.units;
+    L.total_cg = pl.total_cg;
+    L.done = (uint32_t *)workspace;
+    L.counters = (uint32_t *)((char *)workspace + pl.off_counters);
+    L.keys = (unsigned long long *)((char *)workspace + pl.off_keys);
+    L.partial = (float *)((char *)workspace + pl.off_partial);
     L.argmax = argmax;
     L.logits = logits;
     L.ldl = ldl;
-    L.done = (uint32_t *)workspace;
-    L.keys = (unsigned long long *)((char *)workspace + 256);
     dspk::GemmProblem &P = L.p[0];
     P.codes = w->codes;
     P.scales = w->scales;
     P.biases = w->biases;
     P.n = w->n;
     P.k = w->k;
-    P.ncg = pl.ncg;
-    P.splits = 1;
-    P.split_groups = pl.split_groups;
-    P.wg_begin = 0;
-    return launch_result(dspk::launch_lmhead(L, w->bits, pl.ncg, (hipStream_t)stream), who);
+    P.ncg = pl.total_cg;
+    const int gs = dspk::stage_groups(w->bits, m);
+    P.nst = (w->k / 64 + gs - 1) / gs;
+    P.u_begin = 0;
+    P.cg_begin = 0;
+    return launch_result(dspk::launch_lmhead(L, w->bits, pl.grid, (hipStream_t)stream), who);
 }
 
 int dspk_accept_greedy(const int32_t *target_ids, const int32_t *draft_ids, int32_t b, int32_t m_rows,

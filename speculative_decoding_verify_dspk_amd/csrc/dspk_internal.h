@@ -11,31 +11,26 @@ constexpr int kWave = 64;          // CDNA wavefront width
 constexpr int kWavesPerWG = 4;     // waves per workgroup in the projection kernels
 constexpr int kTilesPerWave = 4;   // 16-column MFMA tiles per wave
 constexpr int kBlockCols = 16 * kTilesPerWave;          // columns per wave (64)
-constexpr int kWGCols = kBlockCols * kWavesPerWG;       // columns per workgroup (256)
-constexpr int kSbChunk = 40;       // K groups of scales/biases a wave stages in LDS at a time
-constexpr int kMaxHeadK = 8192;    // largest hidden size of the vocabulary head
 constexpr int kMaxGrouped = 4;
 constexpr int kMaxRows = 32;
 
-// One weight of a (possibly grouped) projection launch, with its work split.
-//   A wave owns 64 output columns and one K range ("split") of a weight; the
-//   four waves of a workgroup take four neighbouring column blocks of the same
-//   split, so they read the same activation rows.  With splits > 1, each split
-//   publishes its partial sums and the last workgroup of a 256-column group to
-//   arrive adds them in split order.
+// Work of a projection launch is a list of units: (weight, 64-column block,
+// K stage).  Units are numbered weight by weight, block by block, stage by
+// stage, and each wave of the persistent grid takes one contiguous range of
+// them ("stream-K"), so every wave streams the same number of weight bytes.
+// A block whose stages straddle waves is finished by the last of them to
+// arrive, adding the pieces in wave order.
 struct GemmProblem {
     const void *codes;        // packed codes (bits 4/8) or bf16 weights (bits 16)
     const uint16_t *scales;   // fp16 [n][k/64]
     const uint16_t *biases;   // fp16 [n][k/64]
     void *y;                  // output [m][ldy]
-    float *partial;           // workspace: [splits][m][n] fp32 (splits > 1)
-    uint32_t *counters;       // workspace: [ncg] arrival counters (splits > 1)
     int64_t ldy;
     int32_t n, k;
-    int32_t ncg;              // 256-column groups: ceil(n / 256)
-    int32_t splits;           // K ranges per column group
-    int32_t split_groups;     // K groups per split (the last may be shorter)
-    int32_t wg_begin;         // first workgroup of this problem in the grid
+    int32_t ncg;              // 64-column blocks: ceil(n / 64)
+    int32_t nst;              // K stages per block
+    int32_t u_begin;          // first unit of this weight
+    int32_t cg_begin;         // first block of this weight in the launch
 };
 
 struct GemmLaunch {
@@ -45,21 +40,28 @@ struct GemmLaunch {
     int32_t count;
     int32_t m;
     int32_t y_bf16;           // store y as bf16 instead of fp32
+    int32_t units;            // total units of the launch
+    int32_t total_cg;         // total blocks of the launch
+    // workspace
+    uint32_t *counters;       // [total_cg] arrival counters of split blocks
+    float *partial;           // [waves][2][m][64] partial sums of split blocks
     // vocabulary-head epilogue (argmax kernel only)
     int32_t *argmax;
     float *logits;
     int64_t ldl;
-    unsigned long long *keys; // workspace: [workgroups][kMaxRows] per-workgroup row maxima
-    uint32_t *done;           // workspace: arrival counter
+    unsigned long long *keys; // [grid][kMaxRows] per-workgroup row maxima
+    uint32_t *done;           // arrival counter over workgroups
 };
 
-// Work split of one weight (host side).
+// Launch plan of one (possibly grouped) projection call (host side).
 struct GemmPlan {
-    int32_t ncg, splits, split_groups;
-    size_t ws_bytes;          // workspace this weight needs (0 when splits == 1)
+    int32_t units, grid, total_cg;
+    size_t off_counters, off_keys, off_partial, ws_bytes;
 };
-GemmPlan plan_gemm(int32_t n, int32_t k, int32_t m, bool single_split);
-size_t lmhead_workspace_bytes(int32_t v);
+// groups of 64 along K per stage for a weight format and row-tile count
+int stage_groups(int bits, int m);
+GemmPlan plan_gemm(int count, const int32_t *n, int32_t k, int32_t m, int bits, bool argmax);
+int device_cus();
 
 hipError_t launch_qgemm(const GemmLaunch &L, int bits, int grid, hipStream_t s);
 hipError_t launch_lmhead(const GemmLaunch &L, int bits, int grid, hipStream_t s);

@@ -73,12 +73,14 @@ def test_qgemm_rejects_bad_rows(lib, args, code):
 
 
 def test_qgemm_workspace_contract(lib):
-    # a short-K weight runs in one split: no workspace; a long-K, narrow one needs one
-    assert lib.dspk_qgemm_workspace_bytes(151936, 2560, 16) == 0
+    # every call needs a workspace (arrival counters and split partial sums)
+    for n, k, m in ((151936, 2560, 16), (1024, 9728, 16), (64, 64, 1), (4096, 4096, 32)):
+        need = lib.dspk_qgemm_workspace_bytes(n, k, m)
+        assert need > 256 and need % 256 == 0
+    assert lib.dspk_qgemm_workspace_bytes(0, 64, 1) == 0
     need = lib.dspk_qgemm_workspace_bytes(1024, 9728, 16)
-    assert need > 0 and need % 256 == 0
     d = _desc(n=1024, k=9728)
-    rc = lib.dspk_qgemm_verify(ctypes.byref(d), X, 9728, 16, Y, 0, 1024, WS, need - 256, None)
+    rc = lib.dspk_qgemm_verify(ctypes.byref(d), X, 9728, 16, Y, 0, 1024, WS, 256, None)
     assert rc == EINVAL and "workspace" in lib.dspk_last_error().decode()
     rc = lib.dspk_qgemm_verify(ctypes.byref(d), X, 9728, 16, Y, 0, 1024, WS + 16, need, None)
     assert rc == EINVAL
