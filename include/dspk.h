@@ -63,12 +63,18 @@ extern "C" {
  *     codes  : uint32[n][k*bits/32], codes packed LSB-first (code c of a row
  *              sits in word c/(32/bits) at bit bits*(c mod 32/bits)),
  *              unsigned 0 .. 2^bits-1;
- *     scales : IEEE binary16 [n][k/64], row-major;
- *     biases : IEEE binary16 [n][k/64], row-major.
+ *     scales : IEEE binary16 [k/64][n], group-major (the n columns of one
+ *              group are contiguous);
+ *     biases : IEEE binary16 [k/64][n], group-major.
  * bits 16 -- unquantised bfloat16 control: codes = bf16[n][k], scales and
  *   biases must be NULL.
  * group must be 64; k must be a multiple of 64; codes must be 16-byte
  * aligned; scales/biases 4-byte aligned.  The struct itself is host memory.
+ *
+ * Activation rows (x, h) are chunk-major: bf16 [k/8][ldm][8], i.e. element
+ * (row i, column r) sits at index ((r / 8) * ldm + i) * 8 + r % 8, ldm >= m.
+ * The 8-element pieces of all rows are adjacent, so the 16 rows one MFMA
+ * operand needs come in one contiguous 256-byte span.
  */
 typedef struct dspk_qweight {
     int32_t n;
@@ -88,9 +94,10 @@ const char *dspk_last_error(void);
 
 /*
  * Workspace for dspk_qgemm_verify: bytes needed for a weight of n x k read by
- * m rows (0 when the kernel needs none).  The first 256 bytes... are split-K
- * counters: the workspace must be zero-filled before its FIRST use; every
- * completed call leaves it zero-filled again, so it can be reused as is.
+ * m rows (never 0: every call needs one).  It holds arrival counters and the
+ * partial sums of K-split column blocks.  The workspace must be zero-filled
+ * before its FIRST use; every completed call leaves its counters at zero
+ * again, so it can be reused as is by calls ordered on one stream.
  */
 size_t dspk_qgemm_workspace_bytes(int32_t n, int32_t k, int32_t m);
 
@@ -103,12 +110,15 @@ size_t dspk_qgemm_workspace_bytes(int32_t n, int32_t k, int32_t m);
  * the 1-bit counter-example in "mlx-dspark 0.7.0", "PrismML Bonsai 27B").
  *
  *   w         : weight descriptor (see dspk_qweight).
- *   x         : bf16 activations [m][ldx], ldx >= k, ldx % 8 == 0, 16-byte aligned.
+ *   x         : bf16 activations, chunk-major [k/8][ldx][8] (see above):
+ *               ldx = rows per chunk, m <= ldx <= 65536; 16-byte aligned.
  *   m         : rows, 1 .. DSPK_MAX_ROWS.
  *   y         : output [m][ldy], element type y_dtype (DSPK_F32 | DSPK_BF16),
  *               ldy >= n; 4-byte aligned.
- *   workspace : >= dspk_qgemm_workspace_bytes(n, k, m) bytes (may be NULL when
- *               that is 0), 256-byte aligned, zero-filled before first use.
+ *   workspace : >= dspk_qgemm_workspace_bytes(n, k, m) bytes, 256-byte
+ *               aligned, zero-filled before first use.
+ * Results are deterministic: the same call on the same inputs gives the same
+ * bits (the K split is fixed by the shapes, not by scheduling).
  * Errors: DSPK_EINVAL (null or misaligned pointer, n < 1, k % 64, ldx/ldy,
  * m out of 1..32, workspace too small), DSPK_EUNSUPPORTED (bits not in
  * {4, 8, 16}, group != 64), DSPK_EDEVICE.
@@ -121,8 +131,10 @@ int dspk_qgemm_verify(const dspk_qweight *w, const uint16_t *x, int64_t ldx, int
  * Grouped form for weights that read the same rows (q/k/v, gate/up): one
  * launch for `count` (1 .. DSPK_MAX_GROUPED) weights with equal k and bits.
  * y[g] is the output of w[g] with leading dimension ldy[g].  The workspace is
- * the sum of dspk_qgemm_workspace_bytes over the weights.  Same results,
- * bit for bit, as `count` separate dspk_qgemm_verify calls.
+ * the sum of dspk_qgemm_workspace_bytes over the weights.  The launch splits
+ * K over the workgroups differently from separate calls, so its results
+ * agree with theirs to fp32 rounding (both within the error bound of the
+ * single call), and are themselves deterministic.
  */
 int dspk_qgemm_verify_grouped(int32_t count, const dspk_qweight *w,
                               const uint16_t *x, int64_t ldx, int32_t m,
@@ -140,8 +152,9 @@ size_t dspk_lmhead_workspace_bytes(int32_t v, int32_t m);
  * summary, "Architecture").  The tie rule is the reading taken where the
  * project page leaves ties to floating-point rounding.
  *
- *   w         : vocabulary head, same format as dspk_qgemm_verify, k <= 8192.
- *   h         : bf16 [m][ldh] final hidden rows (16-byte aligned, ldh % 8 == 0).
+ *   w         : vocabulary head, same format as dspk_qgemm_verify.
+ *   h         : bf16 final hidden rows, chunk-major [k/8][ldh][8], m <= ldh,
+ *               16-byte aligned.
  *   argmax    : int32 [m] output.
  *   logits    : float32 [m][ldl] output, or NULL to skip writing logits.
  *   workspace : >= dspk_lmhead_workspace_bytes(v, m), 256-byte aligned,
@@ -163,8 +176,7 @@ int dspk_lmhead_argmax(const dspk_qweight *w, const uint16_t *h, int64_t ldh, in
  *   accept_len : int32 [b] output, committed tokens per request (1 .. m_rows)
  *   committed  : int32 [b][m_rows] output: accepted drafts, then the target's
  *                token of the first mismatching row (or the last row), then -1.
- * b >= 1, 1 <= m_rows <= DSPK_MAX_ROWS.  A target id < 0 (an argmax that
- * could not be formed) makes that request's accept_len -1.
+ * b >= 1, 1 <= m_rows <= DSPK_MAX_ROWS.
  */
 int dspk_accept_greedy(const int32_t *target_ids, const int32_t *draft_ids,
                        int32_t b, int32_t m_rows,

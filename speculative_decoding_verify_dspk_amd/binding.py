@@ -104,6 +104,25 @@ def _rows(t, name: str) -> int:
     return t.stride(0)
 
 
+def _chunks(t, name: str) -> int:
+    """Rows per chunk (ldm) of a chunk-major activation tensor [k/8][ldm][8]."""
+    if t.dim() != 3 or t.shape[2] != 8 or t.stride(2) != 1 or t.stride(1) != 8 or t.stride(0) != 8 * t.shape[1]:
+        raise ValueError(f"{name}: expected a contiguous chunk-major tensor [k/8][ldm][8]")
+    return t.shape[1]
+
+
+def to_chunk_major(x, ldm: int | None = None):
+    """Row-major activations [m][k] (a device tensor of bf16 bit patterns) ->
+    the library's chunk-major layout [k/8][ldm][8]; rows m..ldm-1 are zero.
+    A pure layout change: element (i, r) moves to ((r / 8) * ldm + i) * 8 + r % 8."""
+    import torch
+    m, k = x.shape
+    ldm = m if ldm is None else ldm
+    out = torch.zeros((k // 8, ldm, 8), dtype=x.dtype, device=x.device)
+    out[:, :m, :] = x.reshape(m, k // 8, 8).permute(1, 0, 2)
+    return out
+
+
 # ---------------------------------------------------------------- weights
 class DeviceQWeight:
     """A weight matrix in device memory plus its C descriptor."""
@@ -122,8 +141,9 @@ class DeviceQWeight:
                                                       else w.codes.view(np.int16))).to(device)
         sc = bi = None
         if w.bits != 16:
-            sc = torch.from_numpy(np.ascontiguousarray(w.scales.view(np.int16))).to(device)
-            bi = torch.from_numpy(np.ascontiguousarray(w.biases.view(np.int16))).to(device)
+            # the library's scale/bias arrays are group-major [k/64][n]
+            sc = torch.from_numpy(np.ascontiguousarray(w.scales.view(np.int16).T)).to(device)
+            bi = torch.from_numpy(np.ascontiguousarray(w.biases.view(np.int16).T)).to(device)
         return cls(w.n, w.k, w.bits, codes, sc, bi)
 
     @property
@@ -158,7 +178,8 @@ def alloc_workspace(nbytes: int, device="cuda"):
 
 
 def qgemm_verify(w: DeviceQWeight, x, m: int, y, workspace=None, stream=None) -> None:
-    ldx, ldy = _rows(x, "x"), _rows(y, "y")
+    """x: chunk-major activations [k/8][ldm][8] (see to_chunk_major)."""
+    ldx, ldy = _chunks(x, "x"), _rows(y, "y")
     dt = DSPK_BF16 if y.element_size() == 2 else DSPK_F32
     ws_bytes = 0 if workspace is None else workspace.numel()
     _check(lib().dspk_qgemm_verify(ctypes.byref(w.desc), x.data_ptr(), ldx, m, y.data_ptr(), dt, ldy,
@@ -172,13 +193,13 @@ def qgemm_verify_grouped(ws: list, x, m: int, ys: list, workspace=None, stream=N
     ldy = (c_int64 * cnt)(*[_rows(y, "y") for y in ys])
     dt = DSPK_BF16 if ys[0].element_size() == 2 else DSPK_F32
     ws_bytes = 0 if workspace is None else workspace.numel()
-    _check(lib().dspk_qgemm_verify_grouped(cnt, descs, x.data_ptr(), _rows(x, "x"), m, yptr, dt, ldy,
+    _check(lib().dspk_qgemm_verify_grouped(cnt, descs, x.data_ptr(), _chunks(x, "x"), m, yptr, dt, ldy,
                                            _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def lmhead_argmax(w: DeviceQWeight, h, m: int, argmax, logits=None, workspace=None, stream=None) -> None:
     ldl = 0 if logits is None else _rows(logits, "logits")
-    _check(lib().dspk_lmhead_argmax(ctypes.byref(w.desc), h.data_ptr(), _rows(h, "h"), m, argmax.data_ptr(),
+    _check(lib().dspk_lmhead_argmax(ctypes.byref(w.desc), h.data_ptr(), _chunks(h, "h"), m, argmax.data_ptr(),
                                     _ptr(logits), ldl, _ptr(workspace),
                                     0 if workspace is None else workspace.numel(), _stream(stream)))
 

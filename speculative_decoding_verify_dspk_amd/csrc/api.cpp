@@ -53,18 +53,33 @@ int check_weight(const dspk_qweight *w, const char *who) {
     return DSPK_OK;
 }
 
-int check_rows(const uint16_t *x, int64_t ldx, int32_t m, int32_t k, const char *who) {
+// Activations are chunk-major: [k/8][ldm][8] bf16, ldm >= m rows per chunk.
+int check_rows(const uint16_t *x, int64_t ldm, int32_t m, int32_t k, const char *who) {
     if (m < 1 || m > DSPK_MAX_ROWS) return fail(DSPK_EINVAL, "%s: m=%d out of 1..%d", who, m, DSPK_MAX_ROWS);
     if (x == nullptr || !aligned(x, 16))
         return fail(DSPK_EINVAL, "%s: activations must be a non-NULL 16-byte aligned device pointer", who);
-    if (ldx < k || ldx % 8) return fail(DSPK_EINVAL, "%s: ldx=%lld must be >= k=%d and a multiple of 8", who,
-                                        (long long)ldx, k);
+    if (ldm < m || ldm > 65536)
+        return fail(DSPK_EINVAL, "%s: ldm=%lld must be in m=%d .. 65536", who, (long long)ldm, m);
+    if ((int64_t)k * ldm >= ((int64_t)1 << 31))
+        return fail(DSPK_EUNSUPPORTED, "%s: activation buffer too large (k * ldm >= 2^31)", who);
     return DSPK_OK;
 }
 
 int launch_result(hipError_t e, const char *who) {
     if (e != hipSuccess) return fail(DSPK_EDEVICE, "%s: launch failed: %s", who, hipGetErrorString(e));
     return ok();
+}
+
+void fill_plan(dspk::GemmLaunch &L, const dspk::GemmPlan &pl, const uint16_t *x, int64_t ldx, int32_t m,
+               int32_t k) {
+    L.x = x;
+    L.ldx = ldx;
+    L.m = m;
+    L.k = k;
+    L.nst = pl.nst;
+    L.nq = pl.nq;
+    L.quads = pl.quads;
+    L.total_cg = pl.total_cg;
 }
 
 int qgemm_common(int32_t count, const dspk_qweight *w, const uint16_t *x, int64_t ldx, int32_t m,
@@ -89,24 +104,19 @@ int qgemm_common(int32_t count, const dspk_qweight *w, const uint16_t *x, int64_
     int32_t ns[DSPK_MAX_GROUPED];
     for (int i = 0; i < count; ++i) ns[i] = w[i].n;
     const dspk::GemmPlan pl = dspk::plan_gemm(count, ns, w[0].k, m, w[0].bits, false);
+    if (!pl.fits) return fail(DSPK_EUNSUPPORTED, "%s: weights too large for one launch", who);
     if (workspace == nullptr || !aligned(workspace, 256))
         return fail(DSPK_EINVAL, "%s: workspace of %zu bytes required (256-byte aligned)", who, pl.ws_bytes);
     if (ws_bytes < pl.ws_bytes)
         return fail(DSPK_EINVAL, "%s: workspace %zu bytes < %zu required", who, ws_bytes, pl.ws_bytes);
 
     dspk::GemmLaunch L{};
-    L.x = x;
-    L.ldx = ldx;
+    fill_plan(L, pl, x, ldx, m, w[0].k);
     L.count = count;
-    L.m = m;
     L.y_bf16 = y_dtype == DSPK_BF16;
-    L.units = pl.units;
-    L.total_cg = pl.total_cg;
     L.counters = (uint32_t *)((char *)workspace + pl.off_counters);
     L.partial = (float *)((char *)workspace + pl.off_partial);
-    const int gs = dspk::stage_groups(w[0].bits, m);
-    const int nst = (w[0].k / 64 + gs - 1) / gs;
-    int u = 0, cg = 0;
+    int cg = 0;
     for (int i = 0; i < count; ++i) {
         dspk::GemmProblem &P = L.p[i];
         P.codes = w[i].codes;
@@ -115,13 +125,8 @@ int qgemm_common(int32_t count, const dspk_qweight *w, const uint16_t *x, int64_
         P.y = y[i];
         P.ldy = ldy[i];
         P.n = w[i].n;
-        P.k = w[i].k;
-        P.ncg = (w[i].n + dspk::kBlockCols - 1) / dspk::kBlockCols;
-        P.nst = nst;
-        P.u_begin = u;
         P.cg_begin = cg;
-        u += P.ncg * nst;
-        cg += P.ncg;
+        cg += (w[i].n + dspk::kBlockCols - 1) / dspk::kBlockCols;
     }
     return launch_result(dspk::launch_qgemm(L, w[0].bits, pl.grid, (hipStream_t)stream), who);
 }
@@ -178,15 +183,12 @@ int dspk_lmhead_argmax(const dspk_qweight *w, const uint16_t *h, int64_t ldh, in
         return fail(DSPK_EINVAL, "%s: workspace of %zu bytes required (256-byte aligned)", who,
                     dspk_lmhead_workspace_bytes(w->n, m));
     const dspk::GemmPlan pl = dspk::plan_gemm(1, &w->n, w->k, m, w->bits, true);
+    if (!pl.fits) return fail(DSPK_EUNSUPPORTED, "%s: vocabulary head too large for one launch", who);
     if (ws_bytes < pl.ws_bytes)
         return fail(DSPK_EINVAL, "%s: workspace %zu bytes < %zu required", who, ws_bytes, pl.ws_bytes);
     dspk::GemmLaunch L{};
-    L.x = h;
-    L.ldx = ldh;
+    fill_plan(L, pl, h, ldh, m, w->k);
     L.count = 1;
-    L.m = m;
-    L.units = pl.units;
-    L.total_cg = pl.total_cg;
     L.done = (uint32_t *)workspace;
     L.counters = (uint32_t *)((char *)workspace + pl.off_counters);
     L.keys = (unsigned long long *)((char *)workspace + pl.off_keys);
@@ -199,11 +201,6 @@ int dspk_lmhead_argmax(const dspk_qweight *w, const uint16_t *h, int64_t ldh, in
     P.scales = w->scales;
     P.biases = w->biases;
     P.n = w->n;
-    P.k = w->k;
-    P.ncg = pl.total_cg;
-    const int gs = dspk::stage_groups(w->bits, m);
-    P.nst = (w->k / 64 + gs - 1) / gs;
-    P.u_begin = 0;
     P.cg_begin = 0;
     return launch_result(dspk::launch_lmhead(L, w->bits, pl.grid, (hipStream_t)stream), who);
 }

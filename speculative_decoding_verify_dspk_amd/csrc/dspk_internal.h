@@ -14,22 +14,20 @@ constexpr int kBlockCols = 16 * kTilesPerWave;          // columns per wave (64)
 constexpr int kMaxGrouped = 4;
 constexpr int kMaxRows = 32;
 
-// Work of a projection launch is a list of units: (weight, 64-column block,
-// K stage).  Units are numbered weight by weight, block by block, stage by
-// stage, and each wave of the persistent grid takes one contiguous range of
-// them ("stream-K"), so every wave streams the same number of weight bytes.
-// A block whose stages straddle waves is finished by the last of them to
-// arrive, adding the pieces in wave order.
+// Work of a projection launch is a list of quads: (weight, 64-column block,
+// four consecutive K stages), one stage per wave of a workgroup.  Quads are
+// numbered weight by weight, block by block, K first, and each workgroup of
+// the persistent grid takes one contiguous range of them ("stream-K"), so
+// every workgroup streams the same number of weight bytes.  A block whose
+// quads straddle workgroups is finished by the last of them to arrive, adding
+// the pieces in workgroup order.  Grouped weights share k, bits and rows.
 struct GemmProblem {
     const void *codes;        // packed codes (bits 4/8) or bf16 weights (bits 16)
     const uint16_t *scales;   // fp16 [n][k/64]
     const uint16_t *biases;   // fp16 [n][k/64]
     void *y;                  // output [m][ldy]
     int64_t ldy;
-    int32_t n, k;
-    int32_t ncg;              // 64-column blocks: ceil(n / 64)
-    int32_t nst;              // K stages per block
-    int32_t u_begin;          // first unit of this weight
+    int32_t n;
     int32_t cg_begin;         // first block of this weight in the launch
 };
 
@@ -39,12 +37,15 @@ struct GemmLaunch {
     int64_t ldx;
     int32_t count;
     int32_t m;
+    int32_t k;
+    int32_t nst;              // K stages per block
+    int32_t nq;               // quads per block: ceil(nst / 4)
+    int32_t quads;            // quads of the launch
+    int32_t total_cg;         // blocks of the launch
     int32_t y_bf16;           // store y as bf16 instead of fp32
-    int32_t units;            // total units of the launch
-    int32_t total_cg;         // total blocks of the launch
     // workspace
-    uint32_t *counters;       // [total_cg] arrival counters of split blocks
-    float *partial;           // [waves][2][m][64] partial sums of split blocks
+    uint32_t *counters;       // [total_cg][4] arrival counters of split blocks
+    float *partial;           // [grid][2][4][MT][64][4] partial sums of split blocks
     // vocabulary-head epilogue (argmax kernel only)
     int32_t *argmax;
     float *logits;
@@ -55,11 +56,12 @@ struct GemmLaunch {
 
 // Launch plan of one (possibly grouped) projection call (host side).
 struct GemmPlan {
-    int32_t units, grid, total_cg;
+    int32_t nst, nq, quads, grid, total_cg;
+    bool fits;                // quads * grid < 2^31 (the kernel's index range)
     size_t off_counters, off_keys, off_partial, ws_bytes;
 };
-// groups of 64 along K per stage for a weight format and row-tile count
-int stage_groups(int bits, int m);
+// K elements of one wave's stage for a weight format
+int stage_k(int bits);
 GemmPlan plan_gemm(int count, const int32_t *n, int32_t k, int32_t m, int bits, bool argmax);
 int device_cus();
 

@@ -245,7 +245,8 @@ def make_qweight_device(n: int, k: int, bits: int, *labels):
     generator: uniform random 32-bit words are exactly LSB-first packed words of
     independent uniform codes; scales U(0.001, 0.01) and biases N(0, 0.1) are
     rounded to fp16; the bf16 control is N(0.7, 0.45).  Returns
-    (codes, scales, biases) device tensors (int32 / int16 / int16 bit patterns)."""
+    (codes, scales, biases) device tensors (int32 / int16 / int16 bit
+    patterns); scales and biases group-major [K/64][N] as the library takes them."""
     import torch
     g = device_generator(*labels, n, k, bits)
     if bits == 16:
@@ -253,14 +254,16 @@ def make_qweight_device(n: int, k: int, bits: int, *labels):
         return w.to(torch.bfloat16).view(torch.int16), None, None
     words = torch.randint(-(1 << 31), 1 << 31, (n, k * bits // 32), dtype=torch.int64, device="cuda",
                           generator=g).to(torch.int32)
-    sc = torch.empty((n, k // GROUP), dtype=torch.float32, device="cuda").uniform_(0.001, 0.01, generator=g)
-    bi = torch.empty((n, k // GROUP), dtype=torch.float32, device="cuda").normal_(0.0, 0.1, generator=g)
+    sc = torch.empty((k // GROUP, n), dtype=torch.float32, device="cuda").uniform_(0.001, 0.01, generator=g)
+    bi = torch.empty((k // GROUP, n), dtype=torch.float32, device="cuda").normal_(0.0, 0.1, generator=g)
     return words, sc.to(torch.float16).view(torch.int16), bi.to(torch.float16).view(torch.int16)
 
 
 def make_activations_device(m: int, k: int, *labels):
-    """bf16 N(0, 1) rows ``[M][K]`` on the GPU (int16 bit patterns)."""
+    """bf16 N(0, 1) rows on the GPU (int16 bit patterns), in the library's
+    chunk-major layout ``[K/8][M][8]`` (independent draws, so the layout does
+    not change the distribution)."""
     import torch
     g = device_generator(*labels, m, k, "act")
-    x = torch.empty((m, k), dtype=torch.float32, device="cuda").normal_(0.0, 1.0, generator=g)
+    x = torch.empty((k // 8, m, 8), dtype=torch.float32, device="cuda").normal_(0.0, 1.0, generator=g)
     return x.to(torch.bfloat16).view(torch.int16)

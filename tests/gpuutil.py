@@ -24,6 +24,12 @@ def dev_u16(a: np.ndarray):
     return t.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
 
 
+def dev_act(a: np.ndarray, ldm: int | None = None):
+    """Row-major uint16 activation rows [m][k] -> the library's chunk-major
+    device layout [k/8][ldm][8]."""
+    return binding.to_chunk_major(dev_u16(a), ldm)
+
+
 def dev_i32(a: np.ndarray):
     t = torch()
     return t.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
@@ -37,7 +43,7 @@ def dev_f32(a: np.ndarray):
 def run_qgemm(w: inputs.QWeight, x_bits: np.ndarray, m: int, out_bf16: bool = False, dw=None):
     t = torch()
     dw = dw or binding.DeviceQWeight.upload(w)
-    x = dev_u16(x_bits)
+    x = dev_act(x_bits)
     y = t.empty((m, w.n), dtype=t.int16 if out_bf16 else t.float32, device="cuda")
     ws = binding.alloc_workspace(binding.qgemm_workspace_bytes(w.n, w.k, m))
     binding.qgemm_verify(dw, x, m, y, ws)
@@ -49,7 +55,7 @@ def run_qgemm(w: inputs.QWeight, x_bits: np.ndarray, m: int, out_bf16: bool = Fa
 def run_lmhead(w: inputs.QWeight, h_bits: np.ndarray, m: int, want_logits: bool = True, dw=None):
     t = torch()
     dw = dw or binding.DeviceQWeight.upload(w)
-    h = dev_u16(h_bits)
+    h = dev_act(h_bits)
     am = t.full((m,), -7, dtype=t.int32, device="cuda")
     z = t.empty((m, w.n), dtype=t.float32, device="cuda") if want_logits else None
     ws = binding.alloc_workspace(binding.lmhead_workspace_bytes(w.n, m))

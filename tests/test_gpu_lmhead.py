@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 from speculative_decoding_verify_dspk_amd import binding, inputs
-from gpuutil import (assert_argmax_parity, assert_rows_close, dev_u16, oracle_logits_chunked, run_lmhead,
+from gpuutil import (assert_argmax_parity, assert_rows_close, dev_act, oracle_logits_chunked, run_lmhead,
                      torch)
 
 pytestmark = pytest.mark.gpu
@@ -69,7 +69,7 @@ def test_lmhead_deterministic_and_workspace_reuse():
     t = torch()
     v, h, m = 20000, 1024, 16
     w = inputs.make_qweight(v, h, 8, "det")
-    x = dev_u16(inputs.make_activations(m, h, "det"))
+    x = dev_act(inputs.make_activations(m, h, "det"))
     dw = binding.DeviceQWeight.upload(w)
     ws = binding.alloc_workspace(binding.lmhead_workspace_bytes(v, m))
     runs = []

@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 from speculative_decoding_verify_dspk_amd import binding, inputs
-from gpuutil import (assert_rows_close, dev_u16, oracle_columns, run_qgemm, torch)
+from gpuutil import (assert_rows_close, dev_act, oracle_columns, run_qgemm, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -51,7 +51,7 @@ def test_qgemm_deterministic_and_grouped_equal():
     ws_ = [inputs.make_qweight(n, k, 8, "grp", n) for n in (4096, 1024, 1024)]
     x = inputs.make_activations(m, k, "grp")
     dws = [binding.DeviceQWeight.upload(w) for w in ws_]
-    xd = dev_u16(x)
+    xd = dev_act(x)
     sep = []
     for w, dw in zip(ws_, dws):
         outs = []
@@ -66,15 +66,22 @@ def test_qgemm_deterministic_and_grouped_equal():
     ys = [t.empty((m, w.n), dtype=t.float32, device="cuda") for w in ws_]
     need = sum(binding.qgemm_workspace_bytes(w.n, k, m) for w in ws_)
     wsp = binding.alloc_workspace(need)
+    first = None
     for _ in range(3):   # the workspace is reused: its counters must come back to zero
         for y in ys:
             y.fill_(float("nan"))
         binding.qgemm_verify_grouped(dws, xd, m, ys, wsp)
         t.cuda.synchronize()
-        for a, b in zip(sep, ys):
-            assert t.equal(a, b), "grouped result differs from separate calls"
-    ref = oracle.qlinear(x, ws_[0].codes, ws_[0].scales, ws_[0].biases, 8, 4096, k)
-    assert_rows_close(sep[0].cpu().numpy(), ref, what="q")
+        if first is None:
+            first = [y.clone() for y in ys]
+        for a, b in zip(first, ys):
+            assert t.equal(a, b), "grouped call not deterministic"
+    # the grouped launch splits K differently, so it agrees with the separate
+    # calls to rounding, and each agrees with the oracle
+    for w, a, b in zip(ws_, sep, ys):
+        ref = oracle.qlinear(x, w.codes, w.scales, w.biases, 8, w.n, k)
+        assert_rows_close(a.cpu().numpy(), ref, what=f"separate n={w.n}")
+        assert_rows_close(b.cpu().numpy(), ref, what=f"grouped n={w.n}")
 
 
 def test_qgemm_bf16_output_is_rounded_fp32():
@@ -84,16 +91,17 @@ def test_qgemm_bf16_output_is_rounded_fp32():
     assert np.array_equal(b, inputs.f32_to_bf16_bits(f))
 
 
-def test_qgemm_strided_rows():
-    """ldx > k and ldy > n: only the first k / n entries of each row are used / written."""
+def test_qgemm_padded_chunks_and_strided_output():
+    """ldm > m rows per activation chunk and ldy > n: the padding rows of each
+    chunk are never read (NaN there would show) and only n entries of each
+    output row are written."""
     t = torch()
     w, x = _case(8, 300, 512, 5, "strided")
-    pad = np.zeros((5, 512 + 64), np.uint16)
-    pad[:, :512] = x
-    pad[:, 512:] = 0x7fc0   # NaN bf16 in the padding must never be read
+    xc = dev_act(x, ldm=9)
+    xc[:, 5:, :] = 0x7fc0            # NaN bf16 bit pattern in the padding rows
     dw = binding.DeviceQWeight.upload(w)
     y = t.full((5, 300 + 12), 123.0, dtype=t.float32, device="cuda")
-    binding.qgemm_verify(dw, dev_u16(pad), 5, y, binding.alloc_workspace(binding.qgemm_workspace_bytes(300, 512, 5)))
+    binding.qgemm_verify(dw, xc, 5, y, binding.alloc_workspace(binding.qgemm_workspace_bytes(300, 512, 5)))
     t.cuda.synchronize()
     yy = y.cpu().numpy()
     assert (yy[:, 300:] == 123.0).all()
