@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--layers", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-s", type=float, default=20.0)
+    ap.add_argument("--calibrate", action="store_true",
+                    help="after the timed region, run one plain device copy of 256 MiB (the reference "
+                         "dispatch for scaling hardware byte counters)")
     return ap.parse_args()
 
 
@@ -81,6 +84,29 @@ def cpu_baseline(model: str, bits: int, m: int, budget_s: float):
             "sample": f"one {model} layer (7 projections) + {slices} x {sl}-row slices of the {v}x{h} head, "
                       f"{bits}-bit, M={m}; {done_bytes / 1e6:.1f} MB of weights in {t_total:.1f} s "
                       f"(numpy fp64, {threads} threads)"}
+
+
+def measured_traffic():
+    """HBM bytes per launch of the head kernel from the committed hardware-
+    counter summary, if it was taken on the current kernel source (else None)."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    summary = os.path.join(here, "profiles", "vocab_head_traffic.txt")
+    src = os.path.join(here, "speculative_decoding_verify_dspk_amd", "csrc", "qgemm.hip")
+    if not os.path.exists(summary):
+        return None
+    kv = {}
+    for line in open(summary):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.strip().split("=", 1)
+            kv[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if kv.get("kernel_source_sha256") != sha:
+        return None
+    try:
+        return int(float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def main():
@@ -176,9 +202,15 @@ def main():
     head_bytes = float(np.mean(head_bytes_all))
     achieved = head_bytes / head_avg_s / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "qgemm_kernel<8,1,4,true> (vocabulary head + argmax)",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                "kernel": f"qgemm_kernel<{args.bits},MT,true> (vocabulary head + argmax)",
                 "avg_launch_us": round(head_avg_s * 1e6, 2), "bytes_per_launch": int(head_bytes)}
+
+    if args.calibrate:
+        src = torch.empty(1 << 26, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
 
     cpu = None
     if not args.no_cpu_baseline:

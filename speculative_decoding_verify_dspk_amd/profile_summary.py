@@ -1,0 +1,119 @@
+"""Turn rocprofv3 CSV output of the benchmark into the short summaries kept
+under profiles/.
+
+    # per-kernel durations (rocprofv3 --kernel-trace --stats --output-format csv)
+    python -m speculative_decoding_verify_dspk_amd.profile_summary stats \\
+        <kernel_stats.csv> <kernel_trace.csv> <out.md> --cmd "<profiled command>"
+
+    # HBM bytes of the head kernel (two --pmc passes: FETCH_SIZE, WRITE_SIZE),
+    # scaled by what the same counters read for a plain 256 MiB device copy
+    python -m speculative_decoding_verify_dspk_amd.profile_summary traffic \\
+        <fetch counter_collection.csv> <write counter_collection.csv> <out.txt> --cmd "<...>"
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SRC = os.path.join(PKG, "csrc", "qgemm.hip")
+COPY_BYTES = 256 << 20          # the calibration copy that bench.py --calibrate runs
+
+
+def short(name: str) -> str:
+    if "qgemm_kernel" in name:
+        return "qgemm_kernel<" + name.split("<", 1)[1].split(">", 1)[0] + ">"
+    m = re.search(r"accept_\w+", name)
+    if m:
+        return m.group(0)
+    return (name[:70] + "...") if len(name) > 73 else name
+
+
+def stats(stats_csv: str, trace_csv: str, out: str, cmd: str) -> None:
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = ["# Kernel durations: benchmark verify rounds", "", "Command:", "", "    " + cmd, "",
+             "| kernel | calls | average us | total % |", "|---|---|---|---|"]
+    for r in rows[:12]:
+        lines.append(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f} |")
+    # per-launch split of the projection kernels by grid (one line per launch shape)
+    per = collections.defaultdict(list)
+    for r in csv.DictReader(open(trace_csv)):
+        if "qgemm_kernel" in r["Kernel_Name"]:
+            per[(short(r["Kernel_Name"]), r["Grid_Size_X"])].append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines += ["", "Projection launches by grid (workgroups x 256 threads):", "",
+              "| kernel | grid threads | launches | median us |", "|---|---|---|---|"]
+    for (k, g), v in sorted(per.items()):
+        v.sort()
+        lines.append(f"| {k} | {g} | {len(v)} | {v[len(v) // 2]:.1f} |")
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
+def counter_means(path: str, counter: str) -> dict:
+    per = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter:
+            per[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return per
+
+
+def traffic(fetch_csv: str, write_csv: str, out: str, cmd_fetch: str, cmd_write: str) -> None:
+    res = {}
+    for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
+        per = counter_means(path, counter)
+        # the calibration copy is the largest copy dispatch of the run (the
+        # others are the rounds' small device-to-host copies)
+        copy = max((v for k, vs in per.items() if "copyBuffer" in k for v in vs), default=0.0)
+        head = [v for k, vs in per.items() if "qgemm_kernel" in k and "true>" in k for v in vs]
+        if copy <= 0 or not head:
+            raise SystemExit(f"{path}: calibration copy or head kernel missing")
+        # bytes per counted KiB, from the copy that reads and writes COPY_BYTES once
+        factor = COPY_BYTES / copy
+        res[counter] = (sum(head) / len(head), factor)
+    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    f_kib, f_fac = res["FETCH_SIZE"]
+    w_kib, w_fac = res["WRITE_SIZE"]
+    lines = [
+        "# HBM traffic of the vocabulary-head kernel (qgemm_kernel<8,MT,true>), per launch",
+        "# Commands (one counter per run):",
+        "#   " + cmd_fetch,
+        "#   " + cmd_write,
+        f"# FETCH_SIZE per head launch: {f_kib:.0f} KiB; a 256 MiB device copy reads as "
+        f"{COPY_BYTES / f_fac:.0f} KiB -> scale {f_fac:.1f} bytes per counted KiB",
+        f"# WRITE_SIZE per head launch: {w_kib:.0f} KiB; the same copy writes as "
+        f"{COPY_BYTES / w_fac:.0f} KiB -> scale {w_fac:.1f} bytes per counted KiB",
+        f"kernel_source_sha256={sha}",
+        f"fetch_bytes_per_launch={f_kib * f_fac:.0f}",
+        f"write_bytes_per_launch={w_kib * w_fac:.0f}",
+    ]
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("stats_csv")
+    a.add_argument("trace_csv")
+    a.add_argument("out")
+    a.add_argument("--cmd", required=True)
+    b = sub.add_parser("traffic")
+    b.add_argument("fetch_csv")
+    b.add_argument("write_csv")
+    b.add_argument("out")
+    b.add_argument("--cmd-fetch", required=True)
+    b.add_argument("--cmd-write", required=True)
+    args = ap.parse_args()
+    if args.what == "stats":
+        stats(args.stats_csv, args.trace_csv, args.out, args.cmd)
+    else:
+        traffic(args.fetch_csv, args.write_csv, args.out, args.cmd_fetch, args.cmd_write)
+
+
+if __name__ == "__main__":
+    main()
