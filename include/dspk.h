@@ -54,7 +54,8 @@ extern "C" {
 #define DSPK_MAX_GROUPED 4    /* most weights in one grouped call              */
 
 /*
- * One weight matrix W[n][k] (out features x in features).
+ * One weight matrix W[n][k] (out features x in features) in its interchange
+ * layout, the input of dspk_qweight_pack.
  *
  * bits 4 or 8 -- affine group quantisation, w[r][c] = s[r][c/64] * q[r][c] +
  *   b[r][c/64], the plain reading of the pages' "quantised" target weights
@@ -63,18 +64,12 @@ extern "C" {
  *     codes  : uint32[n][k*bits/32], codes packed LSB-first (code c of a row
  *              sits in word c/(32/bits) at bit bits*(c mod 32/bits)),
  *              unsigned 0 .. 2^bits-1;
- *     scales : IEEE binary16 [k/64][n], group-major (the n columns of one
- *              group are contiguous);
- *     biases : IEEE binary16 [k/64][n], group-major.
+ *     scales : IEEE binary16 [n][k/64], row-major;
+ *     biases : IEEE binary16 [n][k/64], row-major.
  * bits 16 -- unquantised bfloat16 control: codes = bf16[n][k], scales and
  *   biases must be NULL.
  * group must be 64; k must be a multiple of 64; codes must be 16-byte
- * aligned; scales/biases 4-byte aligned.  The struct itself is host memory.
- *
- * Activation rows (x, h) are chunk-major: bf16 [k/8][ldm][8], i.e. element
- * (row i, column r) sits at index ((r / 8) * ldm + i) * 8 + r % 8, ldm >= m.
- * The 8-element pieces of all rows are adjacent, so the 16 rows one MFMA
- * operand needs come in one contiguous 256-byte span.
+ * aligned; scales/biases 2-byte aligned.  The struct itself is host memory.
  */
 typedef struct dspk_qweight {
     int32_t n;
@@ -86,15 +81,60 @@ typedef struct dspk_qweight {
     const uint16_t *biases;
 } dspk_qweight;
 
+/*
+ * The same weight in the library's tiled layout, which the projection and
+ * vocabulary-head calls stream.  `tiles` is device memory of
+ * dspk_tiled_bytes(n, k, bits) bytes, 256-byte aligned, written by
+ * dspk_qweight_pack.
+ *
+ * Layout: 64-column blocks in column order, each cut along K into units of
+ * KU = 128 (8-bit), 256 (4-bit) or 64 (bf16) elements; unit u of block b
+ * starts at byte (b * ceil(k / KU) + u) * UNIT, UNIT = 8192 + 4 * KU bytes
+ * for 4/8-bit and 8192 for bf16.  A unit holds its codes as eight 1 KiB slots
+ * of 64 x 16 bytes, each 16-byte piece the codes one lane of a wave feeds to
+ * the matrix cores, then (4/8-bit) one dword (scale | bias << 16) per column
+ * and group.  The exact byte order is documented in the packing source; it
+ * is a layout of this library, not an interchange format.  Columns past n
+ * and K past k are zero.  About 6% larger than codes alone at 8-bit, like
+ * the interchange layout with its scales and biases.
+ */
+typedef struct dspk_tiled_weight {
+    int32_t n;
+    int32_t k;
+    int32_t bits;
+    int32_t group;           /* must be 64 */
+    const void *tiles;
+} dspk_tiled_weight;
+
 /* Library version: major*10000 + minor*100 + patch. */
 int dspk_version(void);
 
 /* Message for the last non-zero return on this thread ("" if none). */
 const char *dspk_last_error(void);
 
+/* Bytes of a weight in the tiled layout (0 if the shape or bits are invalid). */
+size_t dspk_tiled_bytes(int32_t n, int32_t k, int32_t bits);
+
+/*
+ * Convert `w` (interchange layout, device memory) into the tiled layout at
+ * `tiles` (device memory, >= dspk_tiled_bytes(w->n, w->k, w->bits) bytes,
+ * 256-byte aligned, not overlapping w).  A one-time, load-time step: one
+ * kernel on `stream`, a pure permutation of the bytes.  Errors: DSPK_EINVAL
+ * (NULL, misaligned, bad shape, tiles too small), DSPK_EUNSUPPORTED (bits,
+ * group), DSPK_EDEVICE.
+ */
+int dspk_qweight_pack(const dspk_qweight *w, void *tiles, size_t tiles_bytes, void *stream);
+
+/*
+ * Activation rows (x, h) are chunk-major: bf16 [k/8][ldm][8], i.e. element
+ * (row i, column r) sits at index ((r / 8) * ldm + i) * 8 + r % 8, ldm >= m.
+ * The 8-element pieces of all rows are adjacent, so the 16 rows one MFMA
+ * operand needs come in one contiguous 256-byte span.
+ */
+
 /*
  * Workspace for dspk_qgemm_verify: bytes needed for a weight of n x k read by
- * m rows (never 0: every call needs one).  It holds arrival counters and the
+ * m rows, any format (never 0: every call needs one).  It holds arrival counters and the
  * partial sums of K-split column blocks.  The workspace must be zero-filled
  * before its FIRST use; every completed call leaves its counters at zero
  * again, so it can be reused as is by calls ordered on one stream.
@@ -109,7 +149,7 @@ size_t dspk_qgemm_workspace_bytes(int32_t n, int32_t k, int32_t m);
  * row ("mlx-dspark" wiki summary, "Key techniques", custom kernels bullet;
  * the 1-bit counter-example in "mlx-dspark 0.7.0", "PrismML Bonsai 27B").
  *
- *   w         : weight descriptor (see dspk_qweight).
+ *   w         : tiled weight (see dspk_tiled_weight, dspk_qweight_pack).
  *   x         : bf16 activations, chunk-major [k/8][ldx][8] (see above):
  *               ldx = rows per chunk, m <= ldx <= 65536; 16-byte aligned.
  *   m         : rows, 1 .. DSPK_MAX_ROWS.
@@ -123,7 +163,7 @@ size_t dspk_qgemm_workspace_bytes(int32_t n, int32_t k, int32_t m);
  * m out of 1..32, workspace too small), DSPK_EUNSUPPORTED (bits not in
  * {4, 8, 16}, group != 64), DSPK_EDEVICE.
  */
-int dspk_qgemm_verify(const dspk_qweight *w, const uint16_t *x, int64_t ldx, int32_t m,
+int dspk_qgemm_verify(const dspk_tiled_weight *w, const uint16_t *x, int64_t ldx, int32_t m,
                       void *y, int32_t y_dtype, int64_t ldy,
                       void *workspace, size_t ws_bytes, void *stream);
 
@@ -136,7 +176,7 @@ int dspk_qgemm_verify(const dspk_qweight *w, const uint16_t *x, int64_t ldx, int
  * agree with theirs to fp32 rounding (both within the error bound of the
  * single call), and are themselves deterministic.
  */
-int dspk_qgemm_verify_grouped(int32_t count, const dspk_qweight *w,
+int dspk_qgemm_verify_grouped(int32_t count, const dspk_tiled_weight *w,
                               const uint16_t *x, int64_t ldx, int32_t m,
                               void *const *y, int32_t y_dtype, const int64_t *ldy,
                               void *workspace, size_t ws_bytes, void *stream);
@@ -152,7 +192,7 @@ size_t dspk_lmhead_workspace_bytes(int32_t v, int32_t m);
  * summary, "Architecture").  The tie rule is the reading taken where the
  * project page leaves ties to floating-point rounding.
  *
- *   w         : vocabulary head, same format as dspk_qgemm_verify.
+ *   w         : vocabulary head, tiled like dspk_qgemm_verify's weights.
  *   h         : bf16 final hidden rows, chunk-major [k/8][ldh][8], m <= ldh,
  *               16-byte aligned.
  *   argmax    : int32 [m] output.
@@ -161,7 +201,7 @@ size_t dspk_lmhead_workspace_bytes(int32_t v, int32_t m);
  *               zero-filled before first use.
  * The result is deterministic (independent of workgroup order).
  */
-int dspk_lmhead_argmax(const dspk_qweight *w, const uint16_t *h, int64_t ldh, int32_t m,
+int dspk_lmhead_argmax(const dspk_tiled_weight *w, const uint16_t *h, int64_t ldh, int32_t m,
                        int32_t *argmax, float *logits, int64_t ldl,
                        void *workspace, size_t ws_bytes, void *stream);
 

@@ -32,8 +32,14 @@ class DspkError(RuntimeError):
 
 
 class QWeightDesc(ctypes.Structure):
+    """dspk_qweight: a weight in the interchange layout (input of the packing)."""
     _fields_ = [("n", c_int32), ("k", c_int32), ("bits", c_int32), ("group", c_int32),
                 ("codes", c_void_p), ("scales", c_void_p), ("biases", c_void_p)]
+
+
+class TiledDesc(ctypes.Structure):
+    """dspk_tiled_weight: a weight in the library's tiled layout."""
+    _fields_ = [("n", c_int32), ("k", c_int32), ("bits", c_int32), ("group", c_int32), ("tiles", c_void_p)]
 
 
 _LIB = None
@@ -52,14 +58,16 @@ def lib() -> ctypes.CDLL:
     sig = {
         "dspk_version": (c_int32, []),
         "dspk_last_error": (ctypes.c_char_p, []),
+        "dspk_tiled_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
+        "dspk_qweight_pack": (c_int32, [P(QWeightDesc), c_void_p, c_size_t, c_void_p]),
         "dspk_qgemm_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
-        "dspk_qgemm_verify": (c_int32, [P(QWeightDesc), c_void_p, c_int64, c_int32, c_void_p, c_int32,
+        "dspk_qgemm_verify": (c_int32, [P(TiledDesc), c_void_p, c_int64, c_int32, c_void_p, c_int32,
                                         c_int64, c_void_p, c_size_t, c_void_p]),
-        "dspk_qgemm_verify_grouped": (c_int32, [c_int32, P(QWeightDesc), c_void_p, c_int64, c_int32,
+        "dspk_qgemm_verify_grouped": (c_int32, [c_int32, P(TiledDesc), c_void_p, c_int64, c_int32,
                                                 P(c_void_p), c_int32, P(c_int64), c_void_p, c_size_t,
                                                 c_void_p]),
         "dspk_lmhead_workspace_bytes": (c_size_t, [c_int32, c_int32]),
-        "dspk_lmhead_argmax": (c_int32, [P(QWeightDesc), c_void_p, c_int64, c_int32, c_void_p, c_void_p,
+        "dspk_lmhead_argmax": (c_int32, [P(TiledDesc), c_void_p, c_int64, c_int32, c_void_p, c_void_p,
                                          c_int64, c_void_p, c_size_t, c_void_p]),
         "dspk_accept_greedy": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
                                          c_void_p]),
@@ -125,14 +133,22 @@ def to_chunk_major(x, ldm: int | None = None):
 
 # ---------------------------------------------------------------- weights
 class DeviceQWeight:
-    """A weight matrix in device memory plus its C descriptor."""
+    """A weight matrix in device memory, in the library's tiled layout, plus
+    its C descriptor.  Built from the interchange layout (packed codes,
+    row-major fp16 scales/biases [n][k/64]) by dspk_qweight_pack."""
 
-    def __init__(self, n: int, k: int, bits: int, codes, scales=None, biases=None):
+    def __init__(self, n: int, k: int, bits: int, codes, scales=None, biases=None, stream=None):
+        import torch
         self.n, self.k, self.bits = n, k, bits
-        self.codes, self.scales, self.biases = codes, scales, biases
-        self.desc = QWeightDesc(n, k, bits, 64, codes.data_ptr(),
-                                None if scales is None else scales.data_ptr(),
-                                None if biases is None else biases.data_ptr())
+        src = QWeightDesc(n, k, bits, 64, codes.data_ptr(),
+                          None if scales is None else scales.data_ptr(),
+                          None if biases is None else biases.data_ptr())
+        nbytes = tiled_bytes(n, k, bits)
+        if nbytes == 0:
+            raise ValueError(f"invalid weight shape n={n} k={k} bits={bits}")
+        self.tiles = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
+        _check(lib().dspk_qweight_pack(ctypes.byref(src), self.tiles.data_ptr(), nbytes, _stream(stream)))
+        self.desc = TiledDesc(n, k, bits, 64, self.tiles.data_ptr())
 
     @classmethod
     def upload(cls, w: inputs.QWeight, device="cuda"):
@@ -141,17 +157,20 @@ class DeviceQWeight:
                                                       else w.codes.view(np.int16))).to(device)
         sc = bi = None
         if w.bits != 16:
-            # the library's scale/bias arrays are group-major [k/64][n]
-            sc = torch.from_numpy(np.ascontiguousarray(w.scales.view(np.int16).T)).to(device)
-            bi = torch.from_numpy(np.ascontiguousarray(w.biases.view(np.int16).T)).to(device)
-        return cls(w.n, w.k, w.bits, codes, sc, bi)
+            sc = torch.from_numpy(np.ascontiguousarray(w.scales.view(np.int16))).to(device)
+            bi = torch.from_numpy(np.ascontiguousarray(w.biases.view(np.int16))).to(device)
+        out = cls(w.n, w.k, w.bits, codes, sc, bi)
+        torch.cuda.current_stream().synchronize()      # the sources may be freed now
+        return out
 
     @property
     def nbytes(self) -> int:
-        b = self.codes.numel() * self.codes.element_size()
-        if self.scales is not None:
-            b += 2 * self.scales.numel() * self.scales.element_size()
-        return b
+        """Algorithmic bytes of the weight (codes plus fp16 scale and bias per group)."""
+        return inputs.weight_bytes(self.n, self.k, self.bits)
+
+
+def tiled_bytes(n: int, k: int, bits: int) -> int:
+    return lib().dspk_tiled_bytes(n, k, bits)
 
 
 # ------------------------------------------------------------ entry points
@@ -188,7 +207,7 @@ def qgemm_verify(w: DeviceQWeight, x, m: int, y, workspace=None, stream=None) ->
 
 def qgemm_verify_grouped(ws: list, x, m: int, ys: list, workspace=None, stream=None) -> None:
     cnt = len(ws)
-    descs = (QWeightDesc * cnt)(*[w.desc for w in ws])
+    descs = (TiledDesc * cnt)(*[w.desc for w in ws])
     yptr = (c_void_p * cnt)(*[y.data_ptr() for y in ys])
     ldy = (c_int64 * cnt)(*[_rows(y, "y") for y in ys])
     dt = DSPK_BF16 if ys[0].element_size() == 2 else DSPK_F32

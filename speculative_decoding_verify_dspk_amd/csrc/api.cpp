@@ -31,14 +31,20 @@ int ok() {
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+int check_shape(int32_t n, int32_t k, int32_t bits, int32_t group, const char *who) {
+    if (bits != 4 && bits != 8 && bits != 16)
+        return fail(DSPK_EUNSUPPORTED, "%s: bits=%d (supported: 4, 8, 16)", who, bits);
+    if (group != DSPK_GROUP) return fail(DSPK_EUNSUPPORTED, "%s: group=%d (must be 64)", who, group);
+    if (n < 1) return fail(DSPK_EINVAL, "%s: n=%d must be >= 1", who, n);
+    if (k < DSPK_GROUP || k % DSPK_GROUP) return fail(DSPK_EINVAL, "%s: k=%d must be a positive multiple of 64", who, k);
+    return DSPK_OK;
+}
+
+// A weight in the interchange layout (input of the packing call).
 int check_weight(const dspk_qweight *w, const char *who) {
     if (w == nullptr) return fail(DSPK_EINVAL, "%s: weight descriptor is NULL", who);
-    if (w->bits != 4 && w->bits != 8 && w->bits != 16)
-        return fail(DSPK_EUNSUPPORTED, "%s: bits=%d (supported: 4, 8, 16)", who, w->bits);
-    if (w->group != DSPK_GROUP) return fail(DSPK_EUNSUPPORTED, "%s: group=%d (must be 64)", who, w->group);
-    if (w->n < 1) return fail(DSPK_EINVAL, "%s: n=%d must be >= 1", who, w->n);
-    if (w->k < DSPK_GROUP || w->k % DSPK_GROUP)
-        return fail(DSPK_EINVAL, "%s: k=%d must be a positive multiple of 64", who, w->k);
+    int rc = check_shape(w->n, w->k, w->bits, w->group, who);
+    if (rc) return rc;
     if (w->codes == nullptr || !aligned(w->codes, 16))
         return fail(DSPK_EINVAL, "%s: codes must be a non-NULL 16-byte aligned device pointer", who);
     if (w->bits == 16) {
@@ -47,9 +53,19 @@ int check_weight(const dspk_qweight *w, const char *who) {
     } else {
         if (w->scales == nullptr || w->biases == nullptr)
             return fail(DSPK_EINVAL, "%s: scales and biases are required for bits=%d", who, w->bits);
-        if (!aligned(w->scales, 4) || !aligned(w->biases, 4))
-            return fail(DSPK_EINVAL, "%s: scales and biases must be 4-byte aligned", who);
+        if (!aligned(w->scales, 2) || !aligned(w->biases, 2))
+            return fail(DSPK_EINVAL, "%s: scales and biases must be 2-byte aligned", who);
     }
+    return DSPK_OK;
+}
+
+// A weight in the tiled layout (what the projection kernels read).
+int check_tiled(const dspk_tiled_weight *w, const char *who) {
+    if (w == nullptr) return fail(DSPK_EINVAL, "%s: weight descriptor is NULL", who);
+    int rc = check_shape(w->n, w->k, w->bits, w->group, who);
+    if (rc) return rc;
+    if (w->tiles == nullptr || !aligned(w->tiles, 256))
+        return fail(DSPK_EINVAL, "%s: tiles must be a non-NULL 256-byte aligned device pointer", who);
     return DSPK_OK;
 }
 
@@ -82,7 +98,7 @@ void fill_plan(dspk::GemmLaunch &L, const dspk::GemmPlan &pl, const uint16_t *x,
     L.total_cg = pl.total_cg;
 }
 
-int qgemm_common(int32_t count, const dspk_qweight *w, const uint16_t *x, int64_t ldx, int32_t m,
+int qgemm_common(int32_t count, const dspk_tiled_weight *w, const uint16_t *x, int64_t ldx, int32_t m,
                  void *const *y, int32_t y_dtype, const int64_t *ldy, void *workspace, size_t ws_bytes,
                  void *stream, const char *who) {
     if (count < 1 || count > DSPK_MAX_GROUPED)
@@ -91,7 +107,7 @@ int qgemm_common(int32_t count, const dspk_qweight *w, const uint16_t *x, int64_
     if (y_dtype != DSPK_F32 && y_dtype != DSPK_BF16)
         return fail(DSPK_EINVAL, "%s: y_dtype=%d (DSPK_F32 or DSPK_BF16)", who, y_dtype);
     for (int i = 0; i < count; ++i) {
-        int rc = check_weight(&w[i], who);
+        int rc = check_tiled(&w[i], who);
         if (rc) return rc;
         if (w[i].k != w[0].k || w[i].bits != w[0].bits)
             return fail(DSPK_EINVAL, "%s: grouped weights must share k and bits", who);
@@ -119,9 +135,7 @@ int qgemm_common(int32_t count, const dspk_qweight *w, const uint16_t *x, int64_
     int cg = 0;
     for (int i = 0; i < count; ++i) {
         dspk::GemmProblem &P = L.p[i];
-        P.codes = w[i].codes;
-        P.scales = w[i].scales;
-        P.biases = w[i].biases;
+        P.tiles = w[i].tiles;
         P.y = y[i];
         P.ldy = ldy[i];
         P.n = w[i].n;
@@ -135,9 +149,24 @@ int qgemm_common(int32_t count, const dspk_qweight *w, const uint16_t *x, int64_
 
 extern "C" {
 
-int dspk_version(void) { return 100; }
+int dspk_version(void) { return 200; }
 
 const char *dspk_last_error(void) { return g_err.c_str(); }
+
+size_t dspk_tiled_bytes(int32_t n, int32_t k, int32_t bits) { return dspk::tiled_bytes(n, k, bits); }
+
+int dspk_qweight_pack(const dspk_qweight *w, void *tiles, size_t tiles_bytes, void *stream) {
+    const char *who = "dspk_qweight_pack";
+    int rc = check_weight(w, who);
+    if (rc) return rc;
+    const size_t need = dspk::tiled_bytes(w->n, w->k, w->bits);
+    if (tiles == nullptr || !aligned(tiles, 256))
+        return fail(DSPK_EINVAL, "%s: tiles must be a non-NULL 256-byte aligned device pointer", who);
+    if (tiles_bytes < need) return fail(DSPK_EINVAL, "%s: tiles %zu bytes < %zu required", who, tiles_bytes, need);
+    return launch_result(dspk::launch_pack(w->n, w->k, w->bits, w->codes, w->scales, w->biases, tiles,
+                                           (hipStream_t)stream),
+                         who);
+}
 
 size_t dspk_qgemm_workspace_bytes(int32_t n, int32_t k, int32_t m) {
     if (n < 1 || k < DSPK_GROUP || k % DSPK_GROUP || m < 1 || m > DSPK_MAX_ROWS) return 0;
@@ -149,14 +178,14 @@ size_t dspk_qgemm_workspace_bytes(int32_t n, int32_t k, int32_t m) {
     return most;
 }
 
-int dspk_qgemm_verify(const dspk_qweight *w, const uint16_t *x, int64_t ldx, int32_t m, void *y,
+int dspk_qgemm_verify(const dspk_tiled_weight *w, const uint16_t *x, int64_t ldx, int32_t m, void *y,
                       int32_t y_dtype, int64_t ldy, void *workspace, size_t ws_bytes, void *stream) {
     void *ys[1] = {y};
     int64_t lds[1] = {ldy};
     return qgemm_common(1, w, x, ldx, m, ys, y_dtype, lds, workspace, ws_bytes, stream, "dspk_qgemm_verify");
 }
 
-int dspk_qgemm_verify_grouped(int32_t count, const dspk_qweight *w, const uint16_t *x, int64_t ldx, int32_t m,
+int dspk_qgemm_verify_grouped(int32_t count, const dspk_tiled_weight *w, const uint16_t *x, int64_t ldx, int32_t m,
                               void *const *y, int32_t y_dtype, const int64_t *ldy, void *workspace,
                               size_t ws_bytes, void *stream) {
     return qgemm_common(count, w, x, ldx, m, y, y_dtype, ldy, workspace, ws_bytes, stream,
@@ -169,10 +198,10 @@ size_t dspk_lmhead_workspace_bytes(int32_t v, int32_t m) {
     return dspk::plan_gemm(1, &v, 1 << 20, m, 8, true).ws_bytes;
 }
 
-int dspk_lmhead_argmax(const dspk_qweight *w, const uint16_t *h, int64_t ldh, int32_t m, int32_t *argmax,
+int dspk_lmhead_argmax(const dspk_tiled_weight *w, const uint16_t *h, int64_t ldh, int32_t m, int32_t *argmax,
                        float *logits, int64_t ldl, void *workspace, size_t ws_bytes, void *stream) {
     const char *who = "dspk_lmhead_argmax";
-    int rc = check_weight(w, who);
+    int rc = check_tiled(w, who);
     if (rc) return rc;
     rc = check_rows(h, ldh, m, w->k, who);
     if (rc) return rc;
@@ -197,9 +226,7 @@ int dspk_lmhead_argmax(const dspk_qweight *w, const uint16_t *h, int64_t ldh, in
     L.logits = logits;
     L.ldl = ldl;
     dspk::GemmProblem &P = L.p[0];
-    P.codes = w->codes;
-    P.scales = w->scales;
-    P.biases = w->biases;
+    P.tiles = w->tiles;
     P.n = w->n;
     P.cg_begin = 0;
     return launch_result(dspk::launch_lmhead(L, w->bits, pl.grid, (hipStream_t)stream), who);

@@ -14,17 +14,36 @@ constexpr int kBlockCols = 16 * kTilesPerWave;          // columns per wave (64)
 constexpr int kMaxGrouped = 4;
 constexpr int kMaxRows = 32;
 
+// Tiled weight layout (the format every projection kernel reads; written by
+// dspk_qweight_pack).  A weight is cut into units of 64 output columns times
+// tile_k(bits) K elements -- 8 KiB of codes in every format -- stored unit
+// after unit, K fastest within a 64-column block, blocks in column order.
+// A unit is 8 slots of 1 KiB (one 16-byte piece per lane of a wave, in the
+// MFMA operand order of that lane) followed, for quantised formats, by the
+// scale/bias dwords of its groups (16 columns x tile_k/64 groups x 4 tiles).
+constexpr int tile_k(int bits) { return bits == 16 ? 64 : bits == 8 ? 128 : 256; }
+constexpr int tile_groups(int bits) { return tile_k(bits) / 64; }
+constexpr int tile_unit_bytes(int bits) { return 8192 + (bits == 16 ? 0 : 256 * tile_groups(bits)); }
+size_t tiled_bytes(int32_t n, int32_t k, int bits);
+hipError_t launch_pack(int32_t n, int32_t k, int bits, const void *codes, const uint16_t *scales,
+                       const uint16_t *biases, void *tiles, hipStream_t s);
+
+// Register-ring depth (units in flight per wave) and workgroups per CU of the
+// projection kernel, by weight format and 16-row tiles; both keep a wave
+// within the registers that OCC waves per SIMD leave it.
+constexpr int kernel_depth(int bits, int mt) { return 2 + 0 * bits * mt; }
+constexpr int kernel_occ(int bits, int mt) { return (bits == 4 && mt == 2) ? 1 : 2; }
+
 // Work of a projection launch is a list of quads: (weight, 64-column block,
-// four consecutive K stages), one stage per wave of a workgroup.  Quads are
+// four consecutive units), one unit per wave of a workgroup.  Quads are
 // numbered weight by weight, block by block, K first, and each workgroup of
 // the persistent grid takes one contiguous range of them ("stream-K"), so
-// every workgroup streams the same number of weight bytes.  A block whose
-// quads straddle workgroups is finished by the last of them to arrive, adding
-// the pieces in workgroup order.  Grouped weights share k, bits and rows.
+// every workgroup streams the same number of weight bytes -- and, with the
+// tiled layout, one contiguous run of memory.  A block whose quads straddle
+// workgroups is finished by the last of them to arrive, adding the pieces in
+// workgroup order.  Grouped weights share k, bits and rows.
 struct GemmProblem {
-    const void *codes;        // packed codes (bits 4/8) or bf16 weights (bits 16)
-    const uint16_t *scales;   // fp16 [n][k/64]
-    const uint16_t *biases;   // fp16 [n][k/64]
+    const void *tiles;        // tiled weight (tiled_bytes(n, k, bits) bytes)
     void *y;                  // output [m][ldy]
     int64_t ldy;
     int32_t n;
@@ -33,12 +52,12 @@ struct GemmProblem {
 
 struct GemmLaunch {
     GemmProblem p[kMaxGrouped];
-    const uint16_t *x;        // bf16 rows [m][ldx]
+    const uint16_t *x;        // bf16 rows, chunk-major [k/8][ldx][8]
     int64_t ldx;
     int32_t count;
     int32_t m;
     int32_t k;
-    int32_t nst;              // K stages per block
+    int32_t nst;              // units per block: ceil(k / tile_k)
     int32_t nq;               // quads per block: ceil(nst / 4)
     int32_t quads;            // quads of the launch
     int32_t total_cg;         // blocks of the launch
@@ -60,8 +79,6 @@ struct GemmPlan {
     bool fits;                // quads * grid < 2^31 (the kernel's index range)
     size_t off_counters, off_keys, off_partial, ws_bytes;
 };
-// K elements of one wave's stage for a weight format
-int stage_k(int bits);
 GemmPlan plan_gemm(int count, const int32_t *n, int32_t k, int32_t m, int bits, bool argmax);
 int device_cus();
 

@@ -1,0 +1,106 @@
+// Conversion of a weight from its interchange layout (packed codes and
+// row-major fp16 scales/biases per 64-wide K group) into the tiled layout the
+// projection kernels stream.  Run once per weight, when it is loaded; a pure
+// permutation of bytes (codes and fp16 bit patterns are copied unchanged).
+//
+// Tiled layout, for a weight of n columns (output features) and k inputs:
+//   KU = 128 (8-bit), 256 (4-bit), 64 (bf16) K elements per unit;
+//   NST = ceil(k / KU) units per 64-column block, NB = ceil(n / 64) blocks;
+//   unit (b, u) starts at byte ((b * NST) + u) * UNIT, UNIT = 8192 + 256 * KU/64
+//   for quantised formats and 8192 for bf16.
+// Inside a unit, slot i (0..7) is 1 KiB: 16 bytes for each lane l = c + 16 j
+// (c = l % 16, j = l / 16) of a wave, holding for column n = 64 b + 16 t + c:
+//   8-bit : i = 4 g + t, the 16 codes of K = KU u + 64 g + 16 j + 0..15 (one byte each);
+//   4-bit : i = 4 p + t, 8 bytes of codes of group 2p then 8 bytes of group 2p+1,
+//           each the 16 codes of K = KU u + 64 g + 16 j + 0..15 (LSB-first nibbles);
+//   bf16  : i = 4 h + t, the 8 weights of K = KU u + 16 j + 8 h + 0..7.
+// Quantised formats then hold, at byte 8192 + 16 * KU/64 * c + 16 g + 4 t, the
+// dword (scale | bias << 16) of group KU/64 * u + g of column 64 b + 16 t + c.
+// Columns past n and K past k hold zeros (code 0, scale 0, bias 0).
+#include "dspk_internal.h"
+
+namespace dspk {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// One workgroup of 64 threads per unit.
+template <int BITS>
+__global__ __launch_bounds__(64) void pack_kernel(int32_t n, int32_t k, const unsigned char *__restrict__ codes,
+                                                  const uint16_t *__restrict__ scales,
+                                                  const uint16_t *__restrict__ biases, unsigned char *__restrict__ tiles,
+                                                  int32_t nst) {
+    constexpr int KU = tile_k(BITS), GS = tile_groups(BITS), UNIT = tile_unit_bytes(BITS);
+    const int lane = threadIdx.x, c = lane & 15, j = lane >> 4;
+    const int b = blockIdx.x / nst, u = blockIdx.x % nst;
+    const size_t rowbytes = (size_t)k * BITS / 8;
+    unsigned char *dst = tiles + (size_t)blockIdx.x * UNIT;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int t = i & 3, hi = i >> 2;
+        const int col = 64 * b + 16 * t + c;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (BITS == 8) {
+            const int k0 = KU * u + 64 * hi + 16 * j;
+            if (col < n && k0 < k) v = *(const u32x4 *)(codes + col * rowbytes + k0);
+        } else if (BITS == 4) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int k0 = KU * u + 64 * (2 * hi + half) + 16 * j;
+                if (col < n && k0 < k) {
+                    const u32x2 p = *(const u32x2 *)(codes + col * rowbytes + k0 / 2);
+                    v[2 * half] = p[0];
+                    v[2 * half + 1] = p[1];
+                }
+            }
+        } else {
+            const int k0 = KU * u + 16 * j + 8 * hi;
+            if (col < n && k0 < k) v = *(const u32x4 *)(codes + col * rowbytes + 2 * k0);
+        }
+        *(u32x4 *)(dst + 1024 * i + 16 * lane) = v;
+    }
+    if (BITS != 16 && j == 0) {
+        const int groups = k / 64;
+        uint32_t *sb = (uint32_t *)(dst + 8192 + 16 * GS * c);
+#pragma unroll
+        for (int g = 0; g < GS; ++g)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int col = 64 * b + 16 * t + c;
+                const int gk = GS * u + g;
+                uint32_t d = 0u;
+                if (col < n && gk < groups)
+                    d = (uint32_t)scales[(size_t)col * groups + gk] |
+                        ((uint32_t)biases[(size_t)col * groups + gk] << 16);
+                sb[4 * g + t] = d;
+            }
+    }
+}
+
+}  // namespace
+
+size_t tiled_bytes(int32_t n, int32_t k, int bits) {
+    if (n < 1 || k < 64 || k % 64 || (bits != 4 && bits != 8 && bits != 16)) return 0;
+    const size_t nb = ((size_t)n + 63) / 64, nst = ((size_t)k + tile_k(bits) - 1) / tile_k(bits);
+    return nb * nst * (size_t)tile_unit_bytes(bits);
+}
+
+hipError_t launch_pack(int32_t n, int32_t k, int bits, const void *codes, const uint16_t *scales,
+                       const uint16_t *biases, void *tiles, hipStream_t s) {
+    const int nst = (k + tile_k(bits) - 1) / tile_k(bits);
+    const int64_t units = ((int64_t)n + 63) / 64 * nst;
+    if (units > 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)units), block(64);
+    const unsigned char *cb = (const unsigned char *)codes;
+    unsigned char *tb = (unsigned char *)tiles;
+    switch (bits) {
+        case 4: hipLaunchKernelGGL(pack_kernel<4>, grid, block, 0, s, n, k, cb, scales, biases, tb, nst); break;
+        case 8: hipLaunchKernelGGL(pack_kernel<8>, grid, block, 0, s, n, k, cb, scales, biases, tb, nst); break;
+        case 16: hipLaunchKernelGGL(pack_kernel<16>, grid, block, 0, s, n, k, cb, scales, biases, tb, nst); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace dspk

@@ -7,15 +7,14 @@
 // weight group dequantised once and reused for every row).
 //
 // How (MI355X-first, not the pages' Metal kernel):
-// * The weights are the only large stream.  They move HBM -> LDS with
-//   direct-to-LDS loads (global_load_lds_dwordx4, non-temporal), whole 16-byte
-//   chunks of 64 weight rows per instruction, into a double-buffered stage per
-//   wave, XOR-swizzled so the MFMA-order reads (ds_read_b128) are free of bank
-//   conflicts.  The per-group fp16 scale/bias pairs ride the same path
-//   (4- or 2-byte direct loads).  The stage's activation fragments
-//   (L2-resident) come into registers alongside.  Each wave requests its next
-//   stage before it waits for the current one, so two stages are in flight
-//   while it waits and one while it computes.
+// * The weights are the only large stream.  They are read in the library's
+//   tiled layout (pack.hip): units of 64 columns x one K slice, 8 KiB of codes
+//   plus their scale/bias dwords, already in the order in which each lane
+//   feeds the matrix cores.  A wave loads a unit straight into registers with
+//   eight fully coalesced 1 KiB global_load_dwordx4 (non-temporal) plus one
+//   16-byte scale/bias load per group, DEPTH units deep, so a workgroup's
+//   four waves read one contiguous 35 KiB run per step and the whole launch
+//   sweeps memory in order.  Nothing passes through LDS on the way in.
 // * The group is the MFMA contraction unit.  Codes 0..255 (and 128+q for
 //   4-bit) are exact in bf16 and the rows are bf16, so
 //     sum_{r in group} x*w = s * sum x*q + b * sum x
@@ -26,16 +25,15 @@
 // * M rows pad to 16 (MT = 1) or 32 (MT = 2) MFMA rows; the weight fragment is
 //   converted once and multiplied into every row tile, so the weight bytes per
 //   call do not depend on M.
-// * Work unit = a "quad": one 64-column block times four consecutive K stages,
-//   one stage per wave of a four-wave workgroup, so the workgroup reads four
-//   adjacent chunks of the same 64 rows at once.  One persistent workgroup per
-//   CU takes an equal contiguous range of the quads of the whole launch
-//   (stream-K over workgroups), so small and large weights alike keep every CU
-//   streaming.  At the end of each block piece the four waves add their
-//   partial sums through LDS (fixed order), each wave keeping one 16-column
-//   tile; a block split between workgroups is completed by the last of them to
-//   arrive, which adds the pieces in workgroup order.  Results do not depend
-//   on scheduling.  Pieces and arrival counters move through device-scope
+// * Work unit of a workgroup = a "quad": one 64-column block times four
+//   consecutive units, one per wave.  Persistent workgroups (OCC per CU) take
+//   equal contiguous ranges of the quads of the whole launch (stream-K over
+//   workgroups), so small and large weights alike keep every CU streaming.
+//   At the end of each block piece the four waves add their partial sums
+//   through LDS (fixed order), each wave keeping one 16-column tile; a block
+//   split between workgroups is completed by the last of them to arrive,
+//   which adds the pieces in workgroup order.  Results do not depend on
+//   scheduling.  Pieces and arrival counters move through device-scope
 //   atomic accesses, so no cache flush is needed.
 #include "dspk_internal.h"
 
@@ -114,147 +112,37 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, int col) {
     return ((unsigned long long)u << 32) | (unsigned long long)(0xffffffffu - (uint32_t)col);
 }
 
-// Stage geometry.  A stage is one wave's share of a quad: 64 weight rows times
-// KS = 128 K elements (64 for bf16 weights), SB bytes per row; GS = 64-wide K
-// groups per stage.  The stage's scale and bias halves (group-major arrays,
-// so the 64 columns of one group are 128 contiguous bytes) come with 2-byte
-// direct loads, one per group and array, each landing in a 4-byte LDS slot.
-//
-// OCC workgroups share a CU.  DEPTH = stages of a wave's LDS ring: a wave
-// requests stage i + DEPTH - 1 before it waits for stage i, so DEPTH stages
-// are in flight while it waits and DEPTH - 1 while it computes.
-#ifndef DSPK_OCC
-#define DSPK_OCC 1
-#endif
-#ifndef DSPK_DEPTH
-#define DSPK_DEPTH 4
-#endif
-constexpr int OCC = DSPK_OCC;
-constexpr int DEPTH = DSPK_DEPTH;
-// 16-column tiles posted per pass of the in-workgroup sum
-constexpr int CTILES = OCC == 1 ? kTilesPerWave : kTilesPerWave / 2;
-
+// Unit geometry of a weight format: KU K elements per unit, GS = KU / 64
+// groups, SBQ 16-byte scale/bias loads per lane (one per group: the dwords of
+// the lane's four column tiles), UNIT bytes per unit.
 template <int BITS>
 struct Cfg {
-    static constexpr int KS = BITS == 16 ? 64 : 128;            // K per stage
-    static constexpr int SB = KS * BITS / 8;                    // bytes of a weight row per stage
-    static constexpr int GS = KS / 64;                          // groups per stage
-    static constexpr int LPR = SB / 16;                         // 16-byte chunks per weight row
-    static constexpr int RPI = 1024 / SB;                       // weight rows per load instruction
-    static constexpr int NDMA = 64 / RPI;                       // weight load instructions per stage
-    static constexpr int B_BYTES = kBlockCols * SB;             // one wave's weights per stage
-    static constexpr int SB_LOADS = BITS == 16 ? 0 : GS;        // loads per array (scales, biases)
-    static constexpr int SBP_BYTES = 2 * SB_LOADS * 256;        // [scales g][biases g] x 64 lanes x 4 bytes
-    static constexpr int WAVE_STAGE = B_BYTES + SBP_BYTES;
-    static constexpr int RING = DEPTH * kWavesPerWG * WAVE_STAGE;
-    static_assert(RING + kWavesPerWG * CTILES * kWave * 16 <= 163840 / OCC, "LDS budget per workgroup");
+    static constexpr int KU = tile_k(BITS);
+    static constexpr int GS = tile_groups(BITS);
+    static constexpr int SBQ = BITS == 16 ? 0 : GS;
+    static constexpr int UNIT = tile_unit_bytes(BITS);
 };
 
-template <int LPR>
-__device__ __forceinline__ int swz(int row) {                 // chunk XOR key of a weight row
-    return (row / (16 / LPR)) & (LPR - 1);
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ void dma16(const void *g, lds_void *l) {
-    __builtin_amdgcn_global_load_lds(g, l, 16, 0, 2 /* non-temporal */);
-}
-__device__ __forceinline__ void dma4(const void *g, lds_void *l) {
-    __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
-}
-__device__ __forceinline__ void dma2(const void *g, lds_void *l) {
-    __builtin_amdgcn_global_load_lds(g, l, 2, 0, 0);
-}
-
-// Wait until at most N of this wave's vector memory operations are pending
-// (they retire in issue order).  The builtin keeps the compiler's own count
-// of outstanding loads in step (so it adds no waits of its own for data that
-// this wait already covers); the empty asm keeps every memory access on its
-// side of the wait.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-    asm volatile("" ::: "memory");
-}
-__device__ __forceinline__ void wait_vm_all() { wait_vm<0>(); }
+// 16-column tiles posted per pass of the in-workgroup sum
+constexpr int CTILES = kTilesPerWave;
 
 // Workgroup barrier for LDS traffic only: it does not wait for this wave's
-// outstanding global loads (the next stage stays in flight across it).
+// outstanding global loads (the next units stay in flight across it).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// LDS accesses through restrict-qualified parameters: once inlined they carry
-// alias-scope information, which tells the compiler that they do not touch
-// the stage buffers that direct-to-LDS loads are filling (it would otherwise
-// wait for those loads).  The stage a wave reads has always landed already:
-// the explicit wait_vm before every compute guarantees it.
 __device__ __forceinline__ f32x4 lds_get(const f32x4 *__restrict__ p) { return *p; }
 __device__ __forceinline__ void lds_put(f32x4 *__restrict__ p, f32x4 v) { *p = v; }
 
-// The scale/bias dwords of one stage for this lane's four columns, read with
-// one asm block that also waits for them.  Plain reads would be merged into
-// ds_read2 instructions, which drop the alias-scope information and make the
-// compiler wait for every load in flight; hidden from it, they need no such
-// wait (the stage has landed already), only the LDS wait inside the block.
-// lds = LDS byte address of this lane's first column; dword k of the result
-// is the word at lds + 256 * (k / 4) + 64 * (k % 4).
-__device__ __forceinline__ void lds_read_8x(uint32_t lds, uint32_t (&v)[8]) {
-    asm volatile(
-        "ds_read_b32 %0, %8\n\t"
-        "ds_read_b32 %1, %8 offset:64\n\t"
-        "ds_read_b32 %2, %8 offset:128\n\t"
-        "ds_read_b32 %3, %8 offset:192\n\t"
-        "ds_read_b32 %4, %8 offset:256\n\t"
-        "ds_read_b32 %5, %8 offset:320\n\t"
-        "ds_read_b32 %6, %8 offset:384\n\t"
-        "ds_read_b32 %7, %8 offset:448\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        // early-clobber outputs: none may share the address register
-        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]),
-          "=&v"(v[7])
-        : "v"(lds)
-        : "memory");
+// Wait until every vector memory access of this wave has completed.
+__device__ __forceinline__ void wait_vm_all() {
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));     // vmcnt(0); expcnt, lgkmcnt not waited
+    asm volatile("" ::: "memory");
 }
 
-// The weight fragments of one stage for this lane, read with one asm block
-// that also waits for them (same reason as lds_read_8x: the compiler would
-// otherwise wait for the direct-to-LDS loads in flight).  For two lane
-// addresses a0, a1 and the four 16-column tiles t: v[h][t] = LDS[a_h + S*t].
-template <int S>
-__device__ __forceinline__ void lds_read_b128_2x4(uint32_t a0, uint32_t a1, u32x4 (&v)[2][4]) {
-    asm volatile(
-        "ds_read_b128 %0, %8\n\t"
-        "ds_read_b128 %1, %8 offset:%10\n\t"
-        "ds_read_b128 %2, %8 offset:%11\n\t"
-        "ds_read_b128 %3, %8 offset:%12\n\t"
-        "ds_read_b128 %4, %9\n\t"
-        "ds_read_b128 %5, %9 offset:%10\n\t"
-        "ds_read_b128 %6, %9 offset:%11\n\t"
-        "ds_read_b128 %7, %9 offset:%12\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]), "=&v"(v[1][0]), "=&v"(v[1][1]),
-          "=&v"(v[1][2]), "=&v"(v[1][3])
-        : "v"(a0), "v"(a1), "n"(S), "n"(2 * S), "n"(3 * S)
-        : "memory");
+__device__ __forceinline__ u32x4 load_nt(const unsigned char *p) {
+    return __builtin_nontemporal_load((const u32x4 *)p);
 }
-template <int S>
-__device__ __forceinline__ void lds_read_b64_2x4(uint32_t a0, uint32_t a1, u32x2 (&v)[2][4]) {
-    asm volatile(
-        "ds_read_b64 %0, %8\n\t"
-        "ds_read_b64 %1, %8 offset:%10\n\t"
-        "ds_read_b64 %2, %8 offset:%11\n\t"
-        "ds_read_b64 %3, %8 offset:%12\n\t"
-        "ds_read_b64 %4, %9\n\t"
-        "ds_read_b64 %5, %9 offset:%10\n\t"
-        "ds_read_b64 %6, %9 offset:%11\n\t"
-        "ds_read_b64 %7, %9 offset:%12\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]), "=&v"(v[1][0]), "=&v"(v[1][1]),
-          "=&v"(v[1][2]), "=&v"(v[1][3])
-        : "v"(a0), "v"(a1), "n"(S), "n"(2 * S), "n"(3 * S)
-        : "memory");
-}
+__device__ __forceinline__ u32x4 load16(const unsigned char *p) { return *(const u32x4 *)p; }
 
 // Result stores as asm: the compiler's count of outstanding memory operations
 // treats pending stores as out of order with the loads and would then wait for
@@ -290,11 +178,10 @@ __device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsig
 }
 
 template <int BITS, int MT, bool ARGMAX>
-__global__ __launch_bounds__(256, OCC) void qgemm_kernel(const GemmLaunch L) {
+__global__ __launch_bounds__(256, kernel_occ(BITS, MT)) void qgemm_kernel(const GemmLaunch L) {
     using C = Cfg<BITS>;
-    constexpr int SB = C::SB;
-    // ring of DEPTH stage buffers per wave: [slot][wave][weights | scales | biases]
-    __shared__ __attribute__((aligned(16))) unsigned char ring[C::RING];
+    constexpr int DEPTH = kernel_depth(BITS, MT);
+    constexpr int XB = MT == 1 ? 4 : 2;        // partial sums in flight when completing a split block
     // In-workgroup sum (each wave posts CTILES of its 16-column tiles per
     // pass, one 16-row tile at a time); after the main loop the same bytes
     // hold the argmax reduction.
@@ -321,14 +208,12 @@ __global__ __launch_bounds__(256, OCC) void qgemm_kernel(const GemmLaunch L) {
     const int GRID = gridDim.x;
     const int QU = KL->quads;                 // quads of the launch
     const int NQ = KL->nq;                    // quads per block
-    const int NST = KL->nst;                  // stages per block
-    const int LASTW = NST - 4 * (NQ - 1);     // waves with a stage in a block's last quad (1..4)
+    const int NST = KL->nst;                  // units per block
+    const int LASTW = NST - 4 * (NQ - 1);     // waves with a unit in a block's last quad (1..4)
     const int K = KL->k;
     const int G = K >> 6;
-    const int64_t rowbytes = (int64_t)K * BITS / 8;
     const int Q0 = quad_begin(QU, GRID, bid), Q1 = quad_begin(QU, GRID, bid + 1);
     const int M = KL->m;
-    unsigned char *const myring = ring + w * C::WAVE_STAGE;   // + slot * (4 * WAVE_STAGE)
 
     // global block -> weight index
     auto weight_of = [&](int gb) __attribute__((always_inline)) {
@@ -341,8 +226,8 @@ __global__ __launch_bounds__(256, OCC) void qgemm_kernel(const GemmLaunch L) {
 
     // This wave's quads in [Q0, Q1), walked with (quad, block, index in block).
     // A quad is skipped only when it is the last of its block and this wave
-    // has no stage in it; when NQ == 1 that holds for all of them, and the
-    // wave has no stage at all.
+    // has no unit in it; when NQ == 1 that holds for all of them, and the
+    // wave has no unit at all.
     struct Cur {
         int q, gb, qi;
     };
@@ -356,92 +241,58 @@ __global__ __launch_bounds__(256, OCC) void qgemm_kernel(const GemmLaunch L) {
                            ? 0
                            : (Q1 - Q0) - (skips_last ? (Q1 / NQ - Q0 / NQ) : 0);
 
-    u32x4 act[DEPTH][C::GS][MT][2];       // one set per ring slot
+    // One ring slot: a unit's eight code pieces and scale/bias dwords of this
+    // lane, and the matching activation fragments.
+    struct Slot {
+        u32x4 w[8];
+        u32x4 sb[C::SBQ > 0 ? C::SBQ : 1];
+        u32x4 a[C::GS][MT][2];
+    };
+    Slot ring[DEPTH];
 
-    // Request state, refreshed when the requests move to a new block: the
-    // weight's base pointers and each lane's 32-bit byte offsets of its rows
-    // (rows past n repeat the last one); a weight holds < 4 GiB of codes.
+    // Base of the block the requests are in (wave-uniform), refreshed when
+    // they move to a new block.
     int ib_gb = -1;
-    const unsigned char *ib_codes = nullptr;
-    const uint16_t *ib_scales = nullptr, *ib_biases = nullptr;
-    int ib_n = 1;
-    uint32_t ib_row[C::NDMA];
-    int ib_col = 0;             // this lane's column for the scale/bias loads
-    uint32_t ch16[C::NDMA];     // 16 * (swizzled chunk) of each weight load of this lane
-#pragma unroll
-    for (int i = 0; i < C::NDMA; ++i) {
-        const int r = i * C::RPI + lane / C::LPR;
-        ch16[i] = 16u * (uint32_t)((lane % C::LPR) ^ swz<C::LPR>(r));
-    }
-    // activations: chunk-major [k/8][ldm][8]; this lane's rows
+    const unsigned char *ib_base = nullptr;
+    // activations: chunk-major [k/8][ldm][8] bf16; byte offset of this lane's
+    // piece (chunk 2*j, row 16*mt + c) within a group's eight chunks
     const int LDM = (int)KL->ldx;
-    int xrowoff[MT];
+    const unsigned char *const xbase = (const unsigned char *)KL->x;
+    uint32_t xlane[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) xrowoff[mt] = 8 * min(16 * mt + c, M - 1);
+    for (int mt = 0; mt < MT; ++mt) xlane[mt] = (uint32_t)(2 * j * LDM + min(16 * mt + c, M - 1)) * 16u;
 
-    // Request this wave's stage of quad u into ring slot `slot`: 64 weight rows
-    // and their scale/bias halves, straight into LDS.  Chunks past the end of
-    // K (a short last stage) re-read valid data, so every load is
-    // unconditional.
-    auto issue = [&](const Cur &u, int slot) __attribute__((always_inline)) {
+    // Request this wave's unit of quad u and its activation fragments into
+    // slot s.  Lane (c, j) takes 16 bytes of each 1 KiB code slot and the
+    // dwords of its column c; units are contiguous, so a quad is one run.
+    auto issue = [&](const Cur &u, Slot &s) __attribute__((always_inline)) {
         if (u.gb != ib_gb) {
             ib_gb = u.gb;
-            const int pi = weight_of(u.gb);
-            const GemmProblem &P = KL->p[pi];
-            const int n0 = (u.gb - P.cg_begin) * kBlockCols;
-            ib_codes = (const unsigned char *)P.codes;
-            ib_scales = P.scales;
-            ib_biases = P.biases;
-#pragma unroll
-            for (int i = 0; i < C::NDMA; ++i) {
-                const int r = i * C::RPI + lane / C::LPR;
-                ib_row[i] = (uint32_t)min(n0 + r, P.n - 1) * (uint32_t)rowbytes;
-            }
-            ib_col = min(n0 + lane, P.n - 1);
-            ib_n = P.n;
+            const GemmProblem &P = KL->p[weight_of(u.gb)];
+            ib_base = (const unsigned char *)P.tiles + (size_t)(u.gb - P.cg_begin) * NST * C::UNIT;
         }
         const int st = 4 * u.qi + w;
-        unsigned char *Bw = myring + slot * (kWavesPerWG * C::WAVE_STAGE);
-        const uint32_t kb = (uint32_t)st * SB;
-        // chunks past the row end (a short last stage) re-read its last 16 bytes
+        const unsigned char *ub = ib_base + (size_t)st * C::UNIT;
 #pragma unroll
-        for (int i = 0; i < C::NDMA; ++i) {
-            const uint32_t off = min(kb + ch16[i], (uint32_t)rowbytes - 16u);
-            dma16(ib_codes + (ib_row[i] + off), (lds_void *)(Bw + i * 1024));
-        }
-        if constexpr (BITS != 16) {
-            const int g0 = st * C::GS;
-            unsigned char *S = Bw + C::B_BYTES;
+        for (int i = 0; i < 8; ++i) s.w[i] = load_nt(ub + i * 1024 + 16 * lane);
 #pragma unroll
-            for (int g = 0; g < C::GS; ++g) {
-                const int64_t o = (int64_t)min(g0 + g, G - 1) * ib_n + ib_col;
-                dma2(ib_scales + o, (lds_void *)(S + 256 * g));
-                dma2(ib_biases + o, (lds_void *)(S + 256 * (C::GS + g)));
+        for (int q = 0; q < C::SBQ; ++q) s.sb[q] = load16(ub + 8192 + c * (16 * C::SBQ) + 16 * q);
+        // lane (c, j) takes row 16*mt + c, K offsets 64*g + 16*j (+8): a
+        // wave-uniform byte offset per (g, h) plus a fixed lane offset.  The
+        // groups past the end of K (a short last unit) re-read the last one.
+        const int ng = min(C::GS, G - st * C::GS);
+#pragma unroll
+        for (int g = 0; g < C::GS; ++g)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int chunk = st * (C::KU / 8) + 8 * min(g, ng - 1) + h;
+                // < 2^32: the host checks k * ldm < 2^31
+                const uint32_t off = (uint32_t)chunk * (uint32_t)LDM * 16u;
+                const unsigned char *xs = xbase + (uint32_t)__builtin_amdgcn_readfirstlane((int)off);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) s.a[g][mt][h] = load16(xs + xlane[mt]);
             }
-        }
     };
-    // The activations of this wave's stage of quad u (L2-resident), requested
-    // with its weights: lane (c, j) takes row 16*mt + c, K offsets
-    // 64*g + 16*j (+8).
-    auto load_act = [&](const Cur &u, u32x4 (&a)[C::GS][MT][2]) __attribute__((always_inline)) {
-        const int st = 4 * u.qi + w;
-        const int last = K / 8 - 1;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-            for (int g = 0; g < C::GS; ++g) {
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int chunk = min(st * (C::KS / 8) + 8 * g + 2 * j + h, last);
-                    a[g][mt][h] = *(const u32x4 *)(KL->x + ((uint32_t)chunk * (uint32_t)LDM * 8u + xrowoff[mt]));
-                }
-            }
-        }
-    };
-    // vector memory instructions of one issue()
-    constexpr int ISSUE_OPS = C::NDMA + 2 * C::SB_LOADS + 2 * MT * C::GS;
-    constexpr int AHEAD_OPS = (DEPTH - 1) * ISSUE_OPS;
-    static_assert(AHEAD_OPS < 64, "the stages in flight must fit the vmcnt range");
 
     f32x4 y[NT][MT];
     auto zero_y = [&]() __attribute__((always_inline)) {
@@ -451,43 +302,10 @@ __global__ __launch_bounds__(256, OCC) void qgemm_kernel(const GemmLaunch L) {
             for (int mt = 0; mt < MT; ++mt) y[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     };
 
-    // MFMA work of this wave's stage of quad u, from ring slot `slot`
-    auto compute = [&](const Cur &u, const unsigned char *__restrict__ Bw, const u32x4 (&act)[C::GS][MT][2])
-        __attribute__((always_inline)) {
+    // MFMA work of this wave's unit of quad u, from slot s
+    auto compute = [&](const Cur &u, const Slot &s) __attribute__((always_inline)) {
         const int st = 4 * u.qi + w;
-        const int ng = min(C::GS, G - st * C::GS);
-        // scale/bias words of columns 16*t + c: [load][t], scales first
-        uint32_t sbw[BITS == 16 ? 1 : 2 * C::SB_LOADS][NT];
-        if constexpr (BITS != 16) {
-            const uint32_t base = (uint32_t)(uintptr_t)(lds_void *)(Bw + C::B_BYTES) + 4 * c;
-#pragma unroll
-            for (int h = 0; h < C::SB_LOADS; ++h) {
-                uint32_t v[8];
-                lds_read_8x(base + 512 * h, v);     // loads 2h and 2h+1 of the region
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    sbw[2 * h][t] = v[t];
-                    sbw[2 * h + 1][t] = v[4 + t];
-                }
-            }
-        }
-        // this lane's weight fragments of the stage: [g or chunk][t]; a tile's
-        // rows are 16 * SB bytes apart and the chunk swizzle of rows 16*t + c
-        // does not depend on t
-        const uint32_t lbase = (uint32_t)(uintptr_t)(lds_void *)Bw + (uint32_t)c * SB;
-        u32x4 wq[2][4];
-        u32x2 wq4[2][4];
-        if constexpr (BITS == 8) {
-            const int sw = swz<C::LPR>(c);
-            lds_read_b128_2x4<16 * SB>(lbase + 16 * ((4 * 0 + j) ^ sw), lbase + 16 * ((4 * 1 + j) ^ sw), wq);
-        } else if constexpr (BITS == 16) {
-            const int sw = swz<C::LPR>(c);
-            lds_read_b128_2x4<16 * SB>(lbase + 16 * ((2 * j) ^ sw), lbase + 16 * ((2 * j + 1) ^ sw), wq);
-        } else {
-            const int sw = swz<C::LPR>(c);
-            lds_read_b64_2x4<16 * SB>(lbase + 16 * ((0 + (j >> 1)) ^ sw) + 8 * (j & 1),
-                                      lbase + 16 * ((2 + (j >> 1)) ^ sw) + 8 * (j & 1), wq4);
-        }
+        const int ng = min(C::GS, G - st * C::GS);      // groups of a short last unit
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         const bf16x8 ones = as_bf16x8(u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 #pragma unroll
@@ -497,18 +315,19 @@ __global__ __launch_bounds__(256, OCC) void qgemm_kernel(const GemmLaunch L) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 if constexpr (BITS == 4) {
-                    a0[mt] = as_bf16x8(perm_x_for4(act[g][mt][0]));
-                    a1[mt] = as_bf16x8(perm_x_for4(act[g][mt][1]));
+                    a0[mt] = as_bf16x8(perm_x_for4(s.a[g][mt][0]));
+                    a1[mt] = as_bf16x8(perm_x_for4(s.a[g][mt][1]));
                 } else {
-                    a0[mt] = as_bf16x8(act[g][mt][0]);
-                    a1[mt] = as_bf16x8(act[g][mt][1]);
+                    a0[mt] = as_bf16x8(s.a[g][mt][0]);
+                    a1[mt] = as_bf16x8(s.a[g][mt][1]);
                 }
             }
             if constexpr (BITS == 16) {
+                // slot h*4 + t: bf16 weights of K offsets 16*j + 8*h of tile t
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
-                    const bf16x8 b0 = as_bf16x8(wq[0][t]);
-                    const bf16x8 b1 = as_bf16x8(wq[1][t]);
+                    const bf16x8 b0 = as_bf16x8(s.w[t]);
+                    const bf16x8 b1 = as_bf16x8(s.w[4 + t]);
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) {
                         y[t][mt] = mfma(a0[mt], b0, y[t][mt]);
@@ -526,18 +345,20 @@ __global__ __launch_bounds__(256, OCC) void qgemm_kernel(const GemmLaunch L) {
                 for (int t = 0; t < NT; ++t) {
                     bf16x8 b0, b1;
                     if constexpr (BITS == 8) {
-                        const u32x4 qv = wq[g][t];
+                        // slot g*4 + t: the 16 codes of K offsets 64*g + 16*j
+                        const u32x4 qv = s.w[4 * g + t];
                         b0 = codes8_to_bf16(qv[0], qv[1]);
                         b1 = codes8_to_bf16(qv[2], qv[3]);
                     } else {
-                        const u32x2 qv = wq4[g][t];
-                        b0 = codes4_to_bf16(qv[0]);
-                        b1 = codes4_to_bf16(qv[1]);
+                        // slot (g/2)*4 + t: groups 2*(g/2) and 2*(g/2)+1, 8 bytes each
+                        const u32x4 qv = s.w[4 * (g >> 1) + t];
+                        b0 = codes4_to_bf16(qv[2 * (g & 1)]);
+                        b1 = codes4_to_bf16(qv[2 * (g & 1) + 1]);
                     }
-                    const uint32_t sh = sbw[g][t] & 0xffffu;
-                    const uint32_t bh = sbw[C::GS + g][t] & 0xffffu;
-                    const float sc = h2f(sh);
-                    float bi = h2f(bh);
+                    // dword t of load g: scale (low half) and bias (high half)
+                    const uint32_t sbd = s.sb[g][t];
+                    const float sc = h2f(sbd & 0xffffu);
+                    float bi = h2f(sbd >> 16);
                     if constexpr (BITS == 4) bi = fmaf(-128.f, sc, bi);   // codes carry +128
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) {
@@ -547,6 +368,9 @@ __global__ __launch_bounds__(256, OCC) void qgemm_kernel(const GemmLaunch L) {
                         for (int r4 = 0; r4 < 4; ++r4)
                             y[t][mt][r4] = fmaf(sc, acc[r4], fmaf(bi, xs[mt][r4], y[t][mt][r4]));
                     }
+                    // one tile at a time: the scheduler would otherwise convert
+                    // every tile's codes up front and run out of registers
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }
@@ -628,17 +452,17 @@ __global__ __launch_bounds__(256, OCC) void qgemm_kernel(const GemmLaunch L) {
         if (lane == 0) ticket = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         ticket = __shfl(ticket, 0);
         if (ticket != (uint32_t)(wl - wf)) return;
-        // Last arrival: the pieces in workgroup order, eight requests in
-        // flight.  Every workgroup after wf starts inside the block (its piece
+        // Last arrival: the pieces in workgroup order, XB pieces in
+        // flight (few: the ring's registers are live here).  Every workgroup after wf starts inside the block (its piece
         // is its first, slot 0); wf's piece is its first only if its range
         // starts at the block start.
         const int wf_side = quad_begin(QU, GRID, wf) >= bq0 ? 0 : 1;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) z[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int v0 = wf; v0 <= wl; v0 += 8) {
-            f32x4 part[8][MT];
+        for (int v0 = wf; v0 <= wl; v0 += XB) {
+            f32x4 part[XB][MT];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < XB; ++i) {
                 const int v = min(v0 + i, wl);
                 const int sl = v == wf ? wf_side : 0;
                 const float *src = KL->partial + (((int64_t)v * 2 + sl) * kWavesPerWG + w) * (MT * kWave * 4);
@@ -650,7 +474,7 @@ __global__ __launch_bounds__(256, OCC) void qgemm_kernel(const GemmLaunch L) {
             // every loaded value is consumed (a duplicate past wl adds zero), so
             // no load of this batch is left pending
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < XB; ++i) {
                 const bool real = v0 + i <= wl;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
@@ -683,34 +507,29 @@ __global__ __launch_bounds__(256, OCC) void qgemm_kernel(const GemmLaunch L) {
     if (skips_last && cu.qi == NQ - 1 && NQ > 1) advance(cu);
     close_until(nsteps > 0 ? cu.q : Q1);
     if (nsteps > 0) {
-        // Requests run DEPTH - 1 stages ahead of the computation; past this
-        // wave's last stage they repeat it, so that every step makes the same
-        // requests and the waits stay positional.
-        // nothing of this wave is in flight here (the compiler's count of
-        // outstanding loads starts the loop from the same state every time)
-        wait_vm<0>();
+        // Requests run DEPTH - 1 units ahead of the computation; past this
+        // wave's last unit they repeat it, so that every step makes the same
+        // requests.  Units land in registers: the compiler's own count of
+        // outstanding loads places each wait just before a slot is used.
         Cur iu = cu;
         int issued = 0;
-        auto issue_next = [&](int slot, u32x4 (&a)[C::GS][MT][2]) __attribute__((always_inline)) {
-            issue(iu, slot);
-            load_act(iu, a);
+        auto issue_next = [&](Slot &sl) __attribute__((always_inline)) {
+            issue(iu, sl);
             if (++issued < nsteps) advance(iu);
         };
 #pragma unroll
-        for (int s = 0; s < DEPTH - 1; ++s) issue_next(s, act[s]);
-        // one stage: request DEPTH - 1 ahead, wait for this one, compute it,
-        // close the pieces that end before the next one
+        for (int s = 0; s < DEPTH - 1; ++s) issue_next(ring[s]);
+        // one step: request DEPTH - 1 ahead, compute this unit, close the
+        // pieces that end before the next one
         auto step = [&](int slot, int nslot) __attribute__((always_inline)) {
-            issue_next(nslot, act[nslot]);
-            wait_vm<AHEAD_OPS>();       // everything older than the last DEPTH - 1 requests has landed
-            compute(cu, myring + slot * (kWavesPerWG * C::WAVE_STAGE), act[slot]);
+            issue_next(ring[nslot]);
+            compute(cu, ring[slot]);
             Cur nu = cu;
             advance(nu);
             close_until(nu.q);
             cu = nu;
         };
-        // unrolled by DEPTH so that every ring slot and activation set is a
-        // constant in each step
+        // unrolled by DEPTH so that every ring slot is a constant in each step
         int i = 0;
         for (; i + DEPTH <= nsteps; i += DEPTH) {
 #pragma unroll
@@ -721,7 +540,7 @@ __global__ __launch_bounds__(256, OCC) void qgemm_kernel(const GemmLaunch L) {
             if (i + s < nsteps) step(s, (s + DEPTH - 1) % DEPTH);
     }
     close_until(Q1);
-    wait_vm_all();                      // no load into LDS outlives the workgroup
+    wait_vm_all();                      // the unused requests past the last unit have landed
 
     if constexpr (ARGMAX) {
         // row maxima: over the wave's columns, the workgroup's waves, then the grid
@@ -804,9 +623,6 @@ hipError_t launch_any(const GemmLaunch &L, int bits, int grid, hipStream_t s) {
 
 }  // namespace
 
-// K elements per stage
-int stage_k(int bits) { return bits == 16 ? 64 : 128; }
-
 int device_cus() {
     static int cached[64] = {0};
     int dev = 0;
@@ -822,23 +638,20 @@ int device_cus() {
 
 GemmPlan plan_gemm(int count, const int32_t *n, int32_t k, int32_t m, int bits, bool argmax) {
     GemmPlan p{};
-    p.nst = (k + stage_k(bits) - 1) / stage_k(bits);
+    p.nst = (k + tile_k(bits) - 1) / tile_k(bits);
     p.nq = (p.nst + kWavesPerWG - 1) / kWavesPerWG;
     int64_t blocks = 0;
     for (int i = 0; i < count; ++i) blocks += (n[i] + kBlockCols - 1) / kBlockCols;
     p.total_cg = (int32_t)blocks;
     const int64_t quads = blocks * p.nq;
+    const int mt = m <= 16 ? 1 : 2;
     // OCC workgroups per CU; never more workgroups than quads
-    const int64_t slots = (int64_t)OCC * device_cus();
+    const int64_t slots = (int64_t)kernel_occ(bits, mt) * device_cus();
     const int64_t grid = quads < slots ? quads : slots;
     p.grid = grid < 1 ? 1 : (int32_t)grid;
-    // the kernel splits quads with 32-bit products and addresses each weight
-    // with 32-bit byte offsets
-    int64_t nmax = 0;
-    for (int i = 0; i < count; ++i) nmax = n[i] > nmax ? n[i] : nmax;
-    p.fits = quads * p.grid < ((int64_t)1 << 31) && nmax * ((int64_t)k * bits / 8) < ((int64_t)1 << 32);
+    // the kernel splits quads with 32-bit products
+    p.fits = quads * p.grid < ((int64_t)1 << 31);
     p.quads = p.fits ? (int32_t)quads : 0;
-    const int mt = m <= 16 ? 1 : 2;
     size_t off = 256;                                   // [0, 256): argmax arrival counter
     p.off_counters = off;
     off += ((size_t)blocks * kWavesPerWG * 4 + 255) / 256 * 256;

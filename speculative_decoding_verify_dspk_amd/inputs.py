@@ -246,7 +246,7 @@ def make_qweight_device(n: int, k: int, bits: int, *labels):
     independent uniform codes; scales U(0.001, 0.01) and biases N(0, 0.1) are
     rounded to fp16; the bf16 control is N(0.7, 0.45).  Returns
     (codes, scales, biases) device tensors (int32 / int16 / int16 bit
-    patterns); scales and biases group-major [K/64][N] as the library takes them."""
+    patterns) in the interchange layout: scales and biases row-major [N][K/64]."""
     import torch
     g = device_generator(*labels, n, k, bits)
     if bits == 16:
@@ -254,8 +254,8 @@ def make_qweight_device(n: int, k: int, bits: int, *labels):
         return w.to(torch.bfloat16).view(torch.int16), None, None
     words = torch.randint(-(1 << 31), 1 << 31, (n, k * bits // 32), dtype=torch.int64, device="cuda",
                           generator=g).to(torch.int32)
-    sc = torch.empty((k // GROUP, n), dtype=torch.float32, device="cuda").uniform_(0.001, 0.01, generator=g)
-    bi = torch.empty((k // GROUP, n), dtype=torch.float32, device="cuda").normal_(0.0, 0.1, generator=g)
+    sc = torch.empty((n, k // GROUP), dtype=torch.float32, device="cuda").uniform_(0.001, 0.01, generator=g)
+    bi = torch.empty((n, k // GROUP), dtype=torch.float32, device="cuda").normal_(0.0, 0.1, generator=g)
     return words, sc.to(torch.float16).view(torch.int16), bi.to(torch.float16).view(torch.int16)
 
 

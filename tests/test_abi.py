@@ -37,7 +37,11 @@ def test_exports_every_header_symbol(lib):
     assert lib.dspk_version() >= 100
 
 
-def _desc(n=64, k=128, bits=8, group=64, codes=0x10000, scales=0x20000, biases=0x30000):
+def _desc(n=64, k=128, bits=8, group=64, tiles=0x10000):
+    return binding.TiledDesc(n, k, bits, group, tiles)
+
+
+def _src(n=64, k=128, bits=8, group=64, codes=0x10000, scales=0x20000, biases=0x30000):
     return binding.QWeightDesc(n, k, bits, group, codes, scales, biases)
 
 
@@ -48,14 +52,41 @@ X, Y, WS = 0x40000, 0x50000, 0x60000
 @pytest.mark.parametrize("mutate,code", [
     (dict(bits=3), EUNSUPPORTED), (dict(bits=2), EUNSUPPORTED), (dict(group=32), EUNSUPPORTED),
     (dict(k=100), EINVAL), (dict(k=0), EINVAL), (dict(n=0), EINVAL),
-    (dict(codes=0), EINVAL), (dict(codes=0x10004), EINVAL), (dict(scales=0), EINVAL),
-    (dict(bits=16), EINVAL),   # bf16 weights must not carry scales/biases
+    (dict(tiles=0), EINVAL), (dict(tiles=0x10010), EINVAL),      # NULL, not 256-byte aligned
 ])
 def test_qgemm_rejects_bad_weight(lib, mutate, code):
     d = _desc(**mutate)
     rc = lib.dspk_qgemm_verify(ctypes.byref(d), X, 128, 4, Y, 0, 64, WS, 1 << 20, None)
     assert rc == code
     assert lib.dspk_last_error().decode().startswith("dspk_qgemm_verify")
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (dict(bits=3), EUNSUPPORTED), (dict(group=32), EUNSUPPORTED), (dict(k=100), EINVAL), (dict(n=0), EINVAL),
+    (dict(codes=0), EINVAL), (dict(codes=0x10004), EINVAL), (dict(scales=0), EINVAL), (dict(biases=0x30001), EINVAL),
+    (dict(bits=16), EINVAL),   # bf16 weights must not carry scales/biases
+])
+def test_pack_rejects_bad_weight(lib, mutate, code):
+    d = _src(**mutate)
+    assert lib.dspk_qweight_pack(ctypes.byref(d), WS, 1 << 30, None) == code
+    assert lib.dspk_last_error().decode().startswith("dspk_qweight_pack")
+
+
+def test_pack_sizes_and_rejects_bad_destination(lib):
+    # whole units of 64 columns x (128 | 256 | 64) K elements: 8 KiB of codes plus 4 * KU bytes of
+    # scale/bias dwords for the quantised formats
+    assert lib.dspk_tiled_bytes(151936, 2560, 8) == 2374 * 20 * 8704 == 151936 * 2560 * 17 // 16
+    assert lib.dspk_tiled_bytes(151936, 2560, 4) == 2374 * 10 * 9216 == 151936 * 2560 * 9 // 16
+    assert lib.dspk_tiled_bytes(4096, 4096, 16) == 64 * 64 * 8192 == 4096 * 4096 * 2
+    assert lib.dspk_tiled_bytes(37, 320, 8) == 1 * 3 * 8704                  # ragged N and K padded
+    assert lib.dspk_tiled_bytes(37, 320, 4) == 1 * 2 * 9216
+    assert lib.dspk_tiled_bytes(0, 64, 8) == 0 and lib.dspk_tiled_bytes(64, 100, 8) == 0
+    assert lib.dspk_tiled_bytes(64, 64, 3) == 0
+    d = _src(n=64, k=128)
+    need = lib.dspk_tiled_bytes(64, 128, 8)
+    assert lib.dspk_qweight_pack(ctypes.byref(d), WS, need - 1, None) == EINVAL
+    assert lib.dspk_qweight_pack(ctypes.byref(d), WS + 16, need, None) == EINVAL
+    assert lib.dspk_qweight_pack(ctypes.byref(d), None, need, None) == EINVAL
 
 
 @pytest.mark.parametrize("args,code", [
@@ -87,7 +118,7 @@ def test_qgemm_workspace_contract(lib):
 
 
 def test_grouped_rejects_mismatch(lib):
-    ds = (binding.QWeightDesc * 2)(_desc(k=128), _desc(k=256))
+    ds = (binding.TiledDesc * 2)(_desc(k=128), _desc(k=256))
     ys = (ctypes.c_void_p * 2)(Y, Y)
     ld = (ctypes.c_int64 * 2)(64, 64)
     assert lib.dspk_qgemm_verify_grouped(2, ds, X, 256, 4, ys, 0, ld, WS, 1 << 20, None) == EINVAL

@@ -133,3 +133,62 @@ def test_qgemm_full_shapes_sampled(model, m):
         err = np.abs(got[:, cols] - ref).max(axis=1) / np.abs(ref).max(axis=1)
         assert (err <= 2e-3).all(), (name, err.max())
         assert np.isfinite(got).all()
+
+
+def _tiles_by_definition(w) -> np.ndarray:
+    """The tiled layout written out from its definition in include/dspk.h and
+    the packing source: 64-column blocks, units of KU K elements, eight 1 KiB
+    slots of one 16-byte piece per lane, then (scale | bias << 16) dwords."""
+    bits, n, k = w.bits, w.n, w.k
+    ku = {8: 128, 4: 256, 16: 64}[bits]
+    gs = ku // 64
+    nst, nb = -(-k // ku), -(-n // 64)
+    unit = 8192 + (0 if bits == 16 else 256 * gs)
+    out = np.zeros(nb * nst * unit, np.uint8)
+    rowb = np.ascontiguousarray(w.codes).view(np.uint8).reshape(n, k * bits // 8)
+    for b in range(nb):
+        for u in range(nst):
+            base = (b * nst + u) * unit
+            for i in range(8):
+                t, hi = i % 4, i // 4
+                for lane in range(64):
+                    c, j = lane % 16, lane // 16
+                    col = 64 * b + 16 * t + c
+                    dst = base + 1024 * i + 16 * lane
+                    if col >= n:
+                        continue
+                    if bits == 8:
+                        k0 = ku * u + 64 * hi + 16 * j
+                        if k0 < k:
+                            out[dst:dst + 16] = rowb[col, k0:k0 + 16]
+                    elif bits == 4:
+                        for half in range(2):
+                            k0 = ku * u + 64 * (2 * hi + half) + 16 * j
+                            if k0 < k:
+                                out[dst + 8 * half:dst + 8 * half + 8] = rowb[col, k0 // 2:k0 // 2 + 8]
+                    else:
+                        k0 = ku * u + 16 * j + 8 * hi
+                        if k0 < k:
+                            out[dst:dst + 16] = rowb[col, 2 * k0:2 * k0 + 16]
+            if bits == 16:
+                continue
+            for c in range(16):
+                for g in range(gs):
+                    for t in range(4):
+                        col, gk = 64 * b + 16 * t + c, gs * u + g
+                        if col < n and gk < k // 64:
+                            d = int(w.scales[col, gk]) | (int(w.biases[col, gk]) << 16)
+                            o = base + 8192 + 16 * gs * c + 4 * (4 * g + t)
+                            out[o:o + 4] = np.array([d], dtype=np.uint32).view(np.uint8)
+    return out
+
+
+@pytest.mark.parametrize("bits", [8, 4, 16])
+@pytest.mark.parametrize("n,k", [(37, 320), (130, 1024), (64, 64)])
+def test_pack_layout_matches_definition(bits, n, k):
+    """dspk_qweight_pack is a pure byte permutation: bit-exact against the
+    layout written out on the host, including the zero padding."""
+    w = inputs.make_qweight(n, k, bits, "pack", n, k)
+    dw = binding.DeviceQWeight.upload(w)
+    got = dw.tiles.cpu().numpy()
+    assert np.array_equal(got, _tiles_by_definition(w))
