@@ -8,7 +8,9 @@ Workload (default): one Qwen3-4B-shaped decoder layer (q 4096x2560, k/v
 greedy acceptance of drafts that match the target's token with probability
 0.7 per position.  One step = one verify round at each width
 M = 1, 2, 4, 6, 8, 12, 16 (the verify-cost curve); each round is
-  4 projection launches + head/argmax + greedy accept + one D2H copy and sync.
+  4 projection launches + head/argmax + greedy accept + one D2H copy and sync,
+launched from the host with arguments marshalled once per width and weight
+copy (--graph replays HIP graphs of the same calls instead).
 
 Printed: one JSON line with the whole-job weight-GB/s (weight bytes of every
 round / wall time), the per-width curve t(M)/t(1), the roofline of the
@@ -42,6 +44,9 @@ def parse():
     ap.add_argument("--layers", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-s", type=float, default=20.0)
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each round as HIP graphs (layers, head, accept) captured once per width and "
+                         "weight copy, instead of host launches with pre-marshalled arguments")
     ap.add_argument("--calibrate", action="store_true",
                     help="after the timed region, run one plain device copy of 256 MiB (the reference "
                          "dispatch for scaling hardware byte counters)")
@@ -133,24 +138,42 @@ def main():
         t = stack.argmax[:m].cpu().numpy()[None, :]
         d = inputs.drafts_match_rate(t, 0.7, V, "bench", args.config, m) if m > 1 else np.zeros((1, 0), np.int32)
         drafts[m] = torch.from_numpy(np.ascontiguousarray(d, dtype=np.int32)).cuda() if m > 1 else None
-        acc[m] = (torch.empty((1,), dtype=torch.int32, device="cuda"),
-                  torch.empty((1, m), dtype=torch.int32, device="cuda"))
-    host_len = torch.empty((1,), dtype=torch.int32).pin_memory()
-    host_com = torch.empty((1, max_m), dtype=torch.int32).pin_memory()
+        res = torch.empty((1 + m,), dtype=torch.int32, device="cuda")   # [accept_len | committed]
+        acc[m] = (res[:1], res[1:].view(1, m), res)
+    host_res = torch.empty((1 + max_m,), dtype=torch.int32).pin_memory()
 
     ev = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
     rounds = {m: 0 for m in sweep}
 
+    # each round's calls, marshalled once per (width, weight copy); with
+    # --graph, captured once as HIP graphs (layers, head, accept) instead
+    prepared, graphs = {}, {}
+    for m in sweep:
+        for cp in range(args.copies):
+            if args.graph:
+                graphs[(m, cp)] = stack.capture_round(m, cp, drafts[m], acc[m][0], acc[m][1])
+            else:
+                prepared[(m, cp)] = stack.prepare_round(m, cp, drafts[m], acc[m][0], acc[m][1], stream)
+
     def run_round(m: int, copy: int, record: list | None):
         e = [ev() for _ in range(4)] if record is not None else None
         if e: e[0].record(stream)
-        stack.launch_layers(m, copy, stream)
-        if e: e[1].record(stream)
-        stack.launch_head(m, copy, stream=stream)
-        if e: e[2].record(stream)
-        binding.accept_greedy(stack.argmax, drafts[m], 1, m, acc[m][0], acc[m][1], stream)
-        host_len.copy_(acc[m][0], non_blocking=True)
-        host_com[:, :m].copy_(acc[m][1], non_blocking=True)
+        if args.graph:
+            gl, gh, ga = graphs[(m, copy)]
+            gl.replay()
+            if e: e[1].record(stream)
+            gh.replay()
+            if e: e[2].record(stream)
+            ga.replay()
+        else:
+            calls, head, accept = prepared[(m, copy)]
+            for f in calls:
+                f()
+            if e: e[1].record(stream)
+            head()
+            if e: e[2].record(stream)
+            accept()
+        host_res[:1 + m].copy_(acc[m][2], non_blocking=True)   # the round's one device-to-host copy
         if e: e[3].record(stream)
         stream.synchronize()       # the round's one device sync
         if record is not None:
@@ -162,14 +185,24 @@ def main():
             run_round(m, step_copy % args.copies, None)
             step_copy += 1
 
+    # A serving loop's long-lived objects (weights, prepared calls, the torch
+    # module) move to the permanent generation, so that a full collection
+    # scans only what the loop itself allocates (one scan of everything takes
+    # tens of milliseconds with torch loaded).
+    import gc
+    gc.collect()
+    gc.freeze()
     records = []
     committed = 0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    walls = []
     for _ in range(args.steps):
         for m in sweep:
+            tr = time.perf_counter()
             run_round(m, step_copy % args.copies, records)
-            committed += int(host_len[0])
+            committed += int(host_res[0])
+            walls.append(time.perf_counter() - tr)
             step_copy += 1
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -223,11 +256,13 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{args.config} layer x{args.layers} + lm_head {V}x{stack.hidden}, "
                                f"{args.bits}-bit g64, greedy alpha=0.7, one round per M in {sweep}",
-                   "widths": sweep, "weight_bytes_per_round": round_b, "rotating_copies": args.copies},
+                   "widths": sweep, "weight_bytes_per_round": round_b, "rotating_copies": args.copies,
+                   "launch": "hip-graph replays" if args.graph else "host launches, arguments marshalled once"},
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "t16_over_t1": curve[sweep[-1]]["t_over_t1"],
         "curve": curve,
         "rounds_per_s": round(n_rounds / wall, 1),
+        "round_wall_us": {"p50": round(float(np.median(walls)) * 1e6, 1), "max": round(max(walls) * 1e6, 1)},
         "rows_per_s": round(sum(sweep) * args.steps / wall, 1),
         "committed_tokens_per_round": round(committed / n_rounds, 3),
         "roofline": roofline,

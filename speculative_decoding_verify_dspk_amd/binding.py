@@ -173,6 +173,61 @@ def tiled_bytes(n: int, k: int, bits: int) -> int:
     return lib().dspk_tiled_bytes(n, k, bits)
 
 
+# ------------------------------------------------------- prepared launches
+_CARG = type(ctypes.byref(ctypes.c_int()))
+
+
+class Prepared:
+    """One entry-point call with every argument already marshalled: calling it
+    is a single foreign call (no Python-side conversion), for rounds that
+    repeat the same launches with the same buffers."""
+
+    def __init__(self, name: str, *args):
+        self.name = name
+        self.fn = getattr(lib(), name)
+        conv = []
+        for t, a in zip(self.fn.argtypes, args):
+            if a is None or isinstance(a, (ctypes._SimpleCData, ctypes.Array, _CARG)):
+                conv.append(a)                   # NULL, or already a ctypes object
+            else:
+                conv.append(t(a))                # plain int / float -> its C type, once
+        self.args = tuple(conv)
+        self.keep = args            # descriptors and arrays the pointers refer to
+
+    def __call__(self) -> None:
+        rc = self.fn(*self.args)
+        if rc != 0:
+            _check(rc)
+
+
+def prepare_qgemm(w: DeviceQWeight, x, m: int, y, workspace, stream=None) -> Prepared:
+    dt = DSPK_BF16 if y.element_size() == 2 else DSPK_F32
+    return Prepared("dspk_qgemm_verify", ctypes.byref(w.desc), x.data_ptr(), _chunks(x, "x"), m, y.data_ptr(), dt,
+                    _rows(y, "y"), workspace.data_ptr(), workspace.numel(), _stream(stream))
+
+
+def prepare_qgemm_grouped(ws: list, x, m: int, ys: list, workspace, stream=None) -> Prepared:
+    cnt = len(ws)
+    descs = (TiledDesc * cnt)(*[w.desc for w in ws])
+    yptr = (c_void_p * cnt)(*[y.data_ptr() for y in ys])
+    ldy = (c_int64 * cnt)(*[_rows(y, "y") for y in ys])
+    dt = DSPK_BF16 if ys[0].element_size() == 2 else DSPK_F32
+    return Prepared("dspk_qgemm_verify_grouped", cnt, descs, x.data_ptr(), _chunks(x, "x"), m, yptr, dt, ldy,
+                    workspace.data_ptr(), workspace.numel(), _stream(stream))
+
+
+def prepare_lmhead(w: DeviceQWeight, h, m: int, argmax, logits, workspace, stream=None) -> Prepared:
+    return Prepared("dspk_lmhead_argmax", ctypes.byref(w.desc), h.data_ptr(), _chunks(h, "h"), m, argmax.data_ptr(),
+                    _ptr(logits), 0 if logits is None else _rows(logits, "logits"), workspace.data_ptr(),
+                    workspace.numel(), _stream(stream))
+
+
+def prepare_accept_greedy(target_ids, draft_ids, b: int, m_rows: int, accept_len, committed,
+                          stream=None) -> Prepared:
+    return Prepared("dspk_accept_greedy", target_ids.data_ptr(), _ptr(draft_ids), b, m_rows, accept_len.data_ptr(),
+                    committed.data_ptr(), _stream(stream))
+
+
 # ------------------------------------------------------------ entry points
 def version() -> int:
     return lib().dspk_version()

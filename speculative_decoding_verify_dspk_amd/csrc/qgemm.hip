@@ -181,7 +181,7 @@ template <int BITS, int MT, bool ARGMAX>
 __global__ __launch_bounds__(256, kernel_occ(BITS, MT)) void qgemm_kernel(const GemmLaunch L) {
     using C = Cfg<BITS>;
     constexpr int DEPTH = kernel_depth(BITS, MT);
-    constexpr int XB = MT == 1 ? 4 : 2;        // partial sums in flight when completing a split block
+    constexpr int XB = MT == 1 ? 8 : 4;        // partial sums in flight when completing a split block
     // In-workgroup sum (each wave posts CTILES of its 16-column tiles per
     // pass, one 16-row tile at a time); after the main loop the same bytes
     // hold the argmax reduction.

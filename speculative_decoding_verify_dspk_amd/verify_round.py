@@ -11,6 +11,11 @@ Weights and activations are seeded synthetic tensors of the workload's shapes
 real layer's dependencies allow: q/k/v grouped (they read the same rows), o,
 gate/up grouped, down.  The four inputs of a layer are independent N(0, 1)
 rows; attention, norms and the activation function are outside this path.
+
+A round's launches can be captured once into HIP graphs (``capture_round``)
+and replayed every round: the kernels take no host-side work between calls
+(their workspaces come back zeroed), so a replay is the whole round in one
+submission, without host launch gaps between its kernels.
 """
 from __future__ import annotations
 
@@ -100,3 +105,38 @@ class VerifyStack:
     def launch_head(self, m: int, copy: int = 0, want_logits: bool = False, stream=None) -> None:
         binding.lmhead_argmax(self.heads[copy], self.h, m, self.argmax, self.logits if want_logits else None,
                               self.ws_head, stream)
+
+    def prepare_round(self, m: int, copy: int, draft_ids, accept_len, committed, stream=None):
+        """The round's calls at width m on weight copy ``copy`` with their
+        arguments marshalled once: (layer calls, head call, accept call)."""
+        layers = []
+        for L in self.layers[copy]:
+            layers += [binding.prepare_qgemm_grouped(L.qkv, self.x_attn, m, self.y_qkv, self.ws_qkv, stream),
+                       binding.prepare_qgemm(L.o, self.x_o, m, self.y_o, self.ws_o, stream),
+                       binding.prepare_qgemm_grouped(L.gateup, self.x_mlp, m, self.y_gu, self.ws_gu, stream),
+                       binding.prepare_qgemm(L.down, self.x_down, m, self.y_down, self.ws_down, stream)]
+        head = binding.prepare_lmhead(self.heads[copy], self.h, m, self.argmax, None, self.ws_head, stream)
+        accept = binding.prepare_accept_greedy(self.argmax, draft_ids, 1, m, accept_len, committed, stream)
+        return layers, head, accept
+
+    def capture_round(self, m: int, copy: int, draft_ids, accept_len, committed):
+        """HIP graphs (layers, head, accept) of one greedy round at width m on
+        weight copy ``copy``; replay them in that order on one stream."""
+        import torch
+        fns = (lambda: self.launch_layers(m, copy),
+               lambda: self.launch_head(m, copy),
+               lambda: binding.accept_greedy(self.argmax, draft_ids, 1, m, accept_len, committed))
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):          # one eager pass before capture
+            for f in fns:
+                f()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for f in fns:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                f()
+            graphs.append(g)
+        return graphs

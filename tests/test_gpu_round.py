@@ -50,3 +50,48 @@ def test_batched_four_requests():
     ral, rcom = oracle.accept_greedy(t, d)
     ok_req = ~near.reshape(b, rows).any(axis=1)
     assert np.array_equal(al[ok_req], ral[ok_req]) and np.array_equal(com[ok_req], rcom[ok_req])
+
+
+def test_graph_replays_match_eager_round():
+    """A round captured into HIP graphs (layers, head, accept) and replayed
+    several times, with eager work and synchronisations in between, gives
+    the eager round's results bit for bit on every replay (the kernels are
+    deterministic and leave their workspaces zeroed for the next call)."""
+    import torch
+    from speculative_decoding_verify_dspk_amd import binding
+    from speculative_decoding_verify_dspk_amd.verify_round import VerifyStack
+    m = 8
+    st = VerifyStack("qwen3-4b", 1, 8, m)
+    st.launch_head(m)
+    torch.cuda.synchronize()
+    t = st.argmax[:m].cpu().numpy()[None, :]
+    d = torch.from_numpy(inputs.drafts_match_rate(t, 0.7, st.vocab, "graph-test")).cuda()
+    alen = torch.empty((1,), dtype=torch.int32, device="cuda")
+    com = torch.empty((1, m), dtype=torch.int32, device="cuda")
+
+    def outputs():
+        return [y.clone() for y in st.y_qkv + [st.y_o] + st.y_gu + [st.y_down]] + \
+               [st.argmax.clone(), alen.clone(), com.clone()]
+
+    st.launch_layers(m)
+    st.launch_head(m)
+    binding.accept_greedy(st.argmax, d, 1, m, alen, com)
+    torch.cuda.synchronize()
+    ref = outputs()
+    graphs = st.capture_round(m, 0, d, alen, com)
+    for rep in range(3):
+        for y in st.y_qkv + [st.y_o] + st.y_gu + [st.y_down]:
+            y.fill_(float("nan"))
+        st.argmax.fill_(-5)
+        alen.fill_(-5)
+        com.fill_(-5)
+        torch.cuda.synchronize()
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        got = outputs()
+        for a, b in zip(ref, got):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager round"
+        # eager work between replays: an unrelated eager call on the same workspaces
+        st.launch_head(m)
+        torch.cuda.synchronize()
