@@ -1,6 +1,6 @@
 """Benchmark of the verify pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config qwen3-4b]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config qwen3-4b] ...
 
 Workload (default): one Qwen3-4B-shaped decoder layer (q 4096x2560, k/v
 1024x2560, o 2560x4096, gate/up 9728x2560, down 2560x9728) plus the
@@ -8,9 +8,18 @@ Workload (default): one Qwen3-4B-shaped decoder layer (q 4096x2560, k/v
 greedy acceptance of drafts that match the target's token with probability
 0.7 per position.  One step = one verify round at each width
 M = 1, 2, 4, 6, 8, 12, 16 (the verify-cost curve); each round is
-  4 projection launches + head/argmax + greedy accept + one D2H copy and sync,
+  4 projection launches per layer + head/argmax + accept + one D2H copy and sync,
 launched from the host with arguments marshalled once per width and weight
 copy (--graph replays HIP graphs of the same calls instead).
+
+Other workloads of the same path:
+  --config dense-27b --layers 64 --sweep 17 --copies 1 --accept sample
+        64 resident 27B-shaped layers, M = 17, speculative sampling at T = 1
+        against draft distributions q = softmax(target logits + N(0, 0.5));
+  --config ornith-9b --bits 4|8|16 --sweep 1,2,...,16
+        the 9B-shaped layer and 151936x4096 head per weight format;
+  --config qwen3-8b --batch 4 --sweep 6 --alpha 0.3,0.5,0.7,0.9
+        four requests of six rows in one launch, greedy accept per request.
 
 Printed: one JSON line with the whole-job weight-GB/s (weight bytes of every
 round / wall time), the per-width curve t(M)/t(1), the roofline of the
@@ -37,11 +46,16 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="qwen3-4b", choices=["qwen3-4b", "dense-27b", "ornith-9b"])
-    ap.add_argument("--bits", type=int, default=8)
-    ap.add_argument("--copies", type=int, default=3, help="rotating weight copies (defeat the 256 MB MALL)")
-    ap.add_argument("--sweep", default=",".join(map(str, SWEEP)))
+    ap.add_argument("--config", default="qwen3-4b", choices=["qwen3-4b", "qwen3-8b", "ornith-9b", "dense-27b"])
+    ap.add_argument("--bits", type=int, default=8, choices=[4, 8, 16])
     ap.add_argument("--layers", type=int, default=1)
+    ap.add_argument("--copies", type=int, default=3, help="rotating weight copies (defeat the 256 MB MALL)")
+    ap.add_argument("--sweep", default=",".join(map(str, SWEEP)), help="rows per request, one round each")
+    ap.add_argument("--batch", type=int, default=1, help="requests verified together in one launch")
+    ap.add_argument("--alpha", default="0.7", help="per-position draft match rate (one per request)")
+    ap.add_argument("--accept", default="greedy", choices=["greedy", "sample"])
+    ap.add_argument("--temperature", type=float, default=1.0)
+    ap.add_argument("--noise", type=float, default=0.5, help="std of the drafter's logit noise (sampling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-s", type=float, default=20.0)
     ap.add_argument("--graph", action="store_true",
@@ -126,24 +140,52 @@ def main():
 
     binding.lib()   # fail loudly if the HIP library is missing
     sweep = [int(s) for s in args.sweep.split(",")]
-    max_m = max(sweep)
+    B = args.batch
+    alpha = np.array([float(a) for a in args.alpha.split(",")])
+    alpha = np.broadcast_to(alpha, (B,)).copy() if alpha.size in (1, B) else None
+    if alpha is None or B * max(sweep) > binding.MAX_ROWS or (args.accept == "sample" and B != 1):
+        print("bench.py: --alpha needs 1 or --batch values, batch * rows <= 32, sampling one request",
+              file=sys.stderr)
+        sys.exit(2)
+    sample = args.accept == "sample"
+    max_m = B * max(sweep)
     stack = VerifyStack(args.config, args.layers, args.bits, max_m, copies=args.copies)
     stream = torch.cuda.current_stream()
     V = stack.vocab
 
-    # untimed pre-pass: target ids per width, then drafts with a 0.7 match rate
-    drafts, acc = {}, {}
+    # untimed pre-pass per width: the target's tokens (and logits), then the
+    # drafter's side -- draft ids with the match rates, or (sampling) draft
+    # distributions q from noisy target logits, draft ids drawn from q, and
+    # the round's uniforms
+    rounds_in = {}
     for m in sweep:
-        stack.launch_head(m, 0, stream=stream)
-        t = stack.argmax[:m].cpu().numpy()[None, :]
-        d = inputs.drafts_match_rate(t, 0.7, V, "bench", args.config, m) if m > 1 else np.zeros((1, 0), np.int32)
-        drafts[m] = torch.from_numpy(np.ascontiguousarray(d, dtype=np.int32)).cuda() if m > 1 else None
-        res = torch.empty((1 + m,), dtype=torch.int32, device="cuda")   # [accept_len | committed]
-        acc[m] = (res[:1], res[1:].view(1, m), res)
-    host_res = torch.empty((1 + max_m,), dtype=torch.int32).pin_memory()
+        M = B * m
+        stack.launch_head(M, 0, want_logits=sample, stream=stream)
+        t = stack.argmax[:M].cpu().numpy().reshape(B, m)
+        res = torch.empty((B + B * m,), dtype=torch.int32, device="cuda")   # [accept_len | committed]
+        r = dict(res=res, alen=res[:B], com=res[B:].view(B, m))
+        if sample:
+            z = stack.logits[:m].cpu().numpy()
+            q, d = inputs.draft_distribution(z, args.temperature, args.noise, "bench", args.config, m)
+            r["q"] = torch.from_numpy(np.ascontiguousarray(q)).cuda()
+            r["d"] = torch.from_numpy(d).cuda()
+            r["u"] = torch.from_numpy(inputs.make_uniforms(m, "bench", args.config, m)).cuda()
+            r["ws"] = binding.alloc_workspace(binding.sample_workspace_bytes(V, m))
+        else:
+            d = inputs.drafts_match_rate(t, alpha, V, "bench", args.config, m) if m > 1 else None
+            r["d"] = torch.from_numpy(np.ascontiguousarray(d, dtype=np.int32)).cuda() if m > 1 else None
+        rounds_in[m] = r
+    host_res = torch.empty((B + max_m,), dtype=torch.int32).pin_memory()
+
+    def accept_call(m, r, prepare=True):
+        if sample:
+            args_ = (stack.logits, r["q"], r["d"], r["u"], m, V, args.temperature, r["alen"], r["com"], r["ws"])
+            return binding.prepare_accept_sample(*args_, stream) if prepare else \
+                (lambda: binding.accept_sample(*args_))
+        args_ = (stack.argmax, r["d"], B, m, r["alen"], r["com"])
+        return binding.prepare_accept_greedy(*args_, stream) if prepare else (lambda: binding.accept_greedy(*args_))
 
     ev = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
-    rounds = {m: 0 for m in sweep}
 
     # each round's calls, marshalled once per (width, weight copy); with
     # --graph, captured once as HIP graphs (layers, head, accept) instead
@@ -151,11 +193,14 @@ def main():
     for m in sweep:
         for cp in range(args.copies):
             if args.graph:
-                graphs[(m, cp)] = stack.capture_round(m, cp, drafts[m], acc[m][0], acc[m][1])
+                graphs[(m, cp)] = stack.capture_calls(B * m, cp, accept_call(m, rounds_in[m], prepare=False),
+                                                      want_logits=sample)
             else:
-                prepared[(m, cp)] = stack.prepare_round(m, cp, drafts[m], acc[m][0], acc[m][1], stream)
+                layers, head = stack.prepare_round(B * m, cp, want_logits=sample, stream=stream)
+                prepared[(m, cp)] = (layers, head, accept_call(m, rounds_in[m]))
 
     def run_round(m: int, copy: int, record: list | None):
+        r = rounds_in[m]
         e = [ev() for _ in range(4)] if record is not None else None
         if e: e[0].record(stream)
         if args.graph:
@@ -173,7 +218,7 @@ def main():
             head()
             if e: e[2].record(stream)
             accept()
-        host_res[:1 + m].copy_(acc[m][2], non_blocking=True)   # the round's one device-to-host copy
+        host_res[:B + B * m].copy_(r["res"], non_blocking=True)   # the round's one device-to-host copy
         if e: e[3].record(stream)
         stream.synchronize()       # the round's one device sync
         if record is not None:
@@ -194,6 +239,7 @@ def main():
     gc.freeze()
     records = []
     committed = 0
+    faults = 0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     walls = []
@@ -201,7 +247,9 @@ def main():
         for m in sweep:
             tr = time.perf_counter()
             run_round(m, step_copy % args.copies, records)
-            committed += int(host_res[0])
+            lens = host_res[:B]
+            committed += int(lens.clamp(min=0).sum())
+            faults += int((lens < 0).sum())
             walls.append(time.perf_counter() - tr)
             step_copy += 1
     torch.cuda.synchronize()
@@ -217,25 +265,29 @@ def main():
     curve = {}
     head_ms_all, head_bytes_all = [], []
     for m in sweep:
+        M = B * m
         rs = [e for (mm, e) in records if mm == m]
         t_round = np.median([e[0].elapsed_time(e[3]) for e in rs])
         t_layer = np.median([e[0].elapsed_time(e[1]) for e in rs])
         t_head = [e[1].elapsed_time(e[2]) for e in rs]
+        t_acc = np.median([e[2].elapsed_time(e[3]) for e in rs])
         head_ms_all += t_head
-        head_bytes_all += [head_b + m * stack.hidden * 2 + m * 4] * len(t_head)
-        curve[m] = {"round_us": round(float(t_round) * 1e3, 2), "layer_us": round(float(t_layer) * 1e3, 2),
+        head_bytes_all += [head_b + M * stack.hidden * 2 + (M * V * 4 if sample else M * 4)] * len(t_head)
+        curve[M] = {"round_us": round(float(t_round) * 1e3, 2), "layer_us": round(float(t_layer) * 1e3, 2),
                     "head_us": round(float(np.median(t_head)) * 1e3, 2),
+                    "accept_copy_us": round(float(t_acc) * 1e3, 2),
                     "weight_GBps": round(round_b / (t_round * 1e-3) / 1e9, 1),
                     "hbm_frac": round(round_b / (t_round * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    t1 = curve[sweep[0]]["round_us"]
-    for m in sweep:
-        curve[m]["t_over_t1"] = round(curve[m]["round_us"] / t1, 4)
+    first = curve[B * sweep[0]]["round_us"]
+    for M in curve:
+        curve[M]["t_over_t1"] = round(curve[M]["round_us"] / first, 4)
 
     head_avg_s = float(np.mean(head_ms_all)) * 1e-3
     head_bytes = float(np.mean(head_bytes_all))
     achieved = head_bytes / head_avg_s / 1e9
+    profiled = args.config == "qwen3-4b" and args.bits == 8 and not sample and B == 1
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic() if profiled else None,
                 "kernel": f"qgemm_kernel<{args.bits},MT,true> (vocabulary head + argmax)",
                 "avg_launch_us": round(head_avg_s * 1e6, 2), "bytes_per_launch": int(head_bytes)}
 
@@ -247,24 +299,30 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args.config, args.bits, 8, args.cpu_sample_s)
+        cpu = cpu_baseline(args.config, args.bits, min(B * max(sweep), 8), args.cpu_sample_s)
 
+    workload = (f"{args.config} layer x{args.layers} + lm_head {V}x{stack.hidden}, "
+                f"{'bf16' if args.bits == 16 else str(args.bits) + '-bit g64'}, "
+                + (f"speculative sampling T={args.temperature}" if sample
+                   else f"greedy alpha={','.join(f'{a:g}' for a in alpha)}")
+                + (f", {B} requests x rows" if B > 1 else "") + f", one round per rows in {sweep}")
     out = {
         "metric": "verify weight-GB/s & % HBM peak vs width M=1..16; t(M)/t(1) cost curve",
         "value": round(value, 1), "unit": "weight-GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"{args.config} layer x{args.layers} + lm_head {V}x{stack.hidden}, "
-                               f"{args.bits}-bit g64, greedy alpha=0.7, one round per M in {sweep}",
-                   "widths": sweep, "weight_bytes_per_round": round_b, "rotating_copies": args.copies,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": workload, "widths": [B * m for m in sweep], "weight_bytes_per_round": round_b,
+                   "rotating_copies": args.copies,
                    "launch": "hip-graph replays" if args.graph else "host launches, arguments marshalled once"},
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
-        "t16_over_t1": curve[sweep[-1]]["t_over_t1"],
+        "t16_over_t1": curve[max(curve)]["t_over_t1"],
         "curve": curve,
         "rounds_per_s": round(n_rounds / wall, 1),
         "round_wall_us": {"p50": round(float(np.median(walls)) * 1e6, 1), "max": round(max(walls) * 1e6, 1)},
-        "rows_per_s": round(sum(sweep) * args.steps / wall, 1),
+        "rows_per_s": round(B * sum(sweep) * args.steps / wall, 1),
         "committed_tokens_per_round": round(committed / n_rounds, 3),
+        "accept_faults": faults,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(0), "host": platform.node(),

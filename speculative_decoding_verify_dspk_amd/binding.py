@@ -228,6 +228,14 @@ def prepare_accept_greedy(target_ids, draft_ids, b: int, m_rows: int, accept_len
                     committed.data_ptr(), _stream(stream))
 
 
+def prepare_accept_sample(logits, q, draft_ids, uniforms, m_rows: int, v: int, temperature: float, accept_len,
+                          committed, workspace, stream=None) -> Prepared:
+    return Prepared("dspk_accept_sample", logits.data_ptr(), _rows(logits, "logits"), q.data_ptr(), _rows(q, "q"),
+                    draft_ids.data_ptr(), uniforms.data_ptr(), m_rows, v, float(temperature),
+                    accept_len.data_ptr(), committed.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                    _stream(stream))
+
+
 # ------------------------------------------------------------ entry points
 def version() -> int:
     return lib().dspk_version()

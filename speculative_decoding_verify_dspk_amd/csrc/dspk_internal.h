@@ -29,10 +29,12 @@ hipError_t launch_pack(int32_t n, int32_t k, int bits, const void *codes, const 
                        const uint16_t *biases, void *tiles, hipStream_t s);
 
 // Register-ring depth (units in flight per wave) and workgroups per CU of the
-// projection kernel, by weight format and 16-row tiles; both keep a wave
-// within the registers that OCC waves per SIMD leave it.
+// projection kernel, by weight format and 16-row tiles.  Two 16-row tiles
+// (17..32 rows) need twice the activation and accumulator registers: one
+// workgroup per CU keeps them out of scratch (measured faster than two
+// workgroups that spill).
 constexpr int kernel_depth(int bits, int mt) { return 2 + 0 * bits * mt; }
-constexpr int kernel_occ(int bits, int mt) { return (bits == 4 && mt == 2) ? 1 : 2; }
+constexpr int kernel_occ(int bits, int mt) { return mt == 2 ? 1 : 2 + 0 * bits; }
 
 // Work of a projection launch is a list of quads: (weight, 64-column block,
 // four consecutive units), one unit per wave of a workgroup.  Quads are

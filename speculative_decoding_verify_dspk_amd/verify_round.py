@@ -106,26 +106,27 @@ class VerifyStack:
         binding.lmhead_argmax(self.heads[copy], self.h, m, self.argmax, self.logits if want_logits else None,
                               self.ws_head, stream)
 
-    def prepare_round(self, m: int, copy: int, draft_ids, accept_len, committed, stream=None):
-        """The round's calls at width m on weight copy ``copy`` with their
-        arguments marshalled once: (layer calls, head call, accept call)."""
+    def prepare_round(self, m: int, copy: int, want_logits: bool = False, stream=None):
+        """The round's projection and head calls at width m on weight copy
+        ``copy`` with their arguments marshalled once: (layer calls, head call)."""
         layers = []
         for L in self.layers[copy]:
             layers += [binding.prepare_qgemm_grouped(L.qkv, self.x_attn, m, self.y_qkv, self.ws_qkv, stream),
                        binding.prepare_qgemm(L.o, self.x_o, m, self.y_o, self.ws_o, stream),
                        binding.prepare_qgemm_grouped(L.gateup, self.x_mlp, m, self.y_gu, self.ws_gu, stream),
                        binding.prepare_qgemm(L.down, self.x_down, m, self.y_down, self.ws_down, stream)]
-        head = binding.prepare_lmhead(self.heads[copy], self.h, m, self.argmax, None, self.ws_head, stream)
-        accept = binding.prepare_accept_greedy(self.argmax, draft_ids, 1, m, accept_len, committed, stream)
-        return layers, head, accept
+        head = binding.prepare_lmhead(self.heads[copy], self.h, m, self.argmax, self.logits if want_logits else None,
+                                      self.ws_head, stream)
+        return layers, head
 
-    def capture_round(self, m: int, copy: int, draft_ids, accept_len, committed):
-        """HIP graphs (layers, head, accept) of one greedy round at width m on
-        weight copy ``copy``; replay them in that order on one stream."""
+    def capture_calls(self, m: int, copy: int, accept, want_logits: bool = False):
+        """HIP graphs (layers, head, accept) of one round at width m on weight
+        copy ``copy``; ``accept`` launches the acceptance step.  Replay them in
+        that order on one stream."""
         import torch
         fns = (lambda: self.launch_layers(m, copy),
-               lambda: self.launch_head(m, copy),
-               lambda: binding.accept_greedy(self.argmax, draft_ids, 1, m, accept_len, committed))
+               lambda: self.launch_head(m, copy, want_logits=want_logits),
+               accept)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):          # one eager pass before capture
@@ -140,3 +141,8 @@ class VerifyStack:
                 f()
             graphs.append(g)
         return graphs
+
+    def capture_round(self, m: int, copy: int, draft_ids, accept_len, committed):
+        """HIP graphs (layers, head, accept) of one greedy round at width m."""
+        return self.capture_calls(m, copy, lambda: binding.accept_greedy(self.argmax, draft_ids, 1, m, accept_len,
+                                                                          committed))
