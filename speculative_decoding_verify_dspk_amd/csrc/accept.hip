@@ -32,18 +32,18 @@ __global__ void accept_greedy_kernel(const int32_t *__restrict__ t, const int32_
 
 // -------------------------------------------------------------- sampling
 // Workspace layout (bytes): [0, 256) arrival counter; then per (row, chunk):
-// stats {max of z/T, sum exp(z/T - max)}, fault flag, masses {residual, p};
-// then per row {max, sum} of the whole row.
+// stats {max of z/T, sum exp(z/T - max)} and the fault flag; then per chunk
+// the masses {residual, p} of the row that supplies the final draw.
 constexpr int CH = kSampleChunk;
 constexpr int TPB = 256;
 constexpr int EPT = CH / TPB;    // logits per thread per chunk
+constexpr int kMaxRowsSample = kMaxRows;
 
 struct SampleWs {
     uint32_t *counter;
     float2 *stats;   // [rows][nchunks]
     int32_t *flags;  // [rows][nchunks]
-    float2 *mass;    // [rows][nchunks]
-    float2 *rowst;   // [rows]
+    float2 *mass;    // [nchunks]
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -58,9 +58,20 @@ __host__ __device__ inline SampleWs carve(void *ws, int rows, int nchunks) {
     s.flags = (int32_t *)p;
     p += align256((size_t)rows * nchunks * sizeof(int32_t));
     s.mass = (float2 *)p;
-    p += align256((size_t)rows * nchunks * sizeof(float2));
-    s.rowst = (float2 *)p;
     return s;
+}
+
+// Values one workgroup hands to another inside a kernel move through
+// device-scope atomic accesses: they are performed where all XCDs see them,
+// so no cache writeback or invalidation (a device-scope fence) is needed;
+// the writer waits for its stores to complete before it signals arrival.
+__device__ inline void store_f2(float2 *p, float2 v) {
+    __hip_atomic_store((unsigned long long *)p, __builtin_bit_cast(unsigned long long, v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float2 load_f2(const float2 *p) {
+    return __builtin_bit_cast(float2, __hip_atomic_load((unsigned long long *)p, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT));
 }
 
 // block-wide reductions in a fixed order (wave butterfly, then waves in order)
@@ -136,74 +147,90 @@ __global__ __launch_bounds__(TPB) void sample_stats_kernel(const float *__restri
     }
 }
 
-// Row maximum and normaliser from the chunk statistics (one wave, fixed order).
-__device__ inline float2 row_stats(const float2 *st, int nchunks, int lane) {
-    float mx = -INFINITY;
-    for (int c = lane; c < nchunks; c += 64) mx = fmaxf(mx, st[c].x);
-    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    float s = 0.f;
-    for (int c = lane; c < nchunks; c += 64) s += st[c].y * expf(st[c].x - mx);
-    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-    return make_float2(mx, s);
-}
-
-// Pass 2: per (row, chunk) mass of the residual max(0, p - q) (draft rows) and
-// of p; then the last workgroup to finish takes the sequential decision.
+// Pass 2, one workgroup per chunk.  Every workgroup repeats the (cheap,
+// deterministic) accept decisions from the row statistics of pass 1 -- so all
+// agree on the row jr that supplies the final draw -- and adds up, over its
+// chunk of row jr only, the mass of the residual max(0, p - q) and of p; the
+// last workgroup to finish draws the token.
 __global__ __launch_bounds__(TPB) void sample_decide_kernel(
     const float *__restrict__ z, int64_t ldz, const float *__restrict__ q, int64_t ldq,
     const int32_t *__restrict__ d, const float *__restrict__ u, int32_t rows, int32_t v,
     float temperature, int32_t *__restrict__ accept_len, int32_t *__restrict__ committed, void *ws) {
     __shared__ float scratch[TPB / 64];
-    __shared__ float2 s_row;
+    __shared__ float2 s_rows[kMaxRowsSample];
     __shared__ float s_pref[TPB];
-    __shared__ int s_flag[4];
+    __shared__ int s_flag[2];
+    __shared__ int s_jr, s_lastc;
+    __shared__ unsigned long long s_cut;
     const int nchunks = (v + CH - 1) / CH;
     const SampleWs W = carve(ws, rows, nchunks);
-    const int c = blockIdx.x, j = blockIdx.y, tid = threadIdx.x;
-    const int v0 = c * CH, v1 = min(v, v0 + CH);
+    const int c = blockIdx.x, tid = threadIdx.x;
 
-    if (tid < 64) {
-        const float2 rs = row_stats(W.stats + j * nchunks, nchunks, tid);
-        if (tid == 0) {
-            s_row = rs;
-            if (c == 0) W.rowst[j] = rs;
-        }
+    // row maxima and normalisers from the chunk statistics: eight threads per
+    // row, chunks k, k + 8, ... each, then a fixed butterfly over the eight
+    {
+        const int j = tid >> 3, k = tid & 7;
+        const float2 *st = W.stats + (int64_t)min(j, rows - 1) * nchunks;
+        float mx = -INFINITY;
+        for (int cc = k; cc < nchunks; cc += 8) mx = fmaxf(mx, st[cc].x);
+        for (int off = 1; off < 8; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+        float sm = 0.f;
+        for (int cc = k; cc < nchunks; cc += 8) sm += st[cc].y * expf(st[cc].x - mx);
+        for (int off = 1; off < 8; off <<= 1) sm += __shfl_xor(sm, off);
+        if (k == 0 && j < rows) s_rows[j] = make_float2(mx, sm);
     }
-    __syncthreads();
-    const float rmax = s_row.x, rsum = s_row.y;
-    const float *zr = z + (int64_t)j * ldz;
-    const bool draft_row = j < rows - 1;
-    const float *qr = q + (int64_t)j * ldq;
-    float res = 0.f, pm = 0.f;
-#pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-        const int col = v0 + tid + TPB * i;
-        if (col < v1) {
-            const float p = expf(zr[col] / temperature - rmax) / rsum;
-            pm += p;
-            if (draft_row) res += fmaxf(0.f, p - qr[col]);
-        }
-    }
-    const float rmass = block_sum(res, scratch);
-    const float pmass = block_sum(pm, scratch);
-    if (tid == 0) W.mass[j * nchunks + c] = make_float2(rmass, pmass);
-
-    // arrival: the last of all rows x chunks workgroups decides
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_flag[0] = atomicAdd(W.counter, 1u) == (uint32_t)(rows * nchunks - 1);
-    __syncthreads();
-    if (!s_flag[0]) return;
-    __threadfence();
-
-    // faults: any flagged chunk, a uniform outside [0, 1), a draft id outside [0, v)
+    // draft ids and uniforms in range (they index memory below)
     int bad = 0;
-    for (int i = tid; i < rows * nchunks; i += TPB) bad |= W.flags[i] != 0;
     if (tid < rows) {
         const float uu = u[tid];
         bad |= !(uu >= 0.f && uu < 1.f);
     }
     if (tid < rows - 1) bad |= (d[tid] < 0 || d[tid] >= v);
+    if (tid == 0) s_jr = rows - 1;
+    bad = __syncthreads_or(bad);
+    // Accept tests of all drafts at once (thread j tests draft j): the first
+    // reject ends the accepted prefix and supplies the final draw, else the
+    // last row does.
+    if (!bad && tid < rows - 1) {
+        const float2 rs = s_rows[tid];
+        const int dj = d[tid];
+        const float pd = expf(z[(int64_t)tid * ldz + dj] / temperature - rs.x) / rs.y;
+        const float qd = q[(int64_t)tid * ldq + dj];
+        if (!(u[tid] * qd < pd)) atomicMin(&s_jr, tid);
+    }
+    __syncthreads();
+    const int jr = s_jr;
+    const bool draft_row = jr < rows - 1;
+    {
+        const float2 rs = s_rows[jr];
+        const int v0 = c * CH, v1 = min(v, v0 + CH);
+        const float *zr = z + (int64_t)jr * ldz;
+        const float *qr = q + (int64_t)jr * ldq;
+        float res = 0.f, pm = 0.f;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            const int col = v0 + tid + TPB * i;
+            if (col < v1) {
+                const float p = expf(zr[col] / temperature - rs.x) / rs.y;
+                pm += p;
+                if (draft_row) res += fmaxf(0.f, p - qr[col]);
+            }
+        }
+        const float rmass = block_sum(res, scratch);
+        const float pmass = block_sum(pm, scratch);
+        // arrival: thread 0 wrote this workgroup's masses and waits for them
+        // to complete before it signals
+        if (tid == 0) {
+            store_f2(&W.mass[c], make_float2(rmass, pmass));
+            __builtin_amdgcn_s_waitcnt(0x0f70);     // vmcnt(0)
+            s_flag[0] = atomicAdd(W.counter, 1u) == (uint32_t)(nchunks - 1);
+        }
+    }
+    __syncthreads();
+    if (!s_flag[0]) return;
+
+    // faults: any flagged chunk (non-finite logit, bad q), a uniform or draft id out of range
+    for (int i = tid; i < rows * nchunks; i += TPB) bad |= W.flags[i] != 0;
     bad = __syncthreads_or(bad);
     if (bad) {
         if (tid < rows) committed[tid] = -1;
@@ -213,64 +240,63 @@ __global__ __launch_bounds__(TPB) void sample_decide_kernel(
         }
         return;
     }
-
-    // accept test per draft, in order, up to the first reject (thread 0)
+    if (tid < jr) committed[tid] = d[tid];
     if (tid == 0) {
-        int jr = rows - 1;   // row that supplies the final draw
-        for (int jj = 0; jj < rows - 1; ++jj) {
-            const float2 rs = W.rowst[jj];
-            const int dj = d[jj];
-            const float pd = expf(z[(int64_t)jj * ldz + dj] / temperature - rs.x) / rs.y;
-            const float qd = q[(int64_t)jj * ldq + dj];
-            if (u[jj] * qd < pd) {
-                committed[jj] = dj;
-            } else {
-                jr = jj;
-                break;
-            }
-        }
-        // mass to sample from: the residual on a reject (p if it has none), p for the bonus
-        int use_res = jr < rows - 1;
-        float total = 0.f;
-        for (int cc = 0; cc < nchunks; ++cc) total += use_res ? W.mass[jr * nchunks + cc].x : W.mass[jr * nchunks + cc].y;
-        if (use_res && !(total > 0.f)) {
-            use_res = 0;
-            total = 0.f;
-            for (int cc = 0; cc < nchunks; ++cc) total += W.mass[jr * nchunks + cc].y;
-        }
-        const float thr = u[rows - 1] * total;
-        float cum = 0.f;
-        int cstar = -1;
-        for (int cc = 0; cc < nchunks; ++cc) {
-            const float mc = use_res ? W.mass[jr * nchunks + cc].x : W.mass[jr * nchunks + cc].y;
-            if (cum + mc > thr) {
-                cstar = cc;
-                break;
-            }
-            cum += mc;
-        }
-        int last_pos = 0;   // no chunk crosses the threshold (rounding): last chunk with mass
-        if (cstar < 0) {
-            last_pos = 1;
-            cstar = nchunks - 1;
-            for (int cc = nchunks - 1; cc >= 0; --cc) {
-                const float mc = use_res ? W.mass[jr * nchunks + cc].x : W.mass[jr * nchunks + cc].y;
-                if (mc > 0.f) {
-                    cstar = cc;
-                    break;
-                }
-            }
-        }
-        s_flag[0] = jr;
-        s_flag[1] = use_res;
-        s_flag[2] = cstar;
-        s_flag[3] = last_pos;
-        s_pref[0] = thr - cum;
+        s_lastc = -1;
+        s_cut = ~0ull;
     }
-    __syncthreads();
-    const int jr = s_flag[0], use_res = s_flag[1], cstar = s_flag[2], last_pos = s_flag[3];
-    const float thr_local = s_pref[0];
-    const float2 rs = W.rowst[jr];
+    // mass to sample from: the residual on a reject (p if it has none), p for
+    // the bonus; totals over the chunks in a fixed order
+    float tr = 0.f, tp = 0.f;
+    for (int cc = tid; cc < nchunks; cc += TPB) {
+        const float2 mm = load_f2(&W.mass[cc]);
+        tr += mm.x;
+        tp += mm.y;
+    }
+    const float total_res = block_sum(tr, scratch);
+    const float total_p = block_sum(tp, scratch);
+    const int use_res = draft_row && total_res > 0.f;
+    const float thr = u[rows - 1] * (use_res ? total_res : total_p);
+    // chunk holding the draw: the first whose inclusive prefix of masses
+    // exceeds thr (prefix sums in chunk order, TPB chunks per round); its
+    // exclusive prefix travels with it in one 64-bit key
+    float carry = 0.f;
+    for (int b0 = 0; b0 < nchunks; b0 += TPB) {
+        const int cc = b0 + tid;
+        float mc = 0.f;
+        if (cc < nchunks) {
+            const float2 mm = load_f2(&W.mass[cc]);
+            mc = use_res ? mm.x : mm.y;
+        }
+        s_pref[tid] = mc;
+        __syncthreads();
+        for (int off = 1; off < TPB; off <<= 1) {
+            const float add = tid >= off ? s_pref[tid - off] : 0.f;
+            __syncthreads();
+            s_pref[tid] += add;
+            __syncthreads();
+        }
+        const float incl = carry + s_pref[tid];
+        if (cc < nchunks && incl > thr)
+            atomicMin(&s_cut, ((unsigned long long)cc << 32) | __float_as_uint(incl - mc));
+        if (cc < nchunks && mc > 0.f) atomicMax(&s_lastc, cc);
+        carry += s_pref[TPB - 1];
+        __syncthreads();
+    }
+    const unsigned long long cut = s_cut;
+    int cstar, last_pos;
+    float thr_local;
+    if (cut != ~0ull) {
+        cstar = (int)(cut >> 32);
+        last_pos = 0;
+        thr_local = thr - __uint_as_float((uint32_t)cut);
+    } else {
+        // no chunk crosses the threshold (rounding): the last chunk with mass
+        cstar = s_lastc >= 0 ? s_lastc : nchunks - 1;
+        last_pos = 1;
+        thr_local = 0.f;
+    }
+    const float2 rs = s_rows[jr];
     __syncthreads();
 
     // inverse CDF inside chunk cstar: thread t owns EPT consecutive logits
@@ -332,7 +358,7 @@ __global__ __launch_bounds__(TPB) void sample_decide_kernel(
 size_t sample_workspace_bytes(int32_t v, int32_t m_rows) {
     const size_t nchunks = (size_t)(v + CH - 1) / CH;
     return 256 + align256(m_rows * nchunks * sizeof(float2)) + align256(m_rows * nchunks * sizeof(int32_t)) +
-           align256(m_rows * nchunks * sizeof(float2)) + align256(m_rows * sizeof(float2));
+           align256(nchunks * sizeof(float2));
 }
 
 hipError_t launch_accept_greedy(const int32_t *t, const int32_t *d, int32_t b, int32_t m_rows,
@@ -352,8 +378,8 @@ hipError_t launch_accept_sample(const float *z, int64_t ldz, const float *q, int
                        temperature, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(sample_decide_kernel, dim3(nchunks, m_rows), dim3(TPB), 0, s, z, ldz, q, ldq, d, u,
-                       m_rows, v, temperature, accept_len, committed, ws);
+    hipLaunchKernelGGL(sample_decide_kernel, dim3(nchunks), dim3(TPB), 0, s, z, ldz, q, ldq, d, u, m_rows, v,
+                       temperature, accept_len, committed, ws);
     return hipGetLastError();
 }
 
