@@ -282,6 +282,17 @@ def main():
     for M in curve:
         curve[M]["t_over_t1"] = round(curve[M]["round_us"] / first, 4)
 
+    # the cap policy on the measured curve (verify round at widths 1..max,
+    # interpolated between the measured widths; drafter time not included)
+    cap_policy = None
+    if B == 1 and len(sweep) > 1 and sweep[0] == 1:
+        widths = np.arange(1, max(sweep) + 1)
+        t_us = np.interp(widths, sweep, [curve[m]["round_us"] for m in sweep])
+        cap_policy = {}
+        for a in (0.3, 0.5, 0.7, 0.9):
+            cap, rate = binding.choose_cap(t_us, None, a)
+            cap_policy[str(a)] = {"cap": cap, "speedup_vs_plain": round(rate * t_us[0], 3)}
+
     head_avg_s = float(np.mean(head_ms_all)) * 1e-3
     head_bytes = float(np.mean(head_bytes_all))
     achieved = head_bytes / head_avg_s / 1e9
@@ -323,6 +334,7 @@ def main():
         "rows_per_s": round(B * sum(sweep) * args.steps / wall, 1),
         "committed_tokens_per_round": round(committed / n_rounds, 3),
         "accept_faults": faults,
+        "cap_policy": cap_policy,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(0), "host": platform.node(),

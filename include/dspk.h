@@ -254,6 +254,61 @@ int dspk_accept_sample(const float *logits, int64_t ldz,
                        int32_t *accept_len, int32_t *committed,
                        void *workspace, size_t ws_bytes, void *stream);
 
+/*
+ * Draft-cap policy (host code; no GPU, no workspace).
+ *
+ * The cap -- how many drafts a round verifies -- does not change what is
+ * committed, only how fast ("mlx-dspark 0.7.0", "Tuning": the cap is
+ * measured per machine and format, not hard-coded).  A round that drafts c
+ * tokens commits 1 + sum_{i=1..c} alpha^i tokens in expectation, alpha the
+ * per-position acceptance ("mlx-dspark" wiki summary, "Key techniques",
+ * auto-calibration bullet), and costs one verify pass at width c + 1 plus the
+ * drafter's work ("mlx-dspark 0.7.0", "The Apple-Silicon speedup ceiling").
+ *
+ *   verify_us : host double [n], verify round time (us) at width 1 .. n,
+ *               as measured on this device (e.g. the benchmark's curve);
+ *   draft_us  : host double [n] or NULL, drafter time per round at cap
+ *               0 .. n-1 (entry 0 is ignored: a parked round drafts nothing).
+ *
+ * dspk_choose_cap returns the cap c in 0 .. n-1 with the most expected
+ * tokens per microsecond (ties: the smaller cap; 0 = speculation parked)
+ * and stores that rate in *tokens_per_us if not NULL; it returns DSPK_EINVAL
+ * for n outside 1 .. DSPK_MAX_ROWS, non-positive or non-finite times, or
+ * alpha outside [0, 1] (these calls set no message).
+ */
+int32_t dspk_choose_cap(const double *verify_us, const double *draft_us, int32_t n, double alpha,
+                        double *tokens_per_us);
+
+/*
+ * A cap controller: the curves above plus a live acceptance estimate (an
+ * exponentially weighted count of accepted / tested draft positions; a
+ * round that accepts a of d drafts tested a positions plus the first
+ * reject).  While the best cap is 0 (parked), every probe_every-th round
+ * drafts probe_cap tokens so that the estimate can recover ("mlx-dspark
+ * 0.7.0", "Tuning": park with periodic probe rounds).  Plain host struct,
+ * owned by the caller; one controller per request stream.
+ */
+typedef struct dspk_cap_controller {
+    double verify_us[DSPK_MAX_ROWS];
+    double draft_us[DSPK_MAX_ROWS];
+    int32_t n;
+    double decay;          /* weight of the past per observed round, (0, 1] */
+    double hits, trials;   /* weighted accepted and tested positions */
+    int32_t probe_every;
+    int32_t probe_cap;
+    int32_t parked_rounds;
+} dspk_cap_controller;
+
+/* prior_alpha counts as one tested position; probe_cap in 1 .. n-1. */
+int dspk_cap_init(dspk_cap_controller *ctl, const double *verify_us, const double *draft_us, int32_t n,
+                  double decay, double prior_alpha, int32_t probe_every, int32_t probe_cap);
+/* Cap for the next round (0 = a plain step), or DSPK_EINVAL. */
+int32_t dspk_cap_next(dspk_cap_controller *ctl);
+/* Record a round's outcome: drafted tokens, accepted drafts (0 .. drafted). */
+int dspk_cap_observe(dspk_cap_controller *ctl, int32_t drafted, int32_t accepted);
+/* The current acceptance estimate. */
+double dspk_cap_alpha(const dspk_cap_controller *ctl);
+
 #ifdef __cplusplus
 }
 #endif

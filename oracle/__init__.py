@@ -7,4 +7,5 @@ from .dspk_oracle import (  # noqa: F401
     GROUP, decode_fp16, decode_bf16, unpack_codes, dequantize, qlinear,
     argmax_lowest, lmhead_argmax, accept_greedy, sequential_greedy,
     softmax_t, inverse_cdf, accept_sample,
+    expected_committed, choose_cap, CapController,
 )

@@ -25,6 +25,12 @@ What it computes, and the passages it follows (pages quoted by title):
 * "mlx-dspark releases", v0.0.2 notes: the sampling path was validated to give
   exactly the target's output distribution.
 
+* "mlx-dspark 0.7.0", "Tuning" and "The Apple-Silicon speedup ceiling"; wiki
+  summary "Key techniques" (auto-calibration) and "Design decisions": the
+  draft cap is chosen from measured verify/drafter cost curves and a live
+  acceptance estimate, maximising expected committed tokens per unit time,
+  and speculation parks (with probe rounds) when it would lose.
+
 Readings where the pages are silent (quantisation format, packing, tie rule,
 the extra committed token, strictness of the accept test, residual with zero
 mass, inverse-CDF rule) are listed in the design notes and restated at each
@@ -269,3 +275,66 @@ def accept_sample(logits, q, draft_ids, uniforms, temperature: float):
     p = softmax_t(z[m_rows - 1], temperature)
     committed[m_rows - 1] = inverse_cdf(p, final_u * p.sum())
     return m_rows, committed
+
+
+# ------------------------------------------------------------ cap policy
+def expected_committed(cap: int, alpha: float) -> float:
+    """Expected tokens committed by a round that drafts ``cap`` tokens with
+    per-position acceptance alpha: 1 + sum_{i=1..cap} alpha^i ("mlx-dspark"
+    wiki summary, "Key techniques", auto-calibration bullet)."""
+    return float(sum(alpha ** i for i in range(cap + 1)))
+
+
+def choose_cap(verify_us, draft_us, alpha: float) -> tuple[int, float]:
+    """The cap c in 0..n-1 with the most expected tokens per microsecond,
+    a round costing the verify pass at width c + 1 plus the drafter's time
+    at cap c (none at c = 0) ("mlx-dspark 0.7.0", "The Apple-Silicon
+    speedup ceiling": tok/s = A / (drafter + overhead + slope * C); "Tuning":
+    the cap is chosen from the measured curves).  Ties keep the smaller cap;
+    cap 0 means speculation is parked.  Returns (cap, tokens per us)."""
+    n = len(verify_us)
+    best, best_rate = 0, None
+    for c in range(n):
+        cost = float(verify_us[c]) + (float(draft_us[c]) if (draft_us is not None and c > 0) else 0.0)
+        rate = expected_committed(c, alpha) / cost
+        if best_rate is None or rate > best_rate:
+            best, best_rate = c, rate
+    return best, best_rate
+
+
+class CapController:
+    """Cap per round from the curves and a live acceptance estimate: an
+    exponentially weighted count of accepted over tested draft positions (a
+    round accepting a of d drafts tested a positions, plus the first reject
+    when a < d); the prior counts as one tested position.  While the best cap
+    is 0 (parked), every probe_every-th round drafts probe_cap tokens
+    ("mlx-dspark 0.7.0", "Tuning": parks speculation with periodic probe
+    rounds)."""
+
+    def __init__(self, verify_us, draft_us, decay: float, prior_alpha: float, probe_every: int, probe_cap: int):
+        self.verify_us, self.draft_us = list(verify_us), (None if draft_us is None else list(draft_us))
+        self.decay = decay
+        self.hits, self.trials = prior_alpha, 1.0
+        self.probe_every, self.probe_cap = probe_every, probe_cap
+        self.parked_rounds = 0
+
+    def alpha(self) -> float:
+        return self.hits / self.trials
+
+    def observe(self, drafted: int, accepted: int) -> None:
+        if drafted == 0:
+            return
+        tested = accepted + (1 if accepted < drafted else 0)
+        self.hits = self.decay * self.hits + accepted
+        self.trials = self.decay * self.trials + tested
+
+    def next_cap(self) -> int:
+        cap, _ = choose_cap(self.verify_us, self.draft_us, self.alpha())
+        if cap > 0:
+            self.parked_rounds = 0
+            return cap
+        self.parked_rounds += 1
+        if self.parked_rounds >= self.probe_every:
+            self.parked_rounds = 0
+            return self.probe_cap
+        return 0

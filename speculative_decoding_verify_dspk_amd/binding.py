@@ -42,6 +42,14 @@ class TiledDesc(ctypes.Structure):
     _fields_ = [("n", c_int32), ("k", c_int32), ("bits", c_int32), ("group", c_int32), ("tiles", c_void_p)]
 
 
+class CapControllerDesc(ctypes.Structure):
+    """dspk_cap_controller (host struct)."""
+    _fields_ = [("verify_us", ctypes.c_double * MAX_ROWS), ("draft_us", ctypes.c_double * MAX_ROWS),
+                ("n", c_int32), ("decay", ctypes.c_double), ("hits", ctypes.c_double),
+                ("trials", ctypes.c_double), ("probe_every", c_int32), ("probe_cap", c_int32),
+                ("parked_rounds", c_int32)]
+
+
 _LIB = None
 
 
@@ -75,6 +83,13 @@ def lib() -> ctypes.CDLL:
         "dspk_accept_sample": (c_int32, [c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_void_p, c_int32,
                                          c_int32, c_float, c_void_p, c_void_p, c_void_p, c_size_t,
                                          c_void_p]),
+        "dspk_choose_cap": (c_int32, [P(ctypes.c_double), P(ctypes.c_double), c_int32, ctypes.c_double,
+                                      P(ctypes.c_double)]),
+        "dspk_cap_init": (c_int32, [P(CapControllerDesc), P(ctypes.c_double), P(ctypes.c_double), c_int32,
+                                    ctypes.c_double, ctypes.c_double, c_int32, c_int32]),
+        "dspk_cap_next": (c_int32, [P(CapControllerDesc)]),
+        "dspk_cap_observe": (c_int32, [P(CapControllerDesc), c_int32, c_int32]),
+        "dspk_cap_alpha": (ctypes.c_double, [P(CapControllerDesc)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -171,6 +186,40 @@ class DeviceQWeight:
 
 def tiled_bytes(n: int, k: int, bits: int) -> int:
     return lib().dspk_tiled_bytes(n, k, bits)
+
+
+# ------------------------------------------------------------ cap policy
+def _doubles(xs):
+    return None if xs is None else (ctypes.c_double * len(xs))(*[float(x) for x in xs])
+
+
+def choose_cap(verify_us, draft_us, alpha: float) -> tuple[int, float]:
+    """(cap, expected tokens per us) for a measured verify curve (width 1..n)."""
+    rate = ctypes.c_double(0.0)
+    cap = lib().dspk_choose_cap(_doubles(verify_us), _doubles(draft_us), len(verify_us), float(alpha),
+                                ctypes.byref(rate))
+    if cap < 0:
+        raise DspkError(cap, "dspk_choose_cap: invalid curve or alpha")
+    return cap, rate.value
+
+
+class CapController:
+    """The library's cap controller (host struct owned here)."""
+
+    def __init__(self, verify_us, draft_us=None, decay: float = 0.9, prior_alpha: float = 0.5,
+                 probe_every: int = 8, probe_cap: int = 1):
+        self.st = CapControllerDesc()
+        _check(lib().dspk_cap_init(ctypes.byref(self.st), _doubles(verify_us), _doubles(draft_us),
+                                   len(verify_us), decay, prior_alpha, probe_every, probe_cap))
+
+    def next_cap(self) -> int:
+        return lib().dspk_cap_next(ctypes.byref(self.st))
+
+    def observe(self, drafted: int, accepted: int) -> None:
+        _check(lib().dspk_cap_observe(ctypes.byref(self.st), drafted, accepted))
+
+    def alpha(self) -> float:
+        return lib().dspk_cap_alpha(ctypes.byref(self.st))
 
 
 # ------------------------------------------------------- prepared launches

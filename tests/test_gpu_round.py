@@ -95,3 +95,18 @@ def test_graph_replays_match_eager_round():
         # eager work between replays: an unrelated eager call on the same workspaces
         st.launch_head(m)
         torch.cuda.synchronize()
+
+
+def test_measured_curve_drives_the_cap_policy(tmp_path):
+    """The verify-cost curve measured on this GPU (cached on disk) feeds the
+    cap controller: costs are positive, and a perfect drafter is never parked."""
+    from speculative_decoding_verify_dspk_amd import binding, calibration
+    from speculative_decoding_verify_dspk_amd.verify_round import VerifyStack
+    st = VerifyStack("qwen3-4b", 1, 8, 8)
+    key = calibration.cache_key("qwen3-4b", 8)
+    curve = calibration.load_or_measure(str(tmp_path / "c.json"), key,
+                                        lambda: calibration.measure_verify_curve(st, range(1, 9), reps=3))
+    assert len(curve) == 8 and all(t > 0 for t in curve)
+    cap, rate = binding.choose_cap(curve, None, 1.0)
+    assert cap >= 1 and rate > 1.0 / curve[0]
+    assert binding.choose_cap(curve, None, 0.0)[0] == 0
