@@ -8,4 +8,5 @@ from .dspk_oracle import (  # noqa: F401
     argmax_lowest, lmhead_argmax, accept_greedy, sequential_greedy,
     softmax_t, inverse_cdf, accept_sample,
     expected_committed, choose_cap, CapController,
+    penalized_logits, truncate, accept_sample_filtered,
 )

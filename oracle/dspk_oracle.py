@@ -338,3 +338,110 @@ class CapController:
             self.parked_rounds = 0
             return self.probe_cap
         return 0
+
+
+# -------------------------------------------- truncated / penalised sampling
+def penalized_logits(logits, counts, draft_ids, presence: float, frequency: float) -> np.ndarray:
+    """Target logits with presence/frequency penalties, row by row
+    ("mlx-dspark releases", v0.2.0 notes: the penalties are applied to the
+    target logits so that speculative output equals sequential decoding of the
+    penalised target).  Row j is reached only when drafts 0..j-1 were
+    accepted, so its token counts are the history's plus those drafts:
+        c_j(v) = counts[v] + #{i < j : d_i = v}
+        z'_j(v) = z_j(v) - presence * [c_j(v) > 0] - frequency * c_j(v)
+    (the OpenAI definition the pages name)."""
+    z = np.asarray(logits, dtype=np.float64)
+    m_rows, v = z.shape
+    c = np.zeros(v, dtype=np.float64) if counts is None else np.asarray(counts, dtype=np.float64).copy()
+    d = np.asarray(draft_ids, dtype=np.int64).ravel()
+    out = np.empty_like(z)
+    for j in range(m_rows):
+        out[j] = z[j] - presence * (c > 0) - frequency * c
+        if j < m_rows - 1 and 0 <= d[j] < v:
+            c[d[j]] += 1
+    return out
+
+
+def truncate(prob, top_k: int, top_p: float) -> np.ndarray:
+    """Keep-mask of top-k then top-p truncation of one distribution
+    ("mlx-dspark releases", v0.1.0 notes: nucleus / top-k truncation applied
+    to both the draft and the target keeps sampling exact for the truncated
+    target).  Reading: order the entries by probability, larger first, ties by
+    the smaller index; top-k keeps the first k (k <= 0: all); top-p then keeps
+    an entry iff the mass of the kept entries before it is below
+    top_p * (mass kept by top-k) -- the smallest leading set whose mass
+    reaches top_p of the top-k distribution (top_p >= 1: all)."""
+    w = np.asarray(prob, dtype=np.float64)
+    v = w.size
+    order = np.lexsort((np.arange(v), -w))       # by -w, then index
+    keep = np.zeros(v, dtype=bool)
+    kk = v if top_k <= 0 else min(top_k, v)
+    kept = order[:kk]
+    if top_p < 1.0:
+        target = top_p * w[kept].sum()
+        excl = np.concatenate([[0.0], np.cumsum(w[kept])[:-1]])
+        kept = kept[excl < target]
+    keep[kept] = True
+    return keep
+
+
+def accept_sample_filtered(logits, q, draft_ids, uniforms, temperature: float, top_k: int = 0,
+                           top_p: float = 1.0, counts=None, presence: float = 0.0,
+                           frequency: float = 0.0):
+    """Speculative sampling over the penalised, truncated target.
+
+    p_j = truncate(softmax(z'_j / T)) renormalised, z' the penalised logits;
+    q~_j = truncate(q_j) renormalised with the same top-k/top-p (the draft
+    was drawn from q~_j).  Then the rule of accept_sample: accept d_j iff
+    u_j * q~_j(d_j) < p~_j(d_j); at the first reject sample the residual
+    max(0, p~_j - q~_j) (p~_j if it has no mass); else the bonus from p~_{M-1}.
+    Without truncation (top_k <= 0 and top_p >= 1) q is used as supplied, as
+    in accept_sample.  Faults as accept_sample, plus top_p outside (0, 1],
+    negative penalties' counts, and counts < 0."""
+    z = np.asarray(logits, dtype=np.float64)
+    m_rows, v = z.shape
+    qq = np.asarray(q, dtype=np.float64).reshape(m_rows - 1, v)
+    d = np.asarray(draft_ids, dtype=np.int64).ravel()
+    u = np.asarray(uniforms, dtype=np.float64).ravel()
+    committed = np.full(m_rows, -1, dtype=np.int32)
+    bad = (not np.isfinite(temperature) or temperature <= 0 or not (0 < top_p <= 1)
+           or not np.isfinite(z).all()
+           or not np.isfinite(qq).all() or (qq < 0).any()
+           or not np.isfinite(u).all() or (u < 0).any() or (u >= 1).any()
+           or (d < 0).any() or (d >= v).any()
+           or (counts is not None and (np.asarray(counts) < 0).any()))
+    if bad:
+        return -1, committed
+    trunc = top_k > 0 or top_p < 1.0
+    zp = penalized_logits(z, counts, d, presence, frequency)
+
+    def target(j):
+        p = softmax_t(zp[j], temperature)
+        if trunc:
+            p = np.where(truncate(p, top_k, top_p), p, 0.0)
+            p = p / p.sum()
+        return p
+
+    def draft(j):
+        if not trunc:
+            return qq[j]
+        w = np.where(truncate(qq[j], top_k, top_p), qq[j], 0.0)
+        s = w.sum()
+        return w / s if s > 0 else w
+
+    final_u = u[m_rows - 1]
+    for j in range(m_rows - 1):
+        p, qj = target(j), draft(j)
+        if u[j] * qj[d[j]] < p[d[j]]:
+            committed[j] = d[j]
+            continue
+        r = np.maximum(0.0, p - qj)
+        mass = r.sum()
+        if not mass > 0:
+            r = p
+            mass = p.sum()
+        committed[j] = inverse_cdf(r, final_u * mass)
+        return j + 1, committed
+    p = target(m_rows - 1)
+    committed[m_rows - 1] = inverse_cdf(p, final_u * p.sum())
+    return m_rows, committed
