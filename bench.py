@@ -16,6 +16,9 @@ Other workloads of the same path:
   --config dense-27b --layers 64 --sweep 17 --copies 1 --accept sample
         64 resident 27B-shaped layers, M = 17, speculative sampling at T = 1
         against draft distributions q = softmax(target logits + N(0, 0.5));
+        add --top-k 50 --top-p 0.9 --presence 0.5 --frequency 0.1 for the
+        truncated, penalised rule (history counts of a seeded 4096-token
+        Zipf-like history; drafts drawn from the untruncated q);
   --config ornith-9b --bits 4|8|16 --sweep 1,2,...,16
         the 9B-shaped layer and 151936x4096 head per weight format;
   --config qwen3-8b --batch 4 --sweep 6 --alpha 0.3,0.5,0.7,0.9
@@ -56,6 +59,11 @@ def parse():
     ap.add_argument("--accept", default="greedy", choices=["greedy", "sample"])
     ap.add_argument("--temperature", type=float, default=1.0)
     ap.add_argument("--noise", type=float, default=0.5, help="std of the drafter's logit noise (sampling)")
+    ap.add_argument("--top-k", type=int, default=0, help="sampling: top-k truncation of target and draft (0: off)")
+    ap.add_argument("--top-p", type=float, default=1.0, help="sampling: nucleus truncation (1: off)")
+    ap.add_argument("--presence", type=float, default=0.0, help="sampling: presence penalty")
+    ap.add_argument("--frequency", type=float, default=0.0, help="sampling: frequency penalty")
+    ap.add_argument("--history", type=int, default=4096, help="sampling with penalties: history length (tokens)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-s", type=float, default=20.0)
     ap.add_argument("--graph", action="store_true",
@@ -148,6 +156,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     sample = args.accept == "sample"
+    filtered = sample and (args.top_k > 0 or args.top_p < 1.0 or args.presence != 0.0 or args.frequency != 0.0)
     max_m = B * max(sweep)
     stack = VerifyStack(args.config, args.layers, args.bits, max_m, copies=args.copies)
     stream = torch.cuda.current_stream()
@@ -171,6 +180,10 @@ def main():
             r["d"] = torch.from_numpy(d).cuda()
             r["u"] = torch.from_numpy(inputs.make_uniforms(m, "bench", args.config, m)).cuda()
             r["ws"] = binding.alloc_workspace(binding.sample_workspace_bytes(V, m))
+            if filtered:
+                r["params"] = binding.sample_params(args.temperature, args.top_k, args.top_p, args.presence,
+                                                    args.frequency)
+                r["counts"] = torch.from_numpy(inputs.history_counts(V, args.history, "bench", args.config)).cuda()
         else:
             d = inputs.drafts_match_rate(t, alpha, V, "bench", args.config, m) if m > 1 else None
             r["d"] = torch.from_numpy(np.ascontiguousarray(d, dtype=np.int32)).cuda() if m > 1 else None
@@ -178,6 +191,11 @@ def main():
     host_res = torch.empty((B + max_m,), dtype=torch.int32).pin_memory()
 
     def accept_call(m, r, prepare=True):
+        if filtered:
+            args_ = (stack.logits, r["q"], r["d"], r["u"], m, V, r["params"], r["counts"], r["alen"], r["com"],
+                     r["ws"])
+            return binding.prepare_accept_sample_ex(*args_, stream) if prepare else \
+                (lambda: binding.accept_sample_ex(*args_))
         if sample:
             args_ = (stack.logits, r["q"], r["d"], r["u"], m, V, args.temperature, r["alen"], r["com"], r["ws"])
             return binding.prepare_accept_sample(*args_, stream) if prepare else \
@@ -316,6 +334,8 @@ def main():
                 f"{'bf16' if args.bits == 16 else str(args.bits) + '-bit g64'}, "
                 + (f"speculative sampling T={args.temperature}" if sample
                    else f"greedy alpha={','.join(f'{a:g}' for a in alpha)}")
+                + (f" top_k={args.top_k} top_p={args.top_p:g} presence={args.presence:g} "
+                   f"frequency={args.frequency:g} over a {args.history}-token history" if filtered else "")
                 + (f", {B} requests x rows" if B > 1 else "") + f", one round per rows in {sweep}")
     out = {
         "metric": "verify weight-GB/s & % HBM peak vs width M=1..16; t(M)/t(1) cost curve",

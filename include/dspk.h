@@ -15,6 +15,7 @@
  *   dspk_lmhead_argmax  - the vocabulary projection fused with the row argmax;
  *   dspk_accept_greedy  - longest matching prefix plus the target's token;
  *   dspk_accept_sample  - min(1, p/q) acceptance with residual resampling.
+ *   dspk_accept_sample_ex - the same over penalised, top-k/top-p truncated distributions.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -222,7 +223,8 @@ int dspk_accept_greedy(const int32_t *target_ids, const int32_t *draft_ids,
                        int32_t b, int32_t m_rows,
                        int32_t *accept_len, int32_t *committed, void *stream);
 
-/* Workspace for dspk_accept_sample (zero-filled before first use, left zeroed). */
+/* Workspace for dspk_accept_sample and dspk_accept_sample_ex (zero-filled before
+ * first use, left zeroed). */
 size_t dspk_sample_workspace_bytes(int32_t v, int32_t m_rows);
 
 /*
@@ -253,6 +255,63 @@ int dspk_accept_sample(const float *logits, int64_t ldz,
                        const float *uniforms, int32_t m_rows, int32_t v, float temperature,
                        int32_t *accept_len, int32_t *committed,
                        void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Sampling options of dspk_accept_sample_ex.
+ *
+ *   temperature       : > 0 and finite;
+ *   top_k             : keep the k most probable entries (0: off; >= v: off);
+ *   top_p             : in (0, 1]; keep the smallest leading set whose mass
+ *                       reaches top_p of the top-k mass (1: off);
+ *   presence_penalty,
+ *   frequency_penalty : finite; OpenAI penalties on the target logits.
+ */
+typedef struct dspk_sample_params {
+    float temperature;
+    int32_t top_k;
+    float top_p;
+    float presence_penalty;
+    float frequency_penalty;
+} dspk_sample_params;
+
+/*
+ * Stochastic acceptance over the penalised, truncated target
+ * ("mlx-dspark releases", v0.1.0 notes: top-k / nucleus truncation of both
+ * the draft and the target keeps speculative sampling exact for the
+ * truncated target; v0.2.0 notes: presence/frequency penalties on the target
+ * logits, so the output equals sequential decoding of the penalised target).
+ *
+ * Row j's penalised logits: z'_j(c) = z_j(c) - presence * [n_j(c) > 0]
+ * - frequency * n_j(c), where n_j(c) = counts[c] + #{i < j : draft_i = c}
+ * (row j is reached only after drafts 0 .. j-1 were accepted).
+ * p_j = softmax(z'_j / T).  Truncation orders a row's entries by value
+ * (larger first, ties by the smaller column), keeps the first top_k, then
+ * keeps an entry iff the kept mass before it is below top_p times the top-k
+ * mass.  p~_j is p_j truncated and renormalised; q~_j is q_j truncated the
+ * same way and renormalised (all zero if nothing with mass is kept).
+ * Without truncation (top_k = 0 or >= v, and top_p = 1) q is used as given.
+ * Then the rule of dspk_accept_sample with p~ and q~: accept draft j iff
+ * u_j * q~_j(d_j) < p~_j(d_j); at the first reject draw from
+ * norm(max(0, p~_j - q~_j)) (from p~_j if that has no mass), else the bonus
+ * from p~_{m_rows-1}, with u_{m_rows-1}, index-order inverse CDF.
+ *
+ *   params : host pointer (read during the call only);
+ *   counts : int32 [v] device, the history's token counts, or NULL (none);
+ *            a negative count is a data fault.
+ * Other arguments, faults and the workspace are as in dspk_accept_sample.
+ * Returns DSPK_EINVAL for a bad parameter (temperature <= 0 or not finite,
+ * top_k < 0, top_p outside (0, 1], a non-finite penalty).
+ * Truncation bounds are found by exact radix selection over unique order keys;
+ * masses for top-p are counted in fixed point with unit (largest entry of the
+ * row) / 2^37, so an entry whose preceding mass is within v * 2^-37 of the
+ * top-p threshold may fall on either side.
+ */
+int dspk_accept_sample_ex(const float *logits, int64_t ldz,
+                          const float *q, int64_t ldq, const int32_t *draft_ids,
+                          const float *uniforms, int32_t m_rows, int32_t v,
+                          const dspk_sample_params *params, const int32_t *counts,
+                          int32_t *accept_len, int32_t *committed,
+                          void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * Draft-cap policy (host code; no GPU, no workspace).

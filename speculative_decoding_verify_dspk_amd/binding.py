@@ -50,6 +50,17 @@ class CapControllerDesc(ctypes.Structure):
                 ("parked_rounds", c_int32)]
 
 
+class SampleParamsDesc(ctypes.Structure):
+    """dspk_sample_params (host struct)."""
+    _fields_ = [("temperature", c_float), ("top_k", c_int32), ("top_p", c_float),
+                ("presence_penalty", c_float), ("frequency_penalty", c_float)]
+
+
+def sample_params(temperature: float, top_k: int = 0, top_p: float = 1.0, presence: float = 0.0,
+                  frequency: float = 0.0) -> SampleParamsDesc:
+    return SampleParamsDesc(float(temperature), int(top_k), float(top_p), float(presence), float(frequency))
+
+
 _LIB = None
 
 
@@ -83,6 +94,9 @@ def lib() -> ctypes.CDLL:
         "dspk_accept_sample": (c_int32, [c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_void_p, c_int32,
                                          c_int32, c_float, c_void_p, c_void_p, c_void_p, c_size_t,
                                          c_void_p]),
+        "dspk_accept_sample_ex": (c_int32, [c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_void_p, c_int32,
+                                            c_int32, P(SampleParamsDesc), c_void_p, c_void_p, c_void_p, c_void_p,
+                                            c_size_t, c_void_p]),
         "dspk_choose_cap": (c_int32, [P(ctypes.c_double), P(ctypes.c_double), c_int32, ctypes.c_double,
                                       P(ctypes.c_double)]),
         "dspk_cap_init": (c_int32, [P(CapControllerDesc), P(ctypes.c_double), P(ctypes.c_double), c_int32,
@@ -285,6 +299,14 @@ def prepare_accept_sample(logits, q, draft_ids, uniforms, m_rows: int, v: int, t
                     _stream(stream))
 
 
+def prepare_accept_sample_ex(logits, q, draft_ids, uniforms, m_rows: int, v: int, params: SampleParamsDesc,
+                             counts, accept_len, committed, workspace, stream=None) -> Prepared:
+    return Prepared("dspk_accept_sample_ex", logits.data_ptr(), _rows(logits, "logits"), q.data_ptr(),
+                    _rows(q, "q"), draft_ids.data_ptr(), uniforms.data_ptr(), m_rows, v, ctypes.byref(params),
+                    _ptr(counts), accept_len.data_ptr(), committed.data_ptr(), workspace.data_ptr(),
+                    workspace.numel(), _stream(stream))
+
+
 # ------------------------------------------------------------ entry points
 def version() -> int:
     return lib().dspk_version()
@@ -346,3 +368,14 @@ def accept_sample(logits, q, draft_ids, uniforms, m_rows: int, v: int, temperatu
                                     draft_ids.data_ptr(), uniforms.data_ptr(), m_rows, v, float(temperature),
                                     accept_len.data_ptr(), committed.data_ptr(), _ptr(workspace),
                                     0 if workspace is None else workspace.numel(), _stream(stream)))
+
+
+def accept_sample_ex(logits, q, draft_ids, uniforms, m_rows: int, v: int, params: SampleParamsDesc, counts=None,
+                     accept_len=None, committed=None, workspace=None, stream=None) -> None:
+    """Speculative sampling over penalised, top-k/top-p truncated
+    distributions; ``params`` from sample_params(), ``counts`` an int32 [v]
+    device tensor of history counts or None."""
+    _check(lib().dspk_accept_sample_ex(logits.data_ptr(), _rows(logits, "logits"), q.data_ptr(), _rows(q, "q"),
+                                       draft_ids.data_ptr(), uniforms.data_ptr(), m_rows, v, ctypes.byref(params),
+                                       _ptr(counts), accept_len.data_ptr(), committed.data_ptr(), _ptr(workspace),
+                                       0 if workspace is None else workspace.numel(), _stream(stream)))

@@ -32,33 +32,154 @@ __global__ void accept_greedy_kernel(const int32_t *__restrict__ t, const int32_
 
 // -------------------------------------------------------------- sampling
 // Workspace layout (bytes): [0, 256) arrival counter; then per (row, chunk):
-// stats {max of z/T, sum exp(z/T - max)} and the fault flag; then per chunk
-// the masses {residual, p} of the row that supplies the final draw.
+// stats {max of z'/T, sum exp(z'/T - max)}, the fault flag and the max of q;
+// then per chunk the masses {residual, p} of the row that supplies the final
+// draw; then per (row, distribution) the truncation record; then, used only
+// when truncating, per (row, distribution) the first-level histograms of
+// each slice of the row and the first-level bin of every entry.
 constexpr int CH = kSampleChunk;
 constexpr int TPB = 256;
 constexpr int EPT = CH / TPB;    // logits per thread per chunk
-constexpr int kMaxRowsSample = kMaxRows;
+constexpr int FT = 1024;         // threads of a truncation workgroup
+constexpr int NB = 2048;         // histogram bins per level
+constexpr int SLICE = 8192;      // entries per workgroup of the binning pass (<= 2^13)
+constexpr int BT = 512;          // threads of a binning workgroup
+static_assert(SLICE <= 8192, "the binning histogram's 32-bit mass halves hold 2^13 entries");
+
+struct Trunc {
+    unsigned long long key;      // kept iff order key >= key
+    float mass;                  // kept mass (of p, or of q as supplied)
+    int32_t pad;
+};
 
 struct SampleWs {
     uint32_t *counter;
     float2 *stats;   // [rows][nchunks]
     int32_t *flags;  // [rows][nchunks]
+    float *qmax;     // [rows][nchunks] (draft rows)
     float2 *mass;    // [nchunks]
+    Trunc *trunc;    // [rows][2]: target p, draft q
+    uint32_t *pcnt;            // [rows][2][nslices][NB]
+    unsigned long long *pmass; // [rows][2][nslices][NB]
+    uint16_t *bin1;            // [rows][2][vpad]
+    int nslices, vpad;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-__host__ __device__ inline SampleWs carve(void *ws, int rows, int nchunks) {
+struct WsLayout {
+    size_t stats, flags, qmax, mass, trunc, pcnt, pmass, bin1, total;
+    int nslices, vpad;
+};
+
+__host__ __device__ inline WsLayout ws_layout(int rows, int v) {
+    const size_t nchunks = (size_t)(v + CH - 1) / CH;
+    WsLayout L;
+    L.nslices = (v + SLICE - 1) / SLICE;
+    L.vpad = (v + 127) / 128 * 128;
+    const size_t nh = (size_t)rows * 2 * L.nslices * NB;
+    size_t o = 256;
+    L.stats = o;
+    o += align256(rows * nchunks * sizeof(float2));
+    L.flags = o;
+    o += align256(rows * nchunks * sizeof(int32_t));
+    L.qmax = o;
+    o += align256(rows * nchunks * sizeof(float));
+    L.mass = o;
+    o += align256(nchunks * sizeof(float2));
+    L.trunc = o;
+    o += align256((size_t)rows * 2 * sizeof(Trunc));
+    L.pcnt = o;
+    o += align256(nh * sizeof(uint32_t));
+    L.pmass = o;
+    o += align256(nh * sizeof(unsigned long long));
+    L.bin1 = o;
+    o += align256((size_t)rows * 2 * L.vpad * sizeof(uint16_t));
+    L.total = o;
+    return L;
+}
+
+__host__ __device__ inline SampleWs carve(void *ws, int rows, int v) {
+    const WsLayout L = ws_layout(rows, v);
     char *p = (char *)ws;
     SampleWs s;
     s.counter = (uint32_t *)p;
-    p += 256;
-    s.stats = (float2 *)p;
-    p += align256((size_t)rows * nchunks * sizeof(float2));
-    s.flags = (int32_t *)p;
-    p += align256((size_t)rows * nchunks * sizeof(int32_t));
-    s.mass = (float2 *)p;
+    s.stats = (float2 *)(p + L.stats);
+    s.flags = (int32_t *)(p + L.flags);
+    s.qmax = (float *)(p + L.qmax);
+    s.mass = (float2 *)(p + L.mass);
+    s.trunc = (Trunc *)(p + L.trunc);
+    s.pcnt = (uint32_t *)(p + L.pcnt);
+    s.pmass = (unsigned long long *)(p + L.pmass);
+    s.bin1 = (uint16_t *)(p + L.bin1);
+    s.nslices = L.nslices;
+    s.vpad = L.vpad;
     return s;
+}
+
+// Everything the sampling kernels read (kernel argument, by value).
+struct SampleArgs {
+    const float *z;
+    int64_t ldz;
+    const float *q;
+    int64_t ldq;
+    const int32_t *d;
+    const float *u;
+    int32_t rows, v;
+    float inv_t;                 // 1 / temperature
+    int32_t top_k;               // 0: off
+    float top_p;                 // 1: off
+    float presence, frequency;   // penalties
+    const int32_t *counts;       // history token counts [v], or NULL
+    int32_t pen;                 // any penalty applies
+    int32_t trunc;               // top-k or top-p applies
+    int32_t *accept_len, *committed;
+    void *ws;
+};
+
+// Penalised, temperature-scaled logit of column col in row j ("mlx-dspark
+// releases", v0.2.0 notes: OpenAI presence/frequency penalties on the target
+// logits, so that the output equals sequential decoding of the penalised
+// target).  Row j is reached only when drafts 0..j-1 were accepted, so its
+// counts include them; drafts are in LDS (s_d).  bloom (or NULL): a 1024-bit
+// filter of the columns of drafts 0..j-1 -- a clear bit means none of them
+// is col, and the scan over the drafts is skipped.
+// hist: counts[col] (0 without counts), loaded by the caller.
+__device__ inline float scaled_logit_h(const SampleArgs &A, const int32_t *s_d, const uint32_t *bloom, int j,
+                                       int col, float zz, int hist) {
+    if (A.pen) {
+        int c = hist;
+        const uint32_t h = (uint32_t)col & 1023u;
+        if (bloom == nullptr || ((bloom[h >> 5] >> (h & 31u)) & 1u))
+            for (int i = 0; i < j; ++i) c += s_d[i] == col;
+        zz = zz - A.presence * (c > 0 ? 1.f : 0.f) - A.frequency * (float)c;
+    }
+    return zz * A.inv_t;
+}
+
+__device__ inline float scaled_logit(const SampleArgs &A, const int32_t *s_d, const uint32_t *bloom, int j, int col,
+                                     float zz) {
+    return scaled_logit_h(A, s_d, bloom, j, col, zz, A.pen && A.counts != nullptr ? A.counts[col] : 0);
+}
+
+// Fill the filter of drafts 0..j-1 (bloom: 32 words of LDS; s_d already
+// loaded); ends with a barrier.
+__device__ inline void build_bloom(uint32_t *bloom, const int32_t *s_d, int j) {
+    if (threadIdx.x < 32) bloom[threadIdx.x] = 0u;
+    __syncthreads();
+    if ((int)threadIdx.x < j) {
+        const uint32_t h = (uint32_t)s_d[threadIdx.x] & 1023u;
+        atomicOr(&bloom[h >> 5], 1u << (h & 31u));
+    }
+    __syncthreads();
+}
+
+// Order key of an entry: larger value first, then the smaller column; unique.
+// -0 and +0 are one value.
+__device__ inline unsigned long long order_key(float x, int col) {
+    uint32_t b = __float_as_uint(x + 0.0f);
+    b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ((unsigned long long)b << 32) | (unsigned long long)(0xffffffffu - (uint32_t)col);
 }
 
 // Values one workgroup hands to another inside a kernel move through
@@ -75,6 +196,7 @@ __device__ inline float2 load_f2(const float2 *p) {
 }
 
 // block-wide reductions in a fixed order (wave butterfly, then waves in order)
+template <int NT>
 __device__ inline float block_sum(float v, float *scratch) {
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
     const int w = threadIdx.x >> 6;
@@ -82,7 +204,7 @@ __device__ inline float block_sum(float v, float *scratch) {
     if ((threadIdx.x & 63) == 0) scratch[w] = v;
     __syncthreads();
     float r = scratch[0];
-    for (int i = 1; i < TPB / 64; ++i) r += scratch[i];
+    for (int i = 1; i < NT / 64; ++i) r += scratch[i];
     return r;
 }
 
@@ -97,18 +219,32 @@ __device__ inline float block_max(float v, float *scratch) {
     return r;
 }
 
-// Pass 1: per (row, chunk) max and sum of exp of z/T, and the fault flag
-// (non-finite logit; non-finite or negative q on draft rows).
-__global__ __launch_bounds__(TPB) void sample_stats_kernel(const float *__restrict__ z, int64_t ldz,
-                                                           const float *__restrict__ q, int64_t ldq,
-                                                           int32_t rows, int32_t v, float temperature,
-                                                           void *ws) {
+// Row maximum and normaliser of z'/T from the chunk statistics, eight threads
+// per row (k = tid % 8 takes chunks k, k + 8, ...), then a fixed butterfly.
+__device__ inline float2 row_stats8(const float2 *st, int nchunks, int k) {
+    float mx = -INFINITY;
+    for (int cc = k; cc < nchunks; cc += 8) mx = fmaxf(mx, st[cc].x);
+    for (int off = 1; off < 8; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    float sm = 0.f;
+    for (int cc = k; cc < nchunks; cc += 8) sm += st[cc].y * expf(st[cc].x - mx);
+    for (int off = 1; off < 8; off <<= 1) sm += __shfl_xor(sm, off);
+    return make_float2(mx, sm);
+}
+
+// Pass 1: per (row, chunk) max and sum of exp of z'/T, and the fault flag
+// (non-finite logit; non-finite or negative q on draft rows; negative count).
+__global__ __launch_bounds__(TPB) void sample_stats_kernel(const SampleArgs A) {
     __shared__ float scratch[TPB / 64];
-    const int nchunks = (v + CH - 1) / CH;
-    const SampleWs W = carve(ws, rows, nchunks);
+    __shared__ int32_t s_d[kMaxRows];
+    __shared__ uint32_t s_bloom[32];
+    const int nchunks = (A.v + CH - 1) / CH;
+    const SampleWs W = carve(A.ws, A.rows, A.v);
     const int c = blockIdx.x, j = blockIdx.y, tid = threadIdx.x;
-    const int v0 = c * CH, v1 = min(v, v0 + CH);
-    const float *zr = z + (int64_t)j * ldz;
+    const int v0 = c * CH, v1 = min(A.v, v0 + CH);
+    if (tid < A.rows - 1) s_d[tid] = A.d[tid];
+    __syncthreads();
+    build_bloom(s_bloom, s_d, j);
+    const float *zr = A.z + (int64_t)j * A.ldz;
     float a[EPT];
     float mx = -INFINITY;
     int bad = 0;
@@ -119,32 +255,741 @@ __global__ __launch_bounds__(TPB) void sample_stats_kernel(const float *__restri
         if (col < v1) {
             const float zz = zr[col];
             bad |= !isfinite(zz);
-            a[i] = zz / temperature;
+            if (A.counts != nullptr) bad |= A.counts[col] < 0;
+            a[i] = scaled_logit(A, s_d, s_bloom, j, col, zz);
             mx = fmaxf(mx, a[i]);
         }
     }
-    if (j < rows - 1) {
-        const float *qr = q + (int64_t)j * ldq;
+    float qm = 0.f;
+    if (j < A.rows - 1) {
+        const float *qr = A.q + (int64_t)j * A.ldq;
 #pragma unroll
         for (int i = 0; i < EPT; ++i) {
             const int col = v0 + tid + TPB * i;
             if (col < v1) {
                 const float qq = qr[col];
                 bad |= !(isfinite(qq) && qq >= 0.f);
+                qm = fmaxf(qm, qq);
             }
         }
     }
     bad = __syncthreads_or(bad);
+    if (A.trunc) {
+        qm = block_max(qm, scratch);
+        if (tid == 0) W.qmax[j * nchunks + c] = qm;
+    }
     const float cmax = block_max(mx, scratch);
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < EPT; ++i)
         if (v0 + tid + TPB * i < v1) s += expf(a[i] - cmax);
-    const float csum = block_sum(s, scratch);
+    const float csum = block_sum<TPB>(s, scratch);
     if (tid == 0) {
         W.stats[j * nchunks + c] = make_float2(cmax, csum);
         W.flags[j * nchunks + c] = bad;
     }
+}
+
+// Truncation of one distribution ("mlx-dspark releases", v0.1.0 notes:
+// nucleus / top-k truncation of both the draft and the target).  Entries are
+// ordered by value (larger first, then the smaller column): their order keys
+// are unique 64-bit values, so each bound is one key.  Top-k keeps the first
+// k; top-p then keeps an entry iff the kept mass before it is below top_p
+// times the top-k mass.  Masses are counted in fixed point -- unit = the
+// row's largest weight / 2^37 (fewer bits for v > 2^25, so that v weights fit
+// 64 bits) -- as integers, so sums do not depend on thread timing; every
+// weight is off by less than one unit (rounded down, but a positive weight
+// counts at least one) and the kept mass is at least the largest weight, so a
+// bound is off by at most v * 2^-37 of the kept mass.  A top-k bound that
+// falls among entries of weight exactly zero keeps all of them instead: they
+// carry no mass, so the truncated distribution is the same.
+//
+// Every entry has a fine index fi (22 bits) that never decreases along the
+// key order, from float bits, so that any spread of values splits evenly in
+// log scale: for p, the bits of t = max(z'/T) - z'/T, clamped to
+// [2^-24, 2^40), in steps of 128 ulps (32 first-level bins per octave); for
+// q, bits of max(q) - bits of q in steps of 512 ulps (8 per octave, the whole
+// float range down to 0).
+//
+// Two kernels.  sample_bins_kernel (one workgroup per slice of SLICE entries
+// of a (row, distribution), the whole GPU) evaluates every entry once, stores
+// its first-level bin fi >> 11 and the slice's histogram (count and mass per
+// bin).  sample_trunc_kernel (one workgroup per (row, distribution)) adds the
+// slice histograms, finds the bin holding a bound with a wave-parallel scan,
+// and, when it holds at most CAP entries, gathers them (found through the
+// stored bins) into LDS, sorts them by key (bitonic) and takes the first at
+// which the running count (top-k) or mass (top-p) reaches its target.  A bin
+// of more entries is split by a second histogram over fi & 2047, and a
+// second-level bin still too full (equal values) falls back to a 64-bit radix
+// selection over the keys (11-bit digits).
+constexpr int CAP = 4096;                      // entries sorted in LDS
+constexpr uint32_t FI_MAX = (1u << 22) - 1;
+constexpr uint32_t kTLo = 103u << 23;          // float bits of 2^-24
+constexpr uint32_t kTHi = (167u << 23) - 1u;   // just below 2^40
+
+// What an entry's evaluation needs of its row.
+struct RowCtx {
+    float rmax;                  // p: max of z'/T
+    float wmax, inv_wmax;        // the row's largest weight (p: 1 / sum exp(z'/T - rmax))
+    uint32_t wbits;              // its bits
+    int fx;                      // fixed point: weight / wmax in units of 2^-fx (fx <= 37)
+};
+
+// Row context of (row j, distribution dist); all threads call it (barriers).
+__device__ inline RowCtx row_ctx(const SampleArgs &A, const SampleWs &W, int j, int dist, float2 *s_rs) {
+    const int nchunks = (A.v + CH - 1) / CH;
+    const int tid = threadIdx.x;
+    if (dist == 0) {
+        if (tid < 8) {
+            const float2 rs = row_stats8(W.stats + (int64_t)j * nchunks, nchunks, tid);
+            if (tid == 0) *s_rs = rs;
+        }
+    } else if (tid < 64) {
+        float mx = 0.f;
+        for (int cc = tid; cc < nchunks; cc += 64) mx = fmaxf(mx, W.qmax[j * nchunks + cc]);
+        for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+        if (tid == 0) *s_rs = make_float2(mx, 0.f);
+    }
+    __syncthreads();
+    RowCtx r;
+    const float2 rs = *s_rs;
+    r.rmax = rs.x;
+    // largest weight: 1 / sum for p (its largest entry has x = rmax)
+    r.wmax = dist == 0 ? 1.f / rs.y : rs.x;
+    r.inv_wmax = r.wmax > 0.f ? 1.f / r.wmax : 0.f;
+    r.wbits = __float_as_uint(r.wmax) & 0x7fffffffu;
+    int lg = 0;
+    while ((1 << lg) < A.v) ++lg;
+    r.fx = min(37, 62 - lg);
+    return r;
+}
+
+// Key, fine index and fixed-point weight of column col.
+// raw: z[j][col] (p) or q[j][col]; hist: counts[col] (p with penalties and
+// counts; else unused).
+__device__ inline void trunc_entry_raw(const SampleArgs &A, const RowCtx &R, int dist, int j, int col, float raw,
+                                       int hist, const int32_t *s_d, const uint32_t *bloom,
+                                       unsigned long long &key, uint32_t &fi, unsigned long long &mfx) {
+    float x, y;     // y: weight / wmax, in [0, 1]
+    if (dist == 0) {
+        x = scaled_logit_h(A, s_d, bloom, j, col, raw, hist);
+        y = expf(x - R.rmax);
+        const uint32_t tb = __float_as_uint(R.rmax - x);
+        fi = tb >= 0x80000000u ? 0u : (min(max(tb, kTLo), kTHi) - kTLo) >> 7;
+    } else {
+        x = raw;
+        y = fminf(x * R.inv_wmax, 1.f);
+        const uint32_t b = __float_as_uint(x) & 0x7fffffffu;
+        fi = b >= R.wbits ? 0u : (R.wbits - b) >> 9;
+    }
+    fi = min(fi, FI_MAX);
+    key = order_key(x, col);
+    // floor(y * 2^fx) from the float's fields (exact: y * 2^fx <= 2^37); a
+    // positive weight counts at least one unit, so a bin's mass is zero only
+    // when all its weights are
+    const uint32_t yb = __float_as_uint(y);
+    const int e = (int)((yb >> 23) & 0xffu) - 127 + R.fx;      // exponent of y * 2^fx
+    const unsigned long long mant = (unsigned long long)((yb & 0x7fffffu) | 0x800000u);
+    const unsigned long long u = e < 0 ? 0ull : (e >= 23 ? mant << (e - 23) : mant >> (23 - e));
+    mfx = (y > 0.f && u == 0ull) ? 1ull : (y > 0.f ? u : 0ull);
+}
+
+__device__ inline void trunc_entry(const SampleArgs &A, const RowCtx &R, int dist, int j, int col,
+                                   const int32_t *s_d, const uint32_t *bloom, unsigned long long &key,
+                                   uint32_t &fi, unsigned long long &mfx) {
+    const float raw = dist == 0 ? A.z[(int64_t)j * A.ldz + col] : A.q[(int64_t)j * A.ldq + col];
+    const int hist = dist == 0 && A.pen && A.counts != nullptr ? A.counts[col] : 0;
+    trunc_entry_raw(A, R, dist, j, col, raw, hist, s_d, bloom, key, fi, mfx);
+}
+
+// Add (1, mfx) to bin b of (cnt, mass) for the lanes with take set.  When
+// every taking lane of the wave has the same bin (crowded bins: equal or
+// nearly equal values, runs of columns), one lane adds the wave's sums: LDS
+// atomics to one address from many lanes would be serialised.  The whole
+// wave calls it.
+__device__ inline void hist_add(uint32_t *cnt, unsigned long long *mass, bool take, int b, unsigned long long mfx) {
+    const unsigned long long act = __ballot(take);
+    if (act == 0ull) return;
+    const int lane = threadIdx.x & 63;
+    const int lead = __ffsll((long long)act) - 1;
+    const int b0 = __builtin_amdgcn_readlane(b, lead);
+    const unsigned long long same = __ballot(take && b == b0);
+    if (same == act) {
+        unsigned long long ms = take ? mfx : 0ull;
+        for (int off = 32; off > 0; off >>= 1) ms += __shfl_xor(ms, off);
+        if (lane == lead) {
+            atomicAdd(&cnt[b0], (uint32_t)__popcll(act));
+            atomicAdd(&mass[b0], ms);
+        }
+    } else if (take) {
+        atomicAdd(&cnt[b], 1u);
+        atomicAdd(&mass[b], mfx);
+    }
+}
+
+// hist_add with the mass in two halves (low 19 bits, the rest) on 32-bit
+// counters (64-bit LDS atomics are much slower): with mfx <= 2^37 and at most
+// SLICE = 2^13 entries per histogram, neither half's sum reaches 2^32.
+__device__ inline void hist_add_split(uint32_t *cnt, uint32_t *lo, uint32_t *hi, bool take, int b,
+                                      unsigned long long mfx) {
+    const unsigned long long act = __ballot(take);
+    if (act == 0ull) return;
+    const int lane = threadIdx.x & 63;
+    const int lead = __ffsll((long long)act) - 1;
+    const int b0 = __builtin_amdgcn_readlane(b, lead);
+    const unsigned long long same = __ballot(take && b == b0);
+    uint32_t l = take ? (uint32_t)(mfx & 0x7ffffu) : 0u, h = take ? (uint32_t)(mfx >> 19) : 0u;
+    if (same == act) {
+        for (int off = 32; off > 0; off >>= 1) {
+            l += __shfl_xor(l, off);
+            h += __shfl_xor(h, off);
+        }
+        if (lane == lead) {
+            atomicAdd(&cnt[b0], (uint32_t)__popcll(act));
+            atomicAdd(&lo[b0], l);
+            atomicAdd(&hi[b0], h);
+        }
+    } else if (take) {
+        atomicAdd(&cnt[b], 1u);
+        if (l != 0u) atomicAdd(&lo[b], l);
+        if (h != 0u) atomicAdd(&hi[b], h);
+    }
+}
+
+__device__ inline unsigned long long wave_incl_scan(unsigned long long x, int lane) {
+    for (int off = 1; off < 64; off <<= 1) {
+        const unsigned long long y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+// Binning pass: grid (nslices, rows, 2).
+__global__ __launch_bounds__(BT) void sample_bins_kernel(const SampleArgs A) {
+    __shared__ uint32_t h_cnt[NB];
+    __shared__ uint32_t h_lo[NB], h_hi[NB];   // mass = hi * 2^19 + lo
+    __shared__ int32_t s_d[kMaxRows];
+    __shared__ uint32_t s_bloom[32];
+    __shared__ float2 s_rs;
+    const int sl = blockIdx.x, j = blockIdx.y, dist = blockIdx.z, tid = threadIdx.x;
+    if (dist == 1 && j >= A.rows - 1) return;
+    const SampleWs W = carve(A.ws, A.rows, A.v);
+    if (tid < A.rows - 1) s_d[tid] = A.d[tid];
+    for (int b = tid; b < NB; b += BT) {
+        h_cnt[b] = 0u;
+        h_lo[b] = 0u;
+        h_hi[b] = 0u;
+    }
+    __syncthreads();
+    build_bloom(s_bloom, s_d, dist == 0 ? j : 0);
+    const RowCtx R = row_ctx(A, W, j, dist, &s_rs);
+    uint16_t *bins = W.bin1 + (size_t)(j * 2 + dist) * W.vpad;
+    const int c_beg = sl * SLICE, c_end = min(A.v, c_beg + SLICE);
+    // the slice's values (and counts) first, all loads in flight
+    constexpr int PER = SLICE / BT;
+    const float *src = dist == 0 ? A.z + (int64_t)j * A.ldz : A.q + (int64_t)j * A.ldq;
+    const bool with_hist = dist == 0 && A.pen && A.counts != nullptr;
+    float raw[PER];
+    int hist[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int col = c_beg + BT * i + tid;
+        raw[i] = col < c_end ? src[col] : 0.f;
+        hist[i] = with_hist && col < c_end ? A.counts[col] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int col = c_beg + BT * i + tid;
+        unsigned long long key = 0, mfx = 0;
+        uint32_t fi = 0;
+        const bool take = col < c_end;
+        if (take) {
+            trunc_entry_raw(A, R, dist, j, col, raw[i], hist[i], s_d, s_bloom, key, fi, mfx);
+            bins[col] = (uint16_t)(fi >> 11);
+        }
+        hist_add_split(h_cnt, h_lo, h_hi, take, (int)(fi >> 11), mfx);
+    }
+    __syncthreads();
+    const size_t slot = ((size_t)(j * 2 + dist) * W.nslices + sl) * NB;
+    for (int b = tid; b < NB; b += BT) {
+        W.pcnt[slot + b] = h_cnt[b];
+        W.pmass[slot + b] = ((unsigned long long)h_hi[b] << 19) + h_lo[b];
+    }
+}
+
+// Running sums at a bound: the count and fixed-point mass of the entries
+// whose keys are >= the bound's key (among those with key >= lo).
+struct Found {
+    unsigned long long key, cnt, mass;
+    int ok;
+};
+
+// Selection: grid (rows, 2).
+__global__ __launch_bounds__(FT) void sample_trunc_kernel(const SampleArgs A) {
+    __shared__ uint32_t h_cnt[NB];
+    __shared__ unsigned long long h_mass[NB];
+    __shared__ unsigned long long c_key[CAP];
+    __shared__ unsigned long long c_mass[CAP];
+    __shared__ unsigned long long s_wsum[FT / 64][2];
+    __shared__ int32_t s_d[kMaxRows];
+    __shared__ uint32_t s_bloom[32];
+    __shared__ float2 s_rs;
+    __shared__ int s_bin, s_n, s_idx;
+    __shared__ unsigned long long s_acnt, s_amass;
+    __shared__ Found s_found;
+    const int j = blockIdx.x, dist = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    if (dist == 1 && j >= A.rows - 1) return;
+    const SampleWs W = carve(A.ws, A.rows, A.v);
+    if (tid < A.rows - 1) s_d[tid] = A.d[tid];
+    __syncthreads();
+    build_bloom(s_bloom, s_d, dist == 0 ? j : 0);
+    const RowCtx R = row_ctx(A, W, j, dist, &s_rs);
+    const uint16_t *bins = W.bin1 + (size_t)(j * 2 + dist) * W.vpad;
+    const size_t slot0 = (size_t)(j * 2 + dist) * W.nslices * NB;
+
+    auto entry = [&](int col, unsigned long long &key, uint32_t &fi, unsigned long long &mfx)
+        __attribute__((always_inline)) { trunc_entry(A, R, dist, j, col, s_d, s_bloom, key, fi, mfx); };
+
+    // Calls visit(match, col) until every entry of first-level bin b1 has
+    // been visited once with match set (col < v); the calls are
+    // wave-uniform, so visit may use wave-wide operations.  The stored bins
+    // are read 16 bytes (8 entries) at a time, 4 loads in flight per thread;
+    // each thread then visits the matches of its 32 entries, lowest first.
+    auto scan_bin = [&](int b1, auto &&visit) __attribute__((always_inline)) {
+        const uint4 *bv = reinterpret_cast<const uint4 *>(bins);
+        const int ng = (A.v + 7) >> 3;
+        constexpr int K = 4;
+        for (int g0 = 0; g0 < ng; g0 += FT * K) {
+            uint4 vv[K];
+#pragma unroll
+            for (int i = 0; i < K; ++i) {
+                const int gi = g0 + FT * i + tid;
+                vv[i] = gi < ng ? bv[gi] : make_uint4(~0u, ~0u, ~0u, ~0u);
+            }
+            uint32_t mask = 0;
+#pragma unroll
+            for (int i = 0; i < K; ++i) {
+                const uint32_t w4[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int col = (g0 + FT * i + tid) * 8 + e;
+                    const uint32_t bb = (w4[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+                    if (col < A.v && bb == (uint32_t)b1) mask |= 1u << (i * 8 + e);
+                }
+            }
+            for (;;) {
+                const bool has = mask != 0u;
+                if (__ballot(has) == 0ull) break;
+                int col = 0;
+                if (has) {
+                    const int e = __ffs(mask) - 1;
+                    mask &= mask - 1u;
+                    col = (g0 + FT * (e >> 3) + tid) * 8 + (e & 7);
+                }
+                visit(has, col);
+            }
+        }
+    };
+
+    // (the barrier first: every thread has read what it needs of the bins)
+    auto clear_hist = [&]() __attribute__((always_inline)) {
+        __syncthreads();
+        for (int b = tid; b < NB; b += FT) {
+            h_cnt[b] = 0u;
+            h_mass[b] = 0ull;
+        }
+        __syncthreads();
+    };
+
+    // first-level histogram of the whole row: the sum of the slices'
+    auto load_level1 = [&]() __attribute__((always_inline)) {
+        __syncthreads();
+        for (int b = tid; b < NB; b += FT) {
+            unsigned long long c = 0, m = 0;
+            for (int sl0 = 0; sl0 < W.nslices; sl0 += 8) {   // 8 slices' loads in flight
+                uint32_t cc[8];
+                unsigned long long mm[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const size_t at = slot0 + (size_t)(sl0 + i) * NB + b;
+                    cc[i] = sl0 + i < W.nslices ? W.pcnt[at] : 0u;
+                    mm[i] = sl0 + i < W.nslices ? W.pmass[at] : 0ull;
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    c += cc[i];
+                    m += mm[i];
+                }
+            }
+            h_cnt[b] = (uint32_t)c;
+            h_mass[b] = m;
+        }
+        __syncthreads();
+    };
+
+    // Wave 0: the first bin, in the order 'ascending' (bin 0 first) or
+    // descending, at which base + running weight (count or mass) reaches
+    // target; s_bin = -1 if none.  s_acnt / s_amass: count and mass before
+    // it.  All threads call it (barriers on both sides).
+    auto find_bin = [&](bool ascending, bool by_mass, unsigned long long target, unsigned long long base_cnt,
+                        unsigned long long base_mass) __attribute__((always_inline)) {
+        __syncthreads();
+        if (wv == 0) {
+            constexpr int PER = NB / 64;
+            unsigned long long lc = 0, lm = 0;
+#pragma unroll 4
+            for (int i = 0; i < PER; ++i) {
+                const int pos = lane * PER + i;
+                const int b = ascending ? pos : NB - 1 - pos;
+                lc += h_cnt[b];
+                lm += h_mass[b];
+            }
+            const unsigned long long ic = wave_incl_scan(lc, lane), im = wave_incl_scan(lm, lane);
+            const unsigned long long reach = by_mass ? base_mass + im : base_cnt + ic;
+            const unsigned long long mask = __ballot(reach >= target);
+            if (lane == 0) s_bin = -1;
+            if (mask != 0ull && lane == __ffsll((long long)mask) - 1) {
+                unsigned long long c = base_cnt + ic - lc, mm = base_mass + im - lm;
+                int bin = -1;
+#pragma unroll 1
+                for (int i = 0; i < PER; ++i) {
+                    const int pos = lane * PER + i;
+                    const int b = ascending ? pos : NB - 1 - pos;
+                    const unsigned long long nc = c + h_cnt[b], nm = mm + h_mass[b];
+                    if ((by_mass ? nm : nc) >= target) {
+                        bin = b;
+                        break;
+                    }
+                    c = nc;
+                    mm = nm;
+                }
+                s_bin = bin;
+                s_acnt = c;
+                s_amass = mm;
+            }
+        }
+        __syncthreads();
+    };
+
+    // Gather the entries of first-level bin b1 with key >= lo and fi in
+    // [f0, f1] into LDS (at most CAP of them), sort them by key
+    // (descending), and find the first at which base + running weight
+    // reaches target; result in s_found.
+    auto gather_sort_find = [&](int b1, unsigned long long lo, uint32_t f0, uint32_t f1, bool by_mass,
+                                unsigned long long target, unsigned long long base_cnt,
+                                unsigned long long base_mass) __attribute__((always_inline)) {
+        if (tid == 0) s_n = 0;
+        __syncthreads();
+        scan_bin(b1, [&](bool match, int col) __attribute__((always_inline)) {
+            bool take = false;
+            unsigned long long key = 0, mfx = 0;
+            if (match) {
+                uint32_t fi;
+                entry(col, key, fi, mfx);
+                take = key >= lo && fi >= f0 && fi <= f1;
+            }
+            const unsigned long long bal = __ballot(take);
+            if (bal != 0ull) {
+                const int lead = __ffsll((long long)bal) - 1;
+                int basei = 0;
+                if (lane == lead) basei = atomicAdd(&s_n, (int)__popcll(bal));
+                basei = __shfl(basei, lead);
+                const int slot = basei + (int)__popcll(bal & ((1ull << lane) - 1ull));
+                if (take && slot < CAP) {
+                    c_key[slot] = key;
+                    c_mass[slot] = mfx;
+                }
+            }
+        });
+        __syncthreads();
+        const int n = min(s_n, CAP);
+        int np = 1;
+        while (np < n) np <<= 1;
+        for (int i = n + tid; i < np; i += FT) {
+            c_key[i] = 0ull;      // below every real key
+            c_mass[i] = 0ull;
+        }
+        __syncthreads();
+        // bitonic sort, descending
+        for (int k = 2; k <= np; k <<= 1) {
+            for (int jj = k >> 1; jj > 0; jj >>= 1) {
+                for (int i = tid; i < np; i += FT) {
+                    const int ixj = i ^ jj;
+                    if (ixj > i) {
+                        const unsigned long long a = c_key[i], b = c_key[ixj];
+                        const bool desc = (i & k) == 0;
+                        if (desc ? (a < b) : (a > b)) {
+                            c_key[i] = b;
+                            c_key[ixj] = a;
+                            const unsigned long long t = c_mass[i];
+                            c_mass[i] = c_mass[ixj];
+                            c_mass[ixj] = t;
+                        }
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        // running weight: thread t owns entries [t*PT, t*PT + PT)
+        constexpr int PT = CAP / FT;
+        unsigned long long lc = 0, lm = 0;
+        for (int i = 0; i < PT; ++i) {
+            const int e = tid * PT + i;
+            if (e < n) {
+                lc += 1;
+                lm += c_mass[e];
+            }
+        }
+        const unsigned long long ic = wave_incl_scan(lc, lane), im = wave_incl_scan(lm, lane);
+        if (lane == 63) {
+            s_wsum[wv][0] = ic;
+            s_wsum[wv][1] = im;
+        }
+        if (tid == 0) s_idx = 0x7fffffff;
+        __syncthreads();
+        unsigned long long pc = base_cnt + ic - lc, pm = base_mass + im - lm;
+        for (int w = 0; w < wv; ++w) {
+            pc += s_wsum[w][0];
+            pm += s_wsum[w][1];
+        }
+        int hit = 0x7fffffff;
+        for (int i = 0; i < PT; ++i) {
+            const int e = tid * PT + i;
+            if (e < n) {
+                pc += 1;
+                pm += c_mass[e];
+                if ((by_mass ? pm : pc) >= target) {
+                    hit = e;
+                    break;
+                }
+            }
+        }
+        if (hit != 0x7fffffff) atomicMin(&s_idx, hit);
+        __syncthreads();
+        if (hit != 0x7fffffff && hit == s_idx) {
+            s_found.key = c_key[hit];
+            s_found.cnt = pc;
+            s_found.mass = pm;
+            s_found.ok = 1;
+        }
+        __syncthreads();
+    };
+
+    // Exact radix selection over keys (rare path: more than CAP entries with
+    // one fine index f in bin b1): the largest key K with key >= lo, fi == f
+    // and base + weight(keys >= K) >= target; then its running sums.
+    auto radix_find = [&](int b1, unsigned long long lo, uint32_t f, bool by_mass, unsigned long long target,
+                          unsigned long long base_cnt, unsigned long long base_mass) __attribute__((always_inline)) {
+        unsigned long long prefix = 0, acnt = base_cnt, amass = base_mass;
+        for (int pass = 0; pass < 6; ++pass) {
+            const int shift = pass < 5 ? 53 - 11 * pass : 0;
+            const int width = pass < 5 ? 11 : 9;
+            const int top = shift + width;
+            clear_hist();
+            scan_bin(b1, [&](bool match, int col) __attribute__((always_inline)) {
+                unsigned long long key = 0, mfx = 0;
+                bool take = false;
+                if (match) {
+                    uint32_t fi;
+                    entry(col, key, fi, mfx);
+                    take = key >= lo && fi == f && (top >= 64 || (key >> top) == (prefix >> top));
+                }
+                hist_add(h_cnt, h_mass, take, (int)((key >> shift) & ((1u << width) - 1u)), mfx);
+            });
+            find_bin(false, by_mass, target, acnt, amass);
+            if (s_bin < 0) return;      // s_found.ok stays 0
+            prefix |= (unsigned long long)s_bin << shift;
+            acnt = s_acnt;
+            amass = s_amass;
+        }
+        // acnt / amass count the keys above 'prefix'; add the entry itself
+        // (one entry has this key)
+        scan_bin(b1, [&](bool match, int col) __attribute__((always_inline)) {
+            if (match) {
+                unsigned long long key, mfx;
+                uint32_t fi;
+                entry(col, key, fi, mfx);
+                if (key == prefix) {
+                    s_found.key = prefix;
+                    s_found.cnt = acnt + 1;
+                    s_found.mass = amass + mfx;
+                    s_found.ok = 1;
+                }
+            }
+        });
+        __syncthreads();
+    };
+
+    // The first entry (key >= lo) at which the running count (by_mass =
+    // false) or mass reaches target, given the first-level histogram of the
+    // entries with key >= lo in h_cnt / h_mass.  Result in s_found (ok = 0:
+    // not reached, 2: see below); the first-level bin and the sums before it in
+    // l1_bin / l1_acnt / l1_amass.
+    int l1_bin = -1;
+    unsigned long long l1_acnt = 0, l1_amass = 0;
+    auto find_bound = [&](unsigned long long lo, bool by_mass, unsigned long long target)
+        __attribute__((always_inline)) {
+        if (tid == 0) s_found.ok = 0;
+        find_bin(true, by_mass, target, 0ull, 0ull);
+        const int b1 = s_bin;
+        l1_bin = b1;
+        if (b1 < 0) return;
+        unsigned long long acnt = s_acnt, amass = s_amass;
+        l1_acnt = acnt;
+        l1_amass = amass;
+        if (!by_mass && h_mass[b1] == 0ull) {
+            // weight-zero bin: every later entry weighs zero too (weights do
+            // not increase along the key order), so the first k hold every
+            // positive weight: ok = 2
+            __syncthreads();
+            if (tid == 0) s_found.ok = 2;
+            __syncthreads();
+            return;
+        }
+        if (h_cnt[b1] <= (uint32_t)CAP) {
+            gather_sort_find(b1, lo, (uint32_t)b1 << 11, ((uint32_t)b1 << 11) | 2047u, by_mass, target, acnt, amass);
+            return;
+        }
+        clear_hist();
+        scan_bin(b1, [&](bool match, int col) __attribute__((always_inline)) {
+            unsigned long long key = 0, mfx = 0;
+            uint32_t fi = 0;
+            bool take = false;
+            if (match) {
+                entry(col, key, fi, mfx);
+                take = key >= lo;
+            }
+            hist_add(h_cnt, h_mass, take, (int)(fi & 2047u), mfx);
+        });
+        find_bin(true, by_mass, target, acnt, amass);
+        const int b2 = s_bin;
+        if (b2 < 0) return;
+        acnt = s_acnt;
+        amass = s_amass;
+        const uint32_t f = ((uint32_t)b1 << 11) | (uint32_t)b2;
+        if (!by_mass && h_mass[b2] == 0ull) {
+            __syncthreads();
+            if (tid == 0) s_found.ok = 2;
+            __syncthreads();
+            return;
+        }
+        if (h_cnt[b2] <= (uint32_t)CAP) {
+            gather_sort_find(b1, lo, f, f, by_mass, target, acnt, amass);
+            return;
+        }
+        radix_find(b1, lo, f, by_mass, target, acnt, amass);
+    };
+
+    load_level1();
+    unsigned long long lo = 0, kmass = 0;
+    const bool topk = A.top_k > 0 && A.top_k < A.v;
+    bool have_k = false;
+    int bk = -1;
+    unsigned long long bk_acnt = 0, bk_amass = 0;
+    if (topk) {
+        // ok = 2: the first k entries hold every positive weight, which is
+        // the same truncation as none
+        find_bound(0ull, false, (unsigned long long)A.top_k);
+        if (s_found.ok == 1) {
+            lo = s_found.key;
+            kmass = s_found.mass;
+            have_k = true;
+            bk = l1_bin;
+            bk_acnt = l1_acnt;
+            bk_amass = l1_amass;
+        }
+    }
+    if (!have_k) {
+        // total mass: the first-level bins' sums, in bin order (reloaded:
+        // the top-k search may have left a finer histogram)
+        if (topk) load_level1();
+        __syncthreads();
+        if (wv == 0) {
+            unsigned long long m = 0;
+            for (int b = lane; b < NB; b += 64) m += h_mass[b];
+            m = wave_incl_scan(m, lane);
+            if (lane == 63) s_wsum[0][1] = m;
+        }
+        __syncthreads();
+        kmass = s_wsum[0][1];
+    }
+    unsigned long long bound = lo, kept = kmass;
+    if (A.top_p < 1.f) {
+        const unsigned long long target = (unsigned long long)ceil((double)A.top_p * (double)kmass);
+        if (target == 0) {
+            bound = ~0ull;            // a row without weight keeps nothing
+            kept = 0;
+        } else {
+            if (have_k) {
+                // first-level histogram of the top-k entries: the bins before
+                // bk whole, bk's part above the bound, nothing after
+                load_level1();
+                for (int b = tid; b < NB; b += FT) {
+                    if (b > bk) {
+                        h_cnt[b] = 0u;
+                        h_mass[b] = 0ull;
+                    } else if (b == bk) {
+                        h_cnt[b] = (uint32_t)((unsigned long long)A.top_k - bk_acnt);
+                        h_mass[b] = kmass - bk_amass;
+                    }
+                }
+                __syncthreads();
+            }
+            find_bound(lo, true, target);
+            if (s_found.ok == 1) {
+                bound = s_found.key;
+                kept = s_found.mass;
+            }
+        }
+    }
+    if (tid == 0) {
+        Trunc t;
+        t.key = bound;
+        t.mass = (float)ldexp((double)kept * (double)R.wmax, -R.fx);
+        t.pad = 0;
+        W.trunc[j * 2 + dist] = t;
+    }
+}
+
+// Probability of column col in the (truncated) target row j and draft row j.
+struct RowView {
+    float rmax, rsum;
+    unsigned long long kp, kq;   // truncation bounds (0: keep all)
+    float mp, mq;                // kept masses (p: 1 untruncated; q: 1 means "as supplied")
+};
+
+__device__ inline float p_of(const SampleArgs &A, const int32_t *s_d, const uint32_t *bloom, const RowView &r, int j,
+                            int col, float zz) {
+    const float x = scaled_logit(A, s_d, bloom, j, col, zz);
+    const float p = expf(x - r.rmax) / r.rsum;
+    if (!A.trunc) return p;
+    return (order_key(x, col) >= r.kp && r.mp > 0.f) ? p / r.mp : 0.f;
+}
+
+__device__ inline float q_of(const SampleArgs &A, const RowView &r, int col, float qq) {
+    if (!A.trunc) return qq;
+    return (order_key(qq, col) >= r.kq && r.mq > 0.f) ? qq / r.mq : 0.f;
+}
+
+__device__ inline RowView row_view(const SampleArgs &A, const SampleWs &W, float2 rs, int j) {
+    RowView r;
+    r.rmax = rs.x;
+    r.rsum = rs.y;
+    r.kp = 0;
+    r.kq = 0;
+    r.mp = 1.f;
+    r.mq = 1.f;
+    if (A.trunc) {
+        const Trunc tp = W.trunc[j * 2];
+        r.kp = tp.key;
+        r.mp = tp.mass;
+        if (j < A.rows - 1) {
+            const Trunc tq = W.trunc[j * 2 + 1];
+            r.kq = tq.key;
+            r.mq = tq.mass;
+        }
+    }
+    return r;
 }
 
 // Pass 2, one workgroup per chunk.  Every workgroup repeats the (cheap,
@@ -152,72 +997,68 @@ __global__ __launch_bounds__(TPB) void sample_stats_kernel(const float *__restri
 // agree on the row jr that supplies the final draw -- and adds up, over its
 // chunk of row jr only, the mass of the residual max(0, p - q) and of p; the
 // last workgroup to finish draws the token.
-__global__ __launch_bounds__(TPB) void sample_decide_kernel(
-    const float *__restrict__ z, int64_t ldz, const float *__restrict__ q, int64_t ldq,
-    const int32_t *__restrict__ d, const float *__restrict__ u, int32_t rows, int32_t v,
-    float temperature, int32_t *__restrict__ accept_len, int32_t *__restrict__ committed, void *ws) {
+__global__ __launch_bounds__(TPB) void sample_decide_kernel(const SampleArgs A) {
     __shared__ float scratch[TPB / 64];
-    __shared__ float2 s_rows[kMaxRowsSample];
+    __shared__ float2 s_rows[kMaxRows];
+    __shared__ int32_t s_d[kMaxRows];
+    __shared__ uint32_t s_bloom[32];
     __shared__ float s_pref[TPB];
     __shared__ int s_flag[2];
     __shared__ int s_jr, s_lastc;
     __shared__ unsigned long long s_cut;
+    const int rows = A.rows, v = A.v;
     const int nchunks = (v + CH - 1) / CH;
-    const SampleWs W = carve(ws, rows, nchunks);
+    const SampleWs W = carve(A.ws, rows, v);
     const int c = blockIdx.x, tid = threadIdx.x;
 
-    // row maxima and normalisers from the chunk statistics: eight threads per
-    // row, chunks k, k + 8, ... each, then a fixed butterfly over the eight
     {
-        const int j = tid >> 3, k = tid & 7;
-        const float2 *st = W.stats + (int64_t)min(j, rows - 1) * nchunks;
-        float mx = -INFINITY;
-        for (int cc = k; cc < nchunks; cc += 8) mx = fmaxf(mx, st[cc].x);
-        for (int off = 1; off < 8; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-        float sm = 0.f;
-        for (int cc = k; cc < nchunks; cc += 8) sm += st[cc].y * expf(st[cc].x - mx);
-        for (int off = 1; off < 8; off <<= 1) sm += __shfl_xor(sm, off);
-        if (k == 0 && j < rows) s_rows[j] = make_float2(mx, sm);
+        const int jj = tid >> 3, k = tid & 7;
+        const float2 rs = row_stats8(W.stats + (int64_t)min(jj, rows - 1) * nchunks, nchunks, k);
+        if (k == 0 && jj < rows) s_rows[jj] = rs;
     }
     // draft ids and uniforms in range (they index memory below)
     int bad = 0;
     if (tid < rows) {
-        const float uu = u[tid];
+        const float uu = A.u[tid];
         bad |= !(uu >= 0.f && uu < 1.f);
     }
-    if (tid < rows - 1) bad |= (d[tid] < 0 || d[tid] >= v);
+    if (tid < rows - 1) {
+        s_d[tid] = A.d[tid];
+        bad |= (A.d[tid] < 0 || A.d[tid] >= v);
+    }
     if (tid == 0) s_jr = rows - 1;
     bad = __syncthreads_or(bad);
     // Accept tests of all drafts at once (thread j tests draft j): the first
     // reject ends the accepted prefix and supplies the final draw, else the
     // last row does.
     if (!bad && tid < rows - 1) {
-        const float2 rs = s_rows[tid];
-        const int dj = d[tid];
-        const float pd = expf(z[(int64_t)tid * ldz + dj] / temperature - rs.x) / rs.y;
-        const float qd = q[(int64_t)tid * ldq + dj];
-        if (!(u[tid] * qd < pd)) atomicMin(&s_jr, tid);
+        const RowView r = row_view(A, W, s_rows[tid], tid);
+        const int dj = s_d[tid];
+        const float pd = p_of(A, s_d, nullptr, r, tid, dj, A.z[(int64_t)tid * A.ldz + dj]);
+        const float qd = q_of(A, r, dj, A.q[(int64_t)tid * A.ldq + dj]);
+        if (!(A.u[tid] * qd < pd)) atomicMin(&s_jr, tid);
     }
     __syncthreads();
     const int jr = s_jr;
+    build_bloom(s_bloom, s_d, jr);
     const bool draft_row = jr < rows - 1;
+    const RowView rv = row_view(A, W, s_rows[jr], jr);
     {
-        const float2 rs = s_rows[jr];
         const int v0 = c * CH, v1 = min(v, v0 + CH);
-        const float *zr = z + (int64_t)jr * ldz;
-        const float *qr = q + (int64_t)jr * ldq;
+        const float *zr = A.z + (int64_t)jr * A.ldz;
+        const float *qr = A.q + (int64_t)jr * A.ldq;
         float res = 0.f, pm = 0.f;
 #pragma unroll
         for (int i = 0; i < EPT; ++i) {
             const int col = v0 + tid + TPB * i;
             if (col < v1) {
-                const float p = expf(zr[col] / temperature - rs.x) / rs.y;
+                const float p = p_of(A, s_d, s_bloom, rv, jr, col, zr[col]);
                 pm += p;
-                if (draft_row) res += fmaxf(0.f, p - qr[col]);
+                if (draft_row) res += fmaxf(0.f, p - q_of(A, rv, col, qr[col]));
             }
         }
-        const float rmass = block_sum(res, scratch);
-        const float pmass = block_sum(pm, scratch);
+        const float rmass = block_sum<TPB>(res, scratch);
+        const float pmass = block_sum<TPB>(pm, scratch);
         // arrival: thread 0 wrote this workgroup's masses and waits for them
         // to complete before it signals
         if (tid == 0) {
@@ -229,18 +1070,18 @@ __global__ __launch_bounds__(TPB) void sample_decide_kernel(
     __syncthreads();
     if (!s_flag[0]) return;
 
-    // faults: any flagged chunk (non-finite logit, bad q), a uniform or draft id out of range
+    // faults: any flagged chunk (non-finite logit, bad q or count), a uniform or draft id out of range
     for (int i = tid; i < rows * nchunks; i += TPB) bad |= W.flags[i] != 0;
     bad = __syncthreads_or(bad);
     if (bad) {
-        if (tid < rows) committed[tid] = -1;
+        if (tid < rows) A.committed[tid] = -1;
         if (tid == 0) {
-            accept_len[0] = -1;
+            A.accept_len[0] = -1;
             atomicExch(W.counter, 0u);
         }
         return;
     }
-    if (tid < jr) committed[tid] = d[tid];
+    if (tid < jr) A.committed[tid] = s_d[tid];
     if (tid == 0) {
         s_lastc = -1;
         s_cut = ~0ull;
@@ -253,10 +1094,10 @@ __global__ __launch_bounds__(TPB) void sample_decide_kernel(
         tr += mm.x;
         tp += mm.y;
     }
-    const float total_res = block_sum(tr, scratch);
-    const float total_p = block_sum(tp, scratch);
+    const float total_res = block_sum<TPB>(tr, scratch);
+    const float total_p = block_sum<TPB>(tp, scratch);
     const int use_res = draft_row && total_res > 0.f;
-    const float thr = u[rows - 1] * (use_res ? total_res : total_p);
+    const float thr = A.u[rows - 1] * (use_res ? total_res : total_p);
     // chunk holding the draw: the first whose inclusive prefix of masses
     // exceeds thr (prefix sums in chunk order, TPB chunks per round); its
     // exclusive prefix travels with it in one 64-bit key
@@ -296,13 +1137,12 @@ __global__ __launch_bounds__(TPB) void sample_decide_kernel(
         last_pos = 1;
         thr_local = 0.f;
     }
-    const float2 rs = s_rows[jr];
     __syncthreads();
 
     // inverse CDF inside chunk cstar: thread t owns EPT consecutive logits
     const int base = cstar * CH + tid * EPT;
-    const float *zj = z + (int64_t)jr * ldz;
-    const float *qj = q + (int64_t)jr * ldq;
+    const float *zj = A.z + (int64_t)jr * A.ldz;
+    const float *qj = A.q + (int64_t)jr * A.ldq;
     float wv[EPT];
     float tot = 0.f;
 #pragma unroll
@@ -310,8 +1150,8 @@ __global__ __launch_bounds__(TPB) void sample_decide_kernel(
         const int col = base + i;
         float wgt = 0.f;
         if (col < v) {
-            const float p = expf(zj[col] / temperature - rs.x) / rs.y;
-            wgt = use_res ? fmaxf(0.f, p - qj[col]) : p;
+            const float p = p_of(A, s_d, s_bloom, rv, jr, col, zj[col]);
+            wgt = use_res ? fmaxf(0.f, p - q_of(A, rv, col, qj[col])) : p;
         }
         wv[i] = wgt;
         tot += wgt;
@@ -346,20 +1186,16 @@ __global__ __launch_bounds__(TPB) void sample_decide_kernel(
     if (tid == 0) {
         int tok = s_pick;
         if (tok == 0x7fffffff) tok = s_last >= 0 ? s_last : min(v - 1, cstar * CH + CH - 1);
-        committed[jr] = tok;
-        for (int i = jr + 1; i < rows; ++i) committed[i] = -1;
-        accept_len[0] = jr + 1;
+        A.committed[jr] = tok;
+        for (int i = jr + 1; i < rows; ++i) A.committed[i] = -1;
+        A.accept_len[0] = jr + 1;
         atomicExch(W.counter, 0u);
     }
 }
 
 }  // namespace
 
-size_t sample_workspace_bytes(int32_t v, int32_t m_rows) {
-    const size_t nchunks = (size_t)(v + CH - 1) / CH;
-    return 256 + align256(m_rows * nchunks * sizeof(float2)) + align256(m_rows * nchunks * sizeof(int32_t)) +
-           align256(nchunks * sizeof(float2));
-}
+size_t sample_workspace_bytes(int32_t v, int32_t m_rows) { return ws_layout(m_rows, v).total; }
 
 hipError_t launch_accept_greedy(const int32_t *t, const int32_t *d, int32_t b, int32_t m_rows,
                                 int32_t *accept_len, int32_t *committed, hipStream_t s) {
@@ -369,17 +1205,40 @@ hipError_t launch_accept_greedy(const int32_t *t, const int32_t *d, int32_t b, i
     return hipGetLastError();
 }
 
-hipError_t launch_accept_sample(const float *z, int64_t ldz, const float *q, int64_t ldq,
-                                const int32_t *d, const float *u, int32_t m_rows, int32_t v,
-                                float temperature, int32_t *accept_len, int32_t *committed, void *ws,
-                                hipStream_t s) {
-    const int nchunks = (v + CH - 1) / CH;
-    hipLaunchKernelGGL(sample_stats_kernel, dim3(nchunks, m_rows), dim3(TPB), 0, s, z, ldz, q, ldq, m_rows, v,
-                       temperature, ws);
+hipError_t launch_accept_sample(const SampleParams &P, hipStream_t s) {
+    SampleArgs A;
+    A.z = P.z;
+    A.ldz = P.ldz;
+    A.q = P.q;
+    A.ldq = P.ldq;
+    A.d = P.d;
+    A.u = P.u;
+    A.rows = P.m_rows;
+    A.v = P.v;
+    A.inv_t = 1.f / P.temperature;
+    A.top_k = P.top_k;
+    A.top_p = P.top_p;
+    A.presence = P.presence;
+    A.frequency = P.frequency;
+    A.counts = P.counts;
+    A.pen = P.presence != 0.f || P.frequency != 0.f;
+    A.trunc = (P.top_k > 0 && P.top_k < P.v) || P.top_p < 1.f;
+    A.accept_len = P.accept_len;
+    A.committed = P.committed;
+    A.ws = P.ws;
+    const int nchunks = (P.v + CH - 1) / CH;
+    hipLaunchKernelGGL(sample_stats_kernel, dim3(nchunks, P.m_rows), dim3(TPB), 0, s, A);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(sample_decide_kernel, dim3(nchunks), dim3(TPB), 0, s, z, ldz, q, ldq, d, u, m_rows, v,
-                       temperature, accept_len, committed, ws);
+    if (A.trunc) {
+        hipLaunchKernelGGL(sample_bins_kernel, dim3((P.v + SLICE - 1) / SLICE, P.m_rows, 2), dim3(BT), 0, s, A);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(sample_trunc_kernel, dim3(P.m_rows, 2), dim3(FT), 0, s, A);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(sample_decide_kernel, dim3(nchunks), dim3(TPB), 0, s, A);
     return hipGetLastError();
 }
 

@@ -251,26 +251,70 @@ size_t dspk_sample_workspace_bytes(int32_t v, int32_t m_rows) {
     return dspk::sample_workspace_bytes(v, m_rows);
 }
 
-int dspk_accept_sample(const float *logits, int64_t ldz, const float *q, int64_t ldq, const int32_t *draft_ids,
-                       const float *uniforms, int32_t m_rows, int32_t v, float temperature, int32_t *accept_len,
-                       int32_t *committed, void *workspace, size_t ws_bytes, void *stream) {
-    const char *who = "dspk_accept_sample";
+static int accept_sample_common(const char *who, const float *logits, int64_t ldz, const float *q, int64_t ldq,
+                                const int32_t *draft_ids, const float *uniforms, int32_t m_rows, int32_t v,
+                                const dspk_sample_params &sp, const int32_t *counts, int32_t *accept_len,
+                                int32_t *committed, void *workspace, size_t ws_bytes, void *stream) {
     if (m_rows < 2 || m_rows > DSPK_MAX_ROWS)
         return fail(DSPK_EINVAL, "%s: m_rows=%d out of 2..%d", who, m_rows, DSPK_MAX_ROWS);
     if (v < 1) return fail(DSPK_EINVAL, "%s: v=%d must be >= 1", who, v);
-    if (!(temperature > 0.f) || !isfinite(temperature))
+    if (!(sp.temperature > 0.f) || !isfinite(sp.temperature))
         return fail(DSPK_EINVAL, "%s: temperature must be finite and > 0", who);
+    if (sp.top_k < 0) return fail(DSPK_EINVAL, "%s: top_k=%d must be >= 0", who, sp.top_k);
+    if (!(sp.top_p > 0.f && sp.top_p <= 1.f)) return fail(DSPK_EINVAL, "%s: top_p must be in (0, 1]", who);
+    if (!isfinite(sp.presence_penalty) || !isfinite(sp.frequency_penalty))
+        return fail(DSPK_EINVAL, "%s: penalties must be finite", who);
     if (logits == nullptr || q == nullptr || draft_ids == nullptr || uniforms == nullptr || accept_len == nullptr ||
         committed == nullptr)
         return fail(DSPK_EINVAL, "%s: NULL pointer", who);
-    if (!aligned(logits, 4) || !aligned(q, 4)) return fail(DSPK_EINVAL, "%s: misaligned logits or q", who);
+    if (!aligned(logits, 4) || !aligned(q, 4) || !aligned(counts, 4))
+        return fail(DSPK_EINVAL, "%s: misaligned logits, q or counts", who);
     if (ldz < v || ldq < v) return fail(DSPK_EINVAL, "%s: ldz/ldq must be >= v", who);
     const size_t need = dspk_sample_workspace_bytes(v, m_rows);
     if (workspace == nullptr || !aligned(workspace, 256) || ws_bytes < need)
         return fail(DSPK_EINVAL, "%s: workspace of %zu bytes required (256-byte aligned)", who, need);
-    return launch_result(dspk::launch_accept_sample(logits, ldz, q, ldq, draft_ids, uniforms, m_rows, v, temperature,
-                                                    accept_len, committed, workspace, (hipStream_t)stream),
-                         who);
+    dspk::SampleParams P;
+    P.z = logits;
+    P.ldz = ldz;
+    P.q = q;
+    P.ldq = ldq;
+    P.d = draft_ids;
+    P.u = uniforms;
+    P.m_rows = m_rows;
+    P.v = v;
+    P.temperature = sp.temperature;
+    P.top_k = sp.top_k;
+    P.top_p = sp.top_p;
+    P.presence = sp.presence_penalty;
+    P.frequency = sp.frequency_penalty;
+    P.counts = counts;
+    P.accept_len = accept_len;
+    P.committed = committed;
+    P.ws = workspace;
+    return launch_result(dspk::launch_accept_sample(P, (hipStream_t)stream), who);
+}
+
+int dspk_accept_sample(const float *logits, int64_t ldz, const float *q, int64_t ldq, const int32_t *draft_ids,
+                       const float *uniforms, int32_t m_rows, int32_t v, float temperature, int32_t *accept_len,
+                       int32_t *committed, void *workspace, size_t ws_bytes, void *stream) {
+    dspk_sample_params sp;
+    sp.temperature = temperature;
+    sp.top_k = 0;
+    sp.top_p = 1.f;
+    sp.presence_penalty = 0.f;
+    sp.frequency_penalty = 0.f;
+    return accept_sample_common("dspk_accept_sample", logits, ldz, q, ldq, draft_ids, uniforms, m_rows, v, sp,
+                                nullptr, accept_len, committed, workspace, ws_bytes, stream);
+}
+
+int dspk_accept_sample_ex(const float *logits, int64_t ldz, const float *q, int64_t ldq, const int32_t *draft_ids,
+                          const float *uniforms, int32_t m_rows, int32_t v, const dspk_sample_params *params,
+                          const int32_t *counts, int32_t *accept_len, int32_t *committed, void *workspace,
+                          size_t ws_bytes, void *stream) {
+    const char *who = "dspk_accept_sample_ex";
+    if (params == nullptr) return fail(DSPK_EINVAL, "%s: params is NULL", who);
+    return accept_sample_common(who, logits, ldz, q, ldq, draft_ids, uniforms, m_rows, v, *params, counts,
+                                accept_len, committed, workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

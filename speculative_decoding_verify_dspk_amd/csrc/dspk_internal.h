@@ -93,9 +93,22 @@ hipError_t launch_accept_greedy(const int32_t *t, const int32_t *d, int32_t b, i
 
 constexpr int kSampleChunk = 4096;   // logits per workgroup in the sampling kernels
 size_t sample_workspace_bytes(int32_t v, int32_t m_rows);
-hipError_t launch_accept_sample(const float *z, int64_t ldz, const float *q, int64_t ldq,
-                                const int32_t *d, const float *u, int32_t m_rows, int32_t v,
-                                float temperature, int32_t *accept_len, int32_t *committed,
-                                void *ws, hipStream_t s);
+struct SampleParams {
+    const float *z;
+    int64_t ldz;
+    const float *q;
+    int64_t ldq;
+    const int32_t *d;
+    const float *u;
+    int32_t m_rows, v;
+    float temperature;
+    int32_t top_k;            // 0: off
+    float top_p;              // 1: off
+    float presence, frequency;
+    const int32_t *counts;    // or NULL
+    int32_t *accept_len, *committed;
+    void *ws;
+};
+hipError_t launch_accept_sample(const SampleParams &p, hipStream_t s);
 
 }  // namespace dspk

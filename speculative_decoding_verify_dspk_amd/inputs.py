@@ -198,6 +198,15 @@ def draft_distribution(target_logits: np.ndarray, temperature: float,
 
 # ------------------------------------------------------- workload shape tables
 # Projection shapes (N out, K in) of the synthetic decoder layers.
+def history_counts(vocab: int, length: int, *labels) -> np.ndarray:
+    """Token counts of a seeded synthetic history of ``length`` tokens
+    (Zipf-like token frequencies, as text has), int32 [vocab]."""
+    g = rng("history", vocab, length, *labels)
+    ranks = np.minimum(g.zipf(1.2, size=length), vocab) - 1
+    ids = g.permutation(vocab)[ranks]
+    return np.bincount(ids, minlength=vocab).astype(np.int32)
+
+
 LAYER_SHAPES = {
     # Qwen3-4B: hidden 2560, 32 q heads x 128, 8 kv heads x 128, intermediate 9728
     "qwen3-4b": dict(hidden=2560, q=4096, kv=1024, inter=9728, vocab=151936),

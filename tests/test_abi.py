@@ -159,6 +159,27 @@ def test_accept_rejects(lib):
     assert call(z=X + 2) == EINVAL
 
 
+def test_accept_sample_ex_rejects(lib):
+    need = lib.dspk_sample_workspace_bytes(1000, 4)
+
+    def call(params=True, counts=None, **kw):
+        sp = binding.sample_params(**{**dict(temperature=1.0), **kw})
+        return lib.dspk_accept_sample_ex(X, 1000, X, 1000, X, X, 4, 1000, ctypes.byref(sp) if params else None,
+                                         counts, Y, Y, WS, need, None)
+    assert call(params=False) == EINVAL
+    assert call(temperature=0.0) == EINVAL
+    assert call(temperature=float("inf")) == EINVAL
+    assert call(top_k=-1) == EINVAL
+    assert call(top_p=0.0) == EINVAL
+    assert call(top_p=1.5) == EINVAL
+    assert call(top_p=float("nan")) == EINVAL
+    assert call(presence=float("nan")) == EINVAL
+    assert call(frequency=float("inf")) == EINVAL
+    assert call(counts=X + 2) == EINVAL
+    # the truncation records live in the same workspace query
+    assert lib.dspk_sample_workspace_bytes(151936, 32) > lib.dspk_sample_workspace_bytes(151936, 2)
+
+
 def _imports(path):
     src = open(path).read()
     return set(re.findall(r"^\s*(?:from|import)\s+([\w\.]+)", src, re.M))
