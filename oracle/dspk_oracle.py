@@ -64,21 +64,25 @@ def decode_bf16(bits) -> np.ndarray:
 def unpack_codes(codes, bits: int, k: int) -> np.ndarray:
     """Integer codes ``[N][K]`` from packed words ``uint32[N][K*bits/32]``.
 
-    Reading of the (unstated) packing: LSB-first, 32/bits codes per word, so
-    code k of a row sits in word k // (32/bits) at bit offset
-    bits * (k mod 32/bits).
+    Reading of the (unstated) packing: each row is one LSB-first bit stream
+    stored in little-endian uint32 words -- bit i of the row is bit i % 32 of
+    word i // 32 -- and code k occupies stream bits bits*k .. bits*k + bits-1,
+    lowest bit first.  For 2, 4 and 8 bits that is 32/bits codes per word;
+    3-bit codes may straddle two words.
     """
-    if bits not in (4, 8):
-        raise ValueError("unpack_codes: bits must be 4 or 8")
-    per = 32 // bits
+    if bits not in (2, 3, 4, 8):
+        raise ValueError("unpack_codes: bits must be 2, 3, 4 or 8")
     words = np.asarray(codes, dtype=np.uint32)
     n = words.shape[0]
-    if words.shape[1] * per != k:
+    if words.shape[1] * 32 != k * bits:
         raise ValueError("unpack_codes: packed width does not match K")
-    mask = np.uint32((1 << bits) - 1)
-    q = np.empty((n, k), dtype=np.int64)
-    for slot in range(per):
-        q[:, slot::per] = (words >> np.uint32(bits * slot)) & mask
+    # the row's bit stream, bit i at column i
+    stream = np.zeros((n, 32 * words.shape[1]), dtype=np.int64)
+    for b in range(32):
+        stream[:, b::32] = (words >> np.uint32(b)) & np.uint32(1)
+    q = np.zeros((n, k), dtype=np.int64)
+    for b in range(bits):
+        q |= stream[:, b::bits][:, :k] << b
     return q
 
 

@@ -9,8 +9,9 @@ Storage formats (the pages say only that the target's weights are quantised in
 groups -- "mlx-dspark" wiki summary, "Key techniques"; the format below is the
 plain affine group format):
 
-* codes: unsigned integers 0 .. 2**bits - 1, packed LSB-first into uint32 words,
-  32/bits codes per word, each output row's K codes contiguous;
+* codes: unsigned integers 0 .. 2**bits - 1, each output row's K codes one
+  LSB-first bit stream in uint32 words (32/bits codes per word for 2, 4 and
+  8 bits; 3-bit codes may straddle words);
 * scales, biases: IEEE binary16 bit patterns, row-major ``[N][K/64]``;
 * activations: bfloat16 bit patterns, row-major ``[M][K]``;
 * uniforms for stochastic acceptance: float32 values k / 2**24.
@@ -71,21 +72,25 @@ def bf16_bits_to_f32(bits) -> np.ndarray:
 
 # ----------------------------------------------------------------------- packing
 def pack_codes(codes_u8: np.ndarray, bits: int) -> np.ndarray:
-    """Pack integer codes ``[N][K]`` LSB-first into ``uint32[N][K*bits/32]``."""
-    if bits not in (4, 8):
-        raise ValueError("bits must be 4 or 8")
-    c = np.asarray(codes_u8, dtype=np.uint32)
+    """Pack integer codes ``[N][K]`` into ``uint32[N][K*bits/32]``: each row an
+    LSB-first bit stream (code k at stream bits bits*k ..), 32 stream bits per
+    little-endian word.  For 2, 4 and 8 bits that is 32/bits codes per word."""
+    if bits not in (2, 3, 4, 8):
+        raise ValueError("bits must be 2, 3, 4 or 8")
+    c = np.asarray(codes_u8, dtype=np.uint64)
     n, k = c.shape
-    per = 32 // bits
-    if k % per:
-        raise ValueError("K must be a multiple of 32/bits")
+    if (k * bits) % 32:
+        raise ValueError("K * bits must be a multiple of 32")
     if c.max(initial=0) >= (1 << bits):
         raise ValueError("code out of range")
-    c = c.reshape(n, k // per, per)
-    words = np.zeros((n, k // per), dtype=np.uint32)
-    for slot in range(per):
-        words |= c[:, :, slot] << np.uint32(bits * slot)
-    return words
+    words = np.zeros((n, k * bits // 32), dtype=np.uint64)
+    pos = np.arange(k, dtype=np.int64) * bits
+    w, off = pos // 32, (pos % 32).astype(np.uint64)
+    for i in range(k):
+        words[:, w[i]] |= (c[:, i] << off[i]) & np.uint64(0xffffffff)
+        if off[i] + bits > 32:                       # the code's high bits start the next word
+            words[:, w[i] + 1] |= c[:, i] >> (np.uint64(32) - off[i])
+    return words.astype(np.uint32)
 
 
 # ----------------------------------------------------------------- weights, acts
@@ -95,10 +100,10 @@ class QWeight:
     n: int
     k: int
     bits: int
-    codes: np.ndarray            # uint32 [N][K*bits/32] (bits 4/8) or uint16 bf16 [N][K] (bits 16)
+    codes: np.ndarray            # uint32 [N][K*bits/32] (bits 2/3/4/8) or uint16 bf16 [N][K] (bits 16)
     scales: np.ndarray | None    # uint16 fp16 [N][K/64]
     biases: np.ndarray | None    # uint16 fp16 [N][K/64]
-    codes_u8: np.ndarray | None  # uint8 [N][K] ground-truth codes (bits 4/8)
+    codes_u8: np.ndarray | None  # uint8 [N][K] ground-truth codes (quantised formats)
 
     @property
     def nbytes(self) -> int:

@@ -34,7 +34,7 @@ def test_decoders_match_bitfield_definition(kind):
     assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("shape", [(1, 64), (3, 128), (17, 320)])
 def test_unpack_matches_ground_truth_codes(bits, shape):
     n, k = shape
@@ -49,9 +49,14 @@ def test_unpack_hand_words():
     for c in cases:
         bits = c["bits"]
         words = np.array([[int(h, 16) for h in c["expected_words_hex"]]], dtype=np.uint32)
-        k = words.shape[1] * (32 // bits)
+        k = words.shape[1] * 32 // bits
         q = oracle.unpack_codes(words, bits, k)
-        expect = np.arange(k) % (1 << bits)
+        if "sparse" in c:
+            expect = np.zeros(k, dtype=np.int64)
+            for i, val in c["sparse"].items():
+                expect[int(i)] = val
+        else:
+            expect = np.arange(k) % (1 << bits)
         assert np.array_equal(q[0], expect), c
         # and the generator's packer produces exactly those words
         assert np.array_equal(inputs.pack_codes(expect[None, :].astype(np.uint8), bits), words)
@@ -61,7 +66,11 @@ def test_unpack_rejects_bad_width():
     with pytest.raises(ValueError):
         oracle.unpack_codes(np.zeros((2, 3), np.uint32), 8, 16)
     with pytest.raises(ValueError):
-        oracle.unpack_codes(np.zeros((2, 3), np.uint32), 2, 48)
+        oracle.unpack_codes(np.zeros((2, 3), np.uint32), 2, 64)
+    with pytest.raises(ValueError):
+        oracle.unpack_codes(np.zeros((2, 3), np.uint32), 3, 64)
+    with pytest.raises(ValueError):
+        oracle.unpack_codes(np.zeros((2, 3), np.uint32), 5, 96 // 5)
 
 
 def test_bf16_rounding_of_generator_is_nearest_even():

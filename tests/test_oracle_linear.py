@@ -47,7 +47,7 @@ def _exact_linear(x_bits, w):
     return y, yabs
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_qlinear_exact_rational(bits):
     m, n, k = 2, 3, 192
     w = inputs.make_qweight(n, k, bits, "exact-pin")
@@ -61,7 +61,7 @@ def test_qlinear_exact_rational(bits):
             assert abs(Fraction(got[i, j]) - ref[i][j]) <= Fraction(k + 2, 2 ** 53) * ref_abs[i][j], (i, j)
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_qlinear_integer_reduction(bits):
     """s = 1, b = 0 and small-integer x: the product is an exact integer matmul."""
     m, n, k = 5, 7, 256
@@ -85,7 +85,7 @@ def test_qlinear_bf16_control_is_plain_matmul():
     assert np.allclose(y, np.matmul(xf, wf.T), rtol=1e-13, atol=1e-12)
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_qlinear_all_ones(bits):
     n, k = 9, 320
     w = inputs.make_qweight(n, k, bits, "ones-pin")
