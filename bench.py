@@ -19,7 +19,7 @@ Other workloads of the same path:
         add --top-k 50 --top-p 0.9 --presence 0.5 --frequency 0.1 for the
         truncated, penalised rule (history counts of a seeded 4096-token
         Zipf-like history; drafts drawn from the untruncated q);
-  --config ornith-9b --bits 4|8|16 --sweep 1,2,...,16
+  --config ornith-9b --bits 2|3|4|8|16 --sweep 1,2,...,16
         the 9B-shaped layer and 151936x4096 head per weight format;
   --config qwen3-8b --batch 4 --sweep 6 --alpha 0.3,0.5,0.7,0.9
         four requests of six rows in one launch, greedy accept per request.
@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="qwen3-4b", choices=["qwen3-4b", "qwen3-8b", "ornith-9b", "dense-27b"])
-    ap.add_argument("--bits", type=int, default=8, choices=[4, 8, 16])
+    ap.add_argument("--bits", type=int, default=8, choices=[2, 3, 4, 8, 16])
     ap.add_argument("--layers", type=int, default=1)
     ap.add_argument("--copies", type=int, default=3, help="rotating weight copies (defeat the 256 MB MALL)")
     ap.add_argument("--sweep", default=",".join(map(str, SWEEP)), help="rows per request, one round each")

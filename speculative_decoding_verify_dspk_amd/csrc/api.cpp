@@ -32,8 +32,8 @@ int ok() {
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 int check_shape(int32_t n, int32_t k, int32_t bits, int32_t group, const char *who) {
-    if (bits != 4 && bits != 8 && bits != 16)
-        return fail(DSPK_EUNSUPPORTED, "%s: bits=%d (supported: 4, 8, 16)", who, bits);
+    if (!dspk::supported_bits(bits))
+        return fail(DSPK_EUNSUPPORTED, "%s: bits=%d (supported: 2, 3, 4, 8, 16)", who, bits);
     if (group != DSPK_GROUP) return fail(DSPK_EUNSUPPORTED, "%s: group=%d (must be 64)", who, group);
     if (n < 1) return fail(DSPK_EINVAL, "%s: n=%d must be >= 1", who, n);
     if (k < DSPK_GROUP || k % DSPK_GROUP) return fail(DSPK_EINVAL, "%s: k=%d must be a positive multiple of 64", who, k);
@@ -171,7 +171,7 @@ int dspk_qweight_pack(const dspk_qweight *w, void *tiles, size_t tiles_bytes, vo
 size_t dspk_qgemm_workspace_bytes(int32_t n, int32_t k, int32_t m) {
     if (n < 1 || k < DSPK_GROUP || k % DSPK_GROUP || m < 1 || m > DSPK_MAX_ROWS) return 0;
     size_t most = 0;
-    for (int bits : {4, 8, 16}) {   // the plan depends on the format only through the stage depth
+    for (int bits : {2, 3, 4, 8, 16}) {   // the plan depends on the format only through the stage depth
         const size_t b = dspk::plan_gemm(1, &n, k, m, bits, false).ws_bytes;
         most = b > most ? b : most;
     }

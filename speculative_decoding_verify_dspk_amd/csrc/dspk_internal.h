@@ -16,14 +16,21 @@ constexpr int kMaxRows = 32;
 
 // Tiled weight layout (the format every projection kernel reads; written by
 // dspk_qweight_pack).  A weight is cut into units of 64 output columns times
-// tile_k(bits) K elements -- 8 KiB of codes in every format -- stored unit
-// after unit, K fastest within a 64-column block, blocks in column order.
-// A unit is 8 slots of 1 KiB (one 16-byte piece per lane of a wave, in the
-// MFMA operand order of that lane) followed, for quantised formats, by the
-// scale/bias dwords of its groups (16 columns x tile_k/64 groups x 4 tiles).
+// tile_k(bits) K elements, stored unit after unit, K fastest within a
+// 64-column block, blocks in column order.  A unit is tile_code_slots(bits)
+// slots of 1 KiB (one 16-byte piece per lane of a wave, in the MFMA operand
+// order of that lane) -- 8 for 4/8-bit and bf16, 4 for 2-bit, 6 for 3-bit --
+// followed, for quantised formats, by the scale/bias dwords of its groups
+// (16 columns x tile_k/64 groups x 4 tiles).  2- and 3-bit units span four
+// groups like 4-bit ones, so a lane's activation registers stay those of
+// the 4-bit kernel.
 constexpr int tile_k(int bits) { return bits == 16 ? 64 : bits == 8 ? 128 : 256; }
 constexpr int tile_groups(int bits) { return tile_k(bits) / 64; }
-constexpr int tile_unit_bytes(int bits) { return 8192 + (bits == 16 ? 0 : 256 * tile_groups(bits)); }
+constexpr int tile_code_slots(int bits) { return bits == 2 ? 4 : bits == 3 ? 6 : 8; }
+constexpr int tile_unit_bytes(int bits) {
+    return 1024 * tile_code_slots(bits) + (bits == 16 ? 0 : 256 * tile_groups(bits));
+}
+constexpr bool supported_bits(int bits) { return bits == 2 || bits == 3 || bits == 4 || bits == 8 || bits == 16; }
 size_t tiled_bytes(int32_t n, int32_t k, int bits);
 hipError_t launch_pack(int32_t n, int32_t k, int bits, const void *codes, const uint16_t *scales,
                        const uint16_t *biases, void *tiles, hipStream_t s);

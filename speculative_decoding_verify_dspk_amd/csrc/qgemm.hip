@@ -79,6 +79,45 @@ __device__ __forceinline__ bf16x8 codes4_to_bf16(uint32_t w) {
     return as_bf16x8(r);
 }
 
+// sixteen 2-bit codes (one dword, code e in bits 2e..2e+1) -> two bf16x8 of
+// 128 + q in the order q0,q8,q1,q9,q2,q10,q3,q11 | q4,q12,...,q7,q15
+__device__ __forceinline__ void codes2_to_bf16(uint32_t w, bf16x8 &b0, bf16x8 &b1) {
+    u32x4 r0, r1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r0[i] = ((w >> (2 * i)) & 0x00030003u) | 0x43004300u;
+        r1[i] = ((w >> (2 * i + 8)) & 0x00030003u) | 0x43004300u;
+    }
+    b0 = as_bf16x8(r0);
+    b1 = as_bf16x8(r1);
+}
+
+// sixteen 3-bit codes: low planes as for 2-bit (lo) and the high bits h with
+// code e's at bit e (e < 8) and at bit 16 + e - 8 (e >= 8), so that the bit of
+// code i lands at bit 2 of a half and that of code i + 8 at bit 18
+__device__ __forceinline__ void codes3_to_bf16(uint32_t lo, uint32_t h, bf16x8 &b0, bf16x8 &b1) {
+    u32x4 r0, r1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r0[i] = ((lo >> (2 * i)) & 0x00030003u) | ((((h >> i) << 2) & 0x00040004u) | 0x43004300u);
+        r1[i] = ((lo >> (2 * i + 8)) & 0x00030003u) | ((((h >> (i + 4)) << 2) & 0x00040004u) | 0x43004300u);
+    }
+    b0 = as_bf16x8(r0);
+    b1 = as_bf16x8(r1);
+}
+
+// activations x0..x7 (p0) and x8..x15 (p1) reordered to match codes2_to_bf16
+__device__ __forceinline__ void perm_x_for2(u32x4 p0, u32x4 p1, u32x4 &a0, u32x4 &a1) {
+    a0[0] = __builtin_amdgcn_perm(p1[0], p0[0], 0x05040100u);
+    a0[1] = __builtin_amdgcn_perm(p1[0], p0[0], 0x07060302u);
+    a0[2] = __builtin_amdgcn_perm(p1[1], p0[1], 0x05040100u);
+    a0[3] = __builtin_amdgcn_perm(p1[1], p0[1], 0x07060302u);
+    a1[0] = __builtin_amdgcn_perm(p1[2], p0[2], 0x05040100u);
+    a1[1] = __builtin_amdgcn_perm(p1[2], p0[2], 0x07060302u);
+    a1[2] = __builtin_amdgcn_perm(p1[3], p0[3], 0x05040100u);
+    a1[3] = __builtin_amdgcn_perm(p1[3], p0[3], 0x07060302u);
+}
+
 // eight bf16 activations reordered to match codes4_to_bf16
 __device__ __forceinline__ u32x4 perm_x_for4(u32x4 x) {
     u32x4 r;
@@ -121,6 +160,8 @@ struct Cfg {
     static constexpr int GS = tile_groups(BITS);
     static constexpr int SBQ = BITS == 16 ? 0 : GS;
     static constexpr int UNIT = tile_unit_bytes(BITS);
+    static constexpr int NS = tile_code_slots(BITS);     // 1 KiB code slots per unit
+    static constexpr int SBOFF = 1024 * NS;              // scale/bias dwords within a unit
 };
 
 // 16-column tiles posted per pass of the in-workgroup sum
@@ -244,7 +285,7 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT)) void qgemm_kernel(const 
     // One ring slot: a unit's eight code pieces and scale/bias dwords of this
     // lane, and the matching activation fragments.
     struct Slot {
-        u32x4 w[8];
+        u32x4 w[C::NS];
         u32x4 sb[C::SBQ > 0 ? C::SBQ : 1];
         u32x4 a[C::GS][MT][2];
     };
@@ -274,9 +315,9 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT)) void qgemm_kernel(const 
         const int st = 4 * u.qi + w;
         const unsigned char *ub = ib_base + (size_t)st * C::UNIT;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) s.w[i] = load_nt(ub + i * 1024 + 16 * lane);
+        for (int i = 0; i < C::NS; ++i) s.w[i] = load_nt(ub + i * 1024 + 16 * lane);
 #pragma unroll
-        for (int q = 0; q < C::SBQ; ++q) s.sb[q] = load16(ub + 8192 + c * (16 * C::SBQ) + 16 * q);
+        for (int q = 0; q < C::SBQ; ++q) s.sb[q] = load16(ub + C::SBOFF + c * (16 * C::SBQ) + 16 * q);
         // lane (c, j) takes row 16*mt + c, K offsets 64*g + 16*j (+8): a
         // wave-uniform byte offset per (g, h) plus a fixed lane offset.  The
         // groups past the end of K (a short last unit) re-read the last one.
@@ -317,6 +358,11 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT)) void qgemm_kernel(const 
                 if constexpr (BITS == 4) {
                     a0[mt] = as_bf16x8(perm_x_for4(s.a[g][mt][0]));
                     a1[mt] = as_bf16x8(perm_x_for4(s.a[g][mt][1]));
+                } else if constexpr (BITS == 2 || BITS == 3) {
+                    u32x4 p0, p1;
+                    perm_x_for2(s.a[g][mt][0], s.a[g][mt][1], p0, p1);
+                    a0[mt] = as_bf16x8(p0);
+                    a1[mt] = as_bf16x8(p1);
                 } else {
                     a0[mt] = as_bf16x8(s.a[g][mt][0]);
                     a1[mt] = as_bf16x8(s.a[g][mt][1]);
@@ -349,6 +395,14 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT)) void qgemm_kernel(const 
                         const u32x4 qv = s.w[4 * g + t];
                         b0 = codes8_to_bf16(qv[0], qv[1]);
                         b1 = codes8_to_bf16(qv[2], qv[3]);
+                    } else if constexpr (BITS == 2) {
+                        // slot t, dword g
+                        codes2_to_bf16(s.w[t][g], b0, b1);
+                    } else if constexpr (BITS == 3) {
+                        // low planes: slot t, dword g; high bits: slot 4 + t/2,
+                        // dword 2*(t%2) + g/2, byte lanes 8*(g%2) of each half
+                        const uint32_t hd = s.w[4 + (t >> 1)][2 * (t & 1) + (g >> 1)];
+                        codes3_to_bf16(s.w[t][g], hd >> (8 * (g & 1)), b0, b1);
                     } else {
                         // slot (g/2)*4 + t: groups 2*(g/2) and 2*(g/2)+1, 8 bytes each
                         const u32x4 qv = s.w[4 * (g >> 1) + t];
@@ -359,7 +413,7 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT)) void qgemm_kernel(const 
                     const uint32_t sbd = s.sb[g][t];
                     const float sc = h2f(sbd & 0xffffu);
                     float bi = h2f(sbd >> 16);
-                    if constexpr (BITS == 4) bi = fmaf(-128.f, sc, bi);   // codes carry +128
+                    if constexpr (BITS <= 4) bi = fmaf(-128.f, sc, bi);   // codes carry +128
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) {
                         f32x4 acc = mfma(a0[mt], b0, zero);
@@ -614,6 +668,8 @@ hipError_t launch_cfg(const GemmLaunch &L, int grid, hipStream_t s) {
 template <bool ARGMAX>
 hipError_t launch_any(const GemmLaunch &L, int bits, int grid, hipStream_t s) {
     switch (bits) {
+        case 2: return launch_cfg<2, ARGMAX>(L, grid, s);
+        case 3: return launch_cfg<3, ARGMAX>(L, grid, s);
         case 4: return launch_cfg<4, ARGMAX>(L, grid, s);
         case 8: return launch_cfg<8, ARGMAX>(L, grid, s);
         case 16: return launch_cfg<16, ARGMAX>(L, grid, s);

@@ -50,7 +50,7 @@ X, Y, WS = 0x40000, 0x50000, 0x60000
 
 
 @pytest.mark.parametrize("mutate,code", [
-    (dict(bits=3), EUNSUPPORTED), (dict(bits=2), EUNSUPPORTED), (dict(group=32), EUNSUPPORTED),
+    (dict(bits=5), EUNSUPPORTED), (dict(bits=1), EUNSUPPORTED), (dict(group=32), EUNSUPPORTED),
     (dict(k=100), EINVAL), (dict(k=0), EINVAL), (dict(n=0), EINVAL),
     (dict(tiles=0), EINVAL), (dict(tiles=0x10010), EINVAL),      # NULL, not 256-byte aligned
 ])
@@ -62,7 +62,7 @@ def test_qgemm_rejects_bad_weight(lib, mutate, code):
 
 
 @pytest.mark.parametrize("mutate,code", [
-    (dict(bits=3), EUNSUPPORTED), (dict(group=32), EUNSUPPORTED), (dict(k=100), EINVAL), (dict(n=0), EINVAL),
+    (dict(bits=6), EUNSUPPORTED), (dict(group=32), EUNSUPPORTED), (dict(k=100), EINVAL), (dict(n=0), EINVAL),
     (dict(codes=0), EINVAL), (dict(codes=0x10004), EINVAL), (dict(scales=0), EINVAL), (dict(biases=0x30001), EINVAL),
     (dict(bits=16), EINVAL),   # bf16 weights must not carry scales/biases
 ])
@@ -81,7 +81,9 @@ def test_pack_sizes_and_rejects_bad_destination(lib):
     assert lib.dspk_tiled_bytes(37, 320, 8) == 1 * 3 * 8704                  # ragged N and K padded
     assert lib.dspk_tiled_bytes(37, 320, 4) == 1 * 2 * 9216
     assert lib.dspk_tiled_bytes(0, 64, 8) == 0 and lib.dspk_tiled_bytes(64, 100, 8) == 0
-    assert lib.dspk_tiled_bytes(64, 64, 3) == 0
+    assert lib.dspk_tiled_bytes(151936, 2560, 2) == 2374 * 10 * 5120 == 151936 * 2560 * 5 // 16
+    assert lib.dspk_tiled_bytes(151936, 2560, 3) == 2374 * 10 * 7168 == 151936 * 2560 * 7 // 16
+    assert lib.dspk_tiled_bytes(64, 64, 5) == 0
     d = _src(n=64, k=128)
     need = lib.dspk_tiled_bytes(64, 128, 8)
     assert lib.dspk_qweight_pack(ctypes.byref(d), WS, need - 1, None) == EINVAL

@@ -16,7 +16,7 @@ from gpuutil import (assert_argmax_parity, assert_rows_close, dev_act, oracle_lo
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("bits", [8, 4, 16])
+@pytest.mark.parametrize("bits", [8, 4, 3, 2, 16])
 @pytest.mark.parametrize("v,h,m", [
     (8192, 2048, 6),      # the single-linear workload's vocabulary head
     (64, 64, 1), (37, 64, 5), (1000, 128, 16), (1000, 640, 17), (300, 256, 32), (5000, 2560, 12),

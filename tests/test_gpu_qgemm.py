@@ -22,7 +22,7 @@ def _case(bits, n, k, m, tag="qgemm"):
     return w, x
 
 
-@pytest.mark.parametrize("bits", [8, 4, 16])
+@pytest.mark.parametrize("bits", [8, 4, 3, 2, 16])
 @pytest.mark.parametrize("n,k,m", [
     (2048, 2048, 6),      # the single-linear workload (anchor + 5 drafts)
     (64, 64, 1), (37, 64, 3), (1000, 320, 16), (130, 1024, 24), (96, 512, 32),
@@ -136,40 +136,65 @@ def test_qgemm_full_shapes_sampled(model, m):
 
 
 def _tiles_by_definition(w) -> np.ndarray:
-    """The tiled layout written out from its definition in include/dspk.h and
-    the packing source: 64-column blocks, units of KU K elements, eight 1 KiB
-    slots of one 16-byte piece per lane, then (scale | bias << 16) dwords."""
+    """The tiled layout written out from its definition in the packing source:
+    64-column blocks, units of KU K elements, S 1 KiB slots of one 16-byte
+    piece per lane (S = 8; 4 for 2-bit, 6 for 3-bit), then (scale | bias <<
+    16) dwords.  2/3-bit pieces are built from the ground-truth codes."""
     bits, n, k = w.bits, w.n, w.k
-    ku = {8: 128, 4: 256, 16: 64}[bits]
+    ku = {8: 128, 4: 256, 3: 256, 2: 256, 16: 64}[bits]
+    ns = {2: 4, 3: 6}.get(bits, 8)
     gs = ku // 64
     nst, nb = -(-k // ku), -(-n // 64)
-    unit = 8192 + (0 if bits == 16 else 256 * gs)
+    unit = 1024 * ns + (0 if bits == 16 else 256 * gs)
     out = np.zeros(nb * nst * unit, np.uint8)
-    rowb = np.ascontiguousarray(w.codes).view(np.uint8).reshape(n, k * bits // 8)
+    if bits in (2, 3):
+        q = np.zeros((n, nst * ku), np.uint32)
+        q[:, :k] = w.codes_u8
+    else:
+        rowb = np.ascontiguousarray(w.codes).view(np.uint8).reshape(n, k * bits // 8)
+
+    def put_dwords(dst, dwords):
+        out[dst:dst + 4 * len(dwords)] = np.array(dwords, dtype=np.uint32).view(np.uint8)
+
     for b in range(nb):
         for u in range(nst):
             base = (b * nst + u) * unit
-            for i in range(8):
-                t, hi = i % 4, i // 4
-                for lane in range(64):
-                    c, j = lane % 16, lane // 16
+            for lane in range(64):
+                c, j = lane % 16, lane // 16
+                for t in range(4):
                     col = 64 * b + 16 * t + c
-                    dst = base + 1024 * i + 16 * lane
                     if col >= n:
                         continue
-                    if bits == 8:
-                        k0 = ku * u + 64 * hi + 16 * j
-                        if k0 < k:
-                            out[dst:dst + 16] = rowb[col, k0:k0 + 16]
-                    elif bits == 4:
-                        for half in range(2):
-                            k0 = ku * u + 64 * (2 * hi + half) + 16 * j
+                    if bits in (2, 3):
+                        # the lane's 16 codes of group g: K = ku*u + 64*g + 16*j + e
+                        grp = [q[col, ku * u + 64 * g + 16 * j: ku * u + 64 * g + 16 * j + 16] for g in range(4)]
+                        lo = [sum(int(cd & 3) << (2 * e) for e, cd in enumerate(grp[g])) for g in range(4)]
+                        put_dwords(base + 1024 * t + 16 * lane, lo)
+                        if bits == 3:
+                            for p in range(2):
+                                d = 0
+                                for r in range(2):
+                                    for e, cd in enumerate(grp[2 * p + r]):
+                                        bit = int(cd) >> 2
+                                        d |= bit << (8 * r + e if e < 8 else 16 + 8 * r + e - 8)
+                                put_dwords(base + 1024 * (4 + t // 2) + 16 * lane + 4 * (2 * (t % 2) + p), [d])
+                        continue
+                    for hi in range(2):
+                        i = 4 * hi + t
+                        dst = base + 1024 * i + 16 * lane
+                        if bits == 8:
+                            k0 = ku * u + 64 * hi + 16 * j
                             if k0 < k:
-                                out[dst + 8 * half:dst + 8 * half + 8] = rowb[col, k0 // 2:k0 // 2 + 8]
-                    else:
-                        k0 = ku * u + 16 * j + 8 * hi
-                        if k0 < k:
-                            out[dst:dst + 16] = rowb[col, 2 * k0:2 * k0 + 16]
+                                out[dst:dst + 16] = rowb[col, k0:k0 + 16]
+                        elif bits == 4:
+                            for half in range(2):
+                                k0 = ku * u + 64 * (2 * hi + half) + 16 * j
+                                if k0 < k:
+                                    out[dst + 8 * half:dst + 8 * half + 8] = rowb[col, k0 // 2:k0 // 2 + 8]
+                        else:
+                            k0 = ku * u + 16 * j + 8 * hi
+                            if k0 < k:
+                                out[dst:dst + 16] = rowb[col, 2 * k0:2 * k0 + 16]
             if bits == 16:
                 continue
             for c in range(16):
@@ -178,12 +203,11 @@ def _tiles_by_definition(w) -> np.ndarray:
                         col, gk = 64 * b + 16 * t + c, gs * u + g
                         if col < n and gk < k // 64:
                             d = int(w.scales[col, gk]) | (int(w.biases[col, gk]) << 16)
-                            o = base + 8192 + 16 * gs * c + 4 * (4 * g + t)
-                            out[o:o + 4] = np.array([d], dtype=np.uint32).view(np.uint8)
+                            put_dwords(base + 1024 * ns + 16 * gs * c + 4 * (4 * g + t), [d])
     return out
 
 
-@pytest.mark.parametrize("bits", [8, 4, 16])
+@pytest.mark.parametrize("bits", [8, 4, 3, 2, 16])
 @pytest.mark.parametrize("n,k", [(37, 320), (130, 1024), (64, 64)])
 def test_pack_layout_matches_definition(bits, n, k):
     """dspk_qweight_pack is a pure byte permutation: bit-exact against the
