@@ -24,6 +24,11 @@ Other workloads of the same path:
   --config qwen3-8b --batch 4 --sweep 6 --alpha 0.3,0.5,0.7,0.9
         four requests of six rows in one launch, greedy accept per request.
 
+  --prefill 2048 [--bits 4]
+        the prefill workload: one layer's seven projections over 2048 prompt
+        rows (dspk_qgemm_prefill) plus the head on the last row, in TFLOP/s
+        against the bf16 matrix-core peak.
+
 Printed: one JSON line with the whole-job weight-GB/s (weight bytes of every
 round / wall time), the per-width curve t(M)/t(1), the roofline of the
 dominant kernel (the vocabulary head), and the CPU oracle timed on a bounded
@@ -64,6 +69,9 @@ def parse():
     ap.add_argument("--presence", type=float, default=0.0, help="sampling: presence penalty")
     ap.add_argument("--frequency", type=float, default=0.0, help="sampling: frequency penalty")
     ap.add_argument("--history", type=int, default=4096, help="sampling with penalties: history length (tokens)")
+    ap.add_argument("--prefill", type=int, default=0,
+                    help="prefill workload instead: one layer's projections over this many prompt rows "
+                         "(dspk_qgemm_prefill) plus the head on the last row")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-s", type=float, default=20.0)
     ap.add_argument("--graph", action="store_true",
@@ -136,12 +144,121 @@ def measured_traffic():
         return None
 
 
+MFMA_BF16_PEAK_TFS = 2500.0   # MI355X dense bf16 matrix peak, published
+
+
+def prefill_bench(args):
+    """Prefill workload: one decoder layer's seven projections over P prompt
+    rows through dspk_qgemm_prefill, then the vocabulary head on the last row
+    only (dspk_lmhead_argmax with m = 1).  One step = one such pass; the
+    metric is MFMA throughput (the wide-row regime is bound by the matrix
+    cores, not by HBM)."""
+    import gc
+    import torch
+    from speculative_decoding_verify_dspk_amd import binding, inputs
+    binding.lib()
+    P = args.prefill
+    s = inputs.LAYER_SHAPES[args.config]
+    H, Q, KV, F, V = s["hidden"], s["q"], s["kv"], s["inter"], s["vocab"]
+    projs = [("q", Q, H), ("k", KV, H), ("v", KV, H), ("o", H, Q), ("gate", F, H), ("up", F, H), ("down", H, F)]
+    calls, ev_pairs, flops = [], [], 0
+    keep = []
+    for name, n, k in projs:
+        c, sc, bi = inputs.make_qweight_device(n, k, args.bits, args.config, "prefill", name)
+        w = binding.DeviceQWeight(n, k, args.bits, c, sc, bi)
+        x = inputs.make_activations_rowmajor_device(P, k, args.config, "prefill", name)
+        y = torch.empty((P, n), dtype=torch.float32, device="cuda")
+        calls.append((name, binding.prepare_qgemm_prefill(w, x, P, y)))
+        keep += [w, x, y, c, sc, bi]
+        flops += 2 * P * n * k
+    c, sc, bi = inputs.make_qweight_device(V, H, args.bits, args.config, "prefill", "head")
+    head = binding.DeviceQWeight(V, H, args.bits, c, sc, bi)
+    hlast = inputs.make_activations_device(1, H, args.config, "prefill", "last")
+    am = torch.empty((1,), dtype=torch.int32, device="cuda")
+    wsh = binding.alloc_workspace(binding.lmhead_workspace_bytes(V, 1))
+    head_call = binding.prepare_lmhead(head, hlast, 1, am, None, wsh)
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
+
+    def step(rec):
+        e = [ev() for _ in range(len(calls) + 2)] if rec is not None else None
+        if e: e[0].record(stream)
+        for i, (_, f) in enumerate(calls):
+            f()
+            if e: e[i + 1].record(stream)
+        head_call()
+        if e:
+            e[-1].record(stream)
+            rec.append(e)
+
+    for _ in range(args.warmup):
+        step(None)
+    gc.collect()
+    gc.freeze()
+    torch.cuda.synchronize()
+    recs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(recs)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {name: float(np.median([r[i].elapsed_time(r[i + 1]) for r in recs])) * 1e3
+           for i, (name, _) in enumerate(calls)}
+    head_us = float(np.median([r[-2].elapsed_time(r[-1]) for r in recs])) * 1e3
+    proj_us = sum(per.values())
+    # dominant kernel: the gate projection (largest), algorithmic flops / its mean launch time
+    gate_us = float(np.mean([r[4].elapsed_time(r[5]) for r in recs])) * 1e3
+    gate_flops = 2 * P * F * H
+    achieved = gate_flops / (gate_us * 1e-6) / 1e12
+    value = flops * args.steps / wall / 1e12
+    out = {
+        "metric": "prefill projection throughput (TFLOP/s) over a prompt",
+        "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.config} layer (7 projections) over {P} prompt rows + lm_head {V}x{H} "
+                               f"on the last row, {'bf16' if args.bits == 16 else str(args.bits) + '-bit g64'}"},
+        "per_projection_us": {k2: round(v2, 1) for k2, v2 in per.items()},
+        "projections_us": round(proj_us, 1), "last_row_head_us": round(head_us, 1),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
+                     "kernel": f"prefill_kernel<{args.bits}> (gate projection {F}x{H})",
+                     "avg_launch_us": round(gate_us, 2), "flops_per_launch": gate_flops},
+        "cpu_baseline": None if args.no_cpu_baseline else prefill_cpu_baseline(args.config, args.bits, P),
+        "device": torch.cuda.get_device_name(0), "host": platform.node(),
+    }
+    print(json.dumps(out))
+
+
+def prefill_cpu_baseline(model: str, bits: int, rows: int, budget_s: float = 15.0):
+    """The oracle's x . deq(W)^T on the gate projection's shape, on as many
+    32-row slices of the prompt as fit the budget, in TFLOP/s."""
+    import oracle
+    from speculative_decoding_verify_dspk_amd import inputs
+    s = inputs.LAYER_SHAPES[model]
+    n, k = s["inter"], s["hidden"]
+    w = inputs.make_qweight(n, k, bits, "cpu-baseline", model, "prefill-gate", keep_codes=False)
+    done = 0
+    t0 = time.perf_counter()
+    while done < rows and time.perf_counter() - t0 < budget_s:
+        x = inputs.make_activations(32, k, "cpu-baseline", model, "prefill", done)
+        oracle.qlinear(x, w.codes, w.scales, w.biases, bits, n, k)
+        done += 32
+    t = time.perf_counter() - t0
+    return {"value": round(2 * done * n * k / t / 1e12, 6), "unit": "TFLOP/s", "cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle", "sample": f"{done} of {rows} prompt rows through the {n}x{k} gate projection, "
+                                        f"{bits}-bit, in {t:.1f} s"}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only (the verify pass is not sharded); "
               "use --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.prefill > 0:
+        prefill_bench(args)
+        return
     import torch
     from speculative_decoding_verify_dspk_amd import binding, inputs
     from speculative_decoding_verify_dspk_amd.verify_round import VerifyStack

@@ -12,6 +12,7 @@
  * The library computes the data-parallel part of that round:
  *   dspk_qgemm_verify   - every projection of the target over the M = m + 1
  *                         rows, through affine group-quantised weights;
+ *   dspk_qgemm_prefill  - the same projection for many rows (a prompt);
  *   dspk_lmhead_argmax  - the vocabulary projection fused with the row argmax;
  *   dspk_accept_greedy  - longest matching prefix plus the target's token;
  *   dspk_accept_sample  - min(1, p/q) acceptance with residual resampling.
@@ -58,12 +59,15 @@ extern "C" {
  * One weight matrix W[n][k] (out features x in features) in its interchange
  * layout, the input of dspk_qweight_pack.
  *
- * bits 4 or 8 -- affine group quantisation, w[r][c] = s[r][c/64] * q[r][c] +
- *   b[r][c/64], the plain reading of the pages' "quantised" target weights
- *   with per-group parameters ("mlx-dspark" wiki summary, "Key techniques",
- *   custom kernels bullet):
- *     codes  : uint32[n][k*bits/32], codes packed LSB-first (code c of a row
- *              sits in word c/(32/bits) at bit bits*(c mod 32/bits)),
+ * bits 2, 3, 4 or 8 -- affine group quantisation, w[r][c] = s[r][c/64] *
+ *   q[r][c] + b[r][c/64], the plain reading of the pages' "quantised" target
+ *   weights with per-group parameters ("mlx-dspark" wiki summary, "Key
+ *   techniques", custom kernels bullet; the lower-bit rows are the pages'
+ *   ternary and 3-bit targets, "mlx-dspark 0.7.0"):
+ *     codes  : uint32[n][k*bits/32]: each row one LSB-first bit stream, code
+ *              c at stream bits bits*c .. bits*c + bits-1, bit i of the
+ *              stream in bit i%32 of word i/32 (so 32/bits codes per word
+ *              for 2, 4 and 8 bits; 3-bit codes may straddle two words);
  *              unsigned 0 .. 2^bits-1;
  *     scales : IEEE binary16 [n][k/64], row-major;
  *     biases : IEEE binary16 [n][k/64], row-major.
@@ -162,7 +166,7 @@ size_t dspk_qgemm_workspace_bytes(int32_t n, int32_t k, int32_t m);
  * bits (the K split is fixed by the shapes, not by scheduling).
  * Errors: DSPK_EINVAL (null or misaligned pointer, n < 1, k % 64, ldx/ldy,
  * m out of 1..32, workspace too small), DSPK_EUNSUPPORTED (bits not in
- * {4, 8, 16}, group != 64), DSPK_EDEVICE.
+ * {2, 3, 4, 8, 16}, group != 64), DSPK_EDEVICE.
  */
 int dspk_qgemm_verify(const dspk_tiled_weight *w, const uint16_t *x, int64_t ldx, int32_t m,
                       void *y, int32_t y_dtype, int64_t ldy,
@@ -181,6 +185,26 @@ int dspk_qgemm_verify_grouped(int32_t count, const dspk_tiled_weight *w,
                               const uint16_t *x, int64_t ldx, int32_t m,
                               void *const *y, int32_t y_dtype, const int64_t *ldy,
                               void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Prefill projection: the same y = x . deq(W)^T for many rows at once -- a
+ * prompt's tokens, the wide-row form of the pass ("mlx-dspark" wiki summary,
+ * "Key techniques": a weight group dequantised once and reused for all rows).
+ * Tiled for the matrix cores (128 x 128 output blocks); exact like the verify
+ * projection (codes contracted exactly, fp32 accumulation, one scale/bias
+ * update per group).  For a prompt's last row only, call dspk_lmhead_argmax
+ * with m = 1 on that row.
+ *
+ *   w   : tiled weight (any format).
+ *   x   : bf16 activations, ROW-major [m][ldx]: ldx >= k, ldx % 8 == 0,
+ *         16-byte aligned.
+ *   m   : rows, >= 1.
+ *   y   : output [m][ldy], y_dtype (DSPK_F32 | DSPK_BF16), ldy >= n.
+ * No workspace; deterministic.  Errors: DSPK_EINVAL (pointers, alignment,
+ * ldx/ldy, m < 1), DSPK_EUNSUPPORTED (bits, group), DSPK_EDEVICE.
+ */
+int dspk_qgemm_prefill(const dspk_tiled_weight *w, const uint16_t *x, int64_t ldx, int32_t m,
+                       void *y, int32_t y_dtype, int64_t ldy, void *stream);
 
 /* Workspace for dspk_lmhead_argmax (zero-filled before first use, left zeroed). */
 size_t dspk_lmhead_workspace_bytes(int32_t v, int32_t m);

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdspk.so")
-SOURCES = ["qgemm.hip", "pack.hip", "accept.hip", "api.cpp", "policy.cpp"]
+SOURCES = ["qgemm.hip", "prefill.hip", "pack.hip", "accept.hip", "api.cpp", "policy.cpp"]
 
 # Packed fp32 instructions are kept out of every HIP object (the compiler
 # would otherwise form them from ordinary float code).

@@ -153,6 +153,34 @@ int dspk_version(void) { return 200; }
 
 const char *dspk_last_error(void) { return g_err.c_str(); }
 
+int dspk_qgemm_prefill(const dspk_tiled_weight *w, const uint16_t *x, int64_t ldx, int32_t m, void *y,
+                       int32_t y_dtype, int64_t ldy, void *stream) {
+    const char *who = "dspk_qgemm_prefill";
+    int rc = check_tiled(w, who);
+    if (rc) return rc;
+    if (m < 1) return fail(DSPK_EINVAL, "%s: m=%d must be >= 1", who, m);
+    if (x == nullptr || !aligned(x, 16)) return fail(DSPK_EINVAL, "%s: x must be a 16-byte aligned device pointer", who);
+    if (ldx < w->k || ldx % 8) return fail(DSPK_EINVAL, "%s: ldx=%lld must be >= k and a multiple of 8", who,
+                                          (long long)ldx);
+    if (y_dtype != DSPK_F32 && y_dtype != DSPK_BF16) return fail(DSPK_EINVAL, "%s: bad y_dtype", who);
+    if (y == nullptr || !aligned(y, y_dtype == DSPK_F32 ? 4 : 2) || ldy < w->n)
+        return fail(DSPK_EINVAL, "%s: y must be aligned with ldy >= n", who);
+    dspk::PrefillArgs A;
+    A.tiles = w->tiles;
+    A.n = w->n;
+    A.k = w->k;
+    A.nst = (w->k + dspk::tile_k(w->bits) - 1) / dspk::tile_k(w->bits);
+    A.nblocks = (w->n + dspk::kBlockCols - 1) / dspk::kBlockCols;
+    if ((A.nblocks + 1) / 2 > 65535) return fail(DSPK_EINVAL, "%s: n=%d too large for one launch", who, w->n);
+    A.x = x;
+    A.ldx = ldx;
+    A.m = m;
+    A.y = y;
+    A.ldy = ldy;
+    A.y_bf16 = y_dtype == DSPK_BF16;
+    return launch_result(dspk::launch_prefill(A, w->bits, (hipStream_t)stream), who);
+}
+
 size_t dspk_tiled_bytes(int32_t n, int32_t k, int32_t bits) { return dspk::tiled_bytes(n, k, bits); }
 
 int dspk_qweight_pack(const dspk_qweight *w, void *tiles, size_t tiles_bytes, void *stream) {

@@ -82,6 +82,20 @@ struct GemmLaunch {
     uint32_t *done;           // arrival counter over workgroups
 };
 
+// One prefill projection (many rows, row-major activations).
+struct PrefillArgs {
+    const void *tiles;        // tiled weight
+    int32_t n, k, nst;        // columns, inputs, units per 64-column block
+    int32_t nblocks;          // 64-column blocks
+    const uint16_t *x;        // bf16 rows [m][ldx]
+    int64_t ldx;
+    int32_t m;
+    void *y;                  // [m][ldy], fp32 or bf16
+    int64_t ldy;
+    int32_t y_bf16;
+};
+hipError_t launch_prefill(const PrefillArgs &a, int bits, hipStream_t s);
+
 // Launch plan of one (possibly grouped) projection call (host side).
 struct GemmPlan {
     int32_t nst, nq, quads, grid, total_cg;

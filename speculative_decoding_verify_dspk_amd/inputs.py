@@ -273,6 +273,15 @@ def make_qweight_device(n: int, k: int, bits: int, *labels):
     return words, sc.to(torch.float16).view(torch.int16), bi.to(torch.float16).view(torch.int16)
 
 
+def make_activations_rowmajor_device(m: int, k: int, *labels):
+    """bf16 N(0, 1) rows on the GPU (int16 bit patterns), row-major [m][k]:
+    the prefill projection's layout."""
+    import torch
+    g = device_generator(*labels, m, k)
+    a = torch.empty((m, k), dtype=torch.float32, device="cuda").normal_(0.0, 1.0, generator=g)
+    return a.to(torch.bfloat16).view(torch.int16)
+
+
 def make_activations_device(m: int, k: int, *labels):
     """bf16 N(0, 1) rows on the GPU (int16 bit patterns), in the library's
     chunk-major layout ``[K/8][M][8]`` (independent draws, so the layout does

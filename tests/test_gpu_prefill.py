@@ -1,0 +1,101 @@
+"""GPU parity of dspk_qgemm_prefill (the wide-row projection) against the
+oracle's x . deq(W)^T (through the C ABI).
+
+Tolerance: per-row normwise relative error <= 2e-3 (the contract), as for the
+verify projection.  Shapes: ragged rows (not a multiple of the 128-row block)
+and columns (not a multiple of 64, an odd number of 64-column blocks), the
+smallest K, a short last K unit, padded leading dimensions, bf16 output,
+every weight format; at a full projection shape with 2048 rows, sampled rows.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from speculative_decoding_verify_dspk_amd import binding, inputs
+from gpuutil import assert_rows_close, dev_u16, torch
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill(w, x_bits, m, ldx=None, ldy=None, out_bf16=False, dw=None):
+    t = torch()
+    dw = dw or binding.DeviceQWeight.upload(w)
+    k = w.k
+    ldx = ldx or k
+    xp = np.zeros((m, ldx), np.uint16)
+    xp[:, :k] = x_bits
+    x = dev_u16(xp)
+    ldy = ldy or w.n
+    y = t.full((m, ldy), -7, dtype=t.int16 if out_bf16 else t.float32, device="cuda")
+    binding.qgemm_prefill(dw, x, m, y)
+    t.cuda.synchronize()
+    r = y.cpu().numpy()
+    assert (r[:, w.n:] == -7).all(), "columns past n were written"
+    r = r[:, :w.n]
+    if out_bf16:
+        r = inputs.bf16_bits_to_f32(np.ascontiguousarray(r).view(np.uint16))
+    return r
+
+
+@pytest.mark.parametrize("bits", [8, 4, 3, 2, 16])
+@pytest.mark.parametrize("n,k,m", [
+    (64, 64, 1), (37, 320, 130), (200, 1024, 300), (130, 2560, 129), (520, 4160, 64), (1000, 512, 257),
+])
+def test_prefill_matches_oracle(bits, n, k, m):
+    print(f"prefill bits={bits} n={n} k={k} m={m}", flush=True)
+    w = inputs.make_qweight(n, k, bits, "prefill", n, k)
+    x = inputs.make_activations(m, k, "prefill", m, k)
+    ref = oracle.qlinear(x, w.codes, w.scales, w.biases, bits, n, k)
+    worst = assert_rows_close(run_prefill(w, x, m), ref, what=f"bits={bits} n={n} k={k} m={m}")
+    print(f"  worst row normwise error {worst:.2e}")
+
+
+def test_prefill_padded_strides_and_bf16_output():
+    n, k, m = 300, 640, 200
+    w = inputs.make_qweight(n, k, 8, "prefill-ld")
+    x = inputs.make_activations(m, k, "prefill-ld")
+    ref = oracle.qlinear(x, w.codes, w.scales, w.biases, 8, n, k)
+    assert_rows_close(run_prefill(w, x, m, ldx=k + 24, ldy=n + 5), ref, what="padded")
+    got = run_prefill(w, x, m, out_bf16=True)
+    # bf16 output: the fp32 result rounded once (<= 2^-9 relative per element)
+    assert_rows_close(got, ref, rtol=2e-3 + 2 ** -8, what="bf16 out")
+
+
+def test_prefill_deterministic():
+    t = torch()
+    n, k, m = 700, 2560, 300
+    w = inputs.make_qweight(n, k, 4, "prefill-det")
+    x = inputs.make_activations(m, k, "prefill-det")
+    dw = binding.DeviceQWeight.upload(w)
+    a = run_prefill(w, x, m, dw=dw)
+    b = run_prefill(w, x, m, dw=dw)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_prefill_full_shape_sampled_rows(bits):
+    """Qwen3-4B gate projection (9728 x 2560) over 2048 prompt rows on the
+    device; the oracle recomputes 12 sampled rows in full."""
+    t = torch()
+    n, k, m = 9728, 2560, 2048
+    w = inputs.make_qweight(n, k, bits, "prefill-full")
+    x = inputs.make_activations(m, k, "prefill-full")
+    got = run_prefill(w, x, m)
+    rows = np.unique(np.concatenate([[0, 127, 128, m - 1], np.random.default_rng(3).integers(0, m, 8)]))
+    ref = oracle.qlinear(x[rows], w.codes, w.scales, w.biases, bits, n, k)
+    assert_rows_close(got[rows], ref, what=f"bits={bits} sampled rows")
+    assert np.isfinite(got).all()
+
+
+def test_prefill_rejects_bad_arguments():
+    t = torch()
+    w = inputs.make_qweight(64, 128, 8, "prefill-bad")
+    dw = binding.DeviceQWeight.upload(w)
+    x = t.zeros((4, 128), dtype=t.int16, device="cuda")
+    y = t.zeros((4, 64), dtype=t.float32, device="cuda")
+    with pytest.raises(binding.DspkError):
+        binding.qgemm_prefill(dw, x, 0, y)
+    with pytest.raises(binding.DspkError):
+        binding.qgemm_prefill(dw, t.zeros((4, 120), dtype=t.int16, device="cuda"), 4, y)   # ldx < k
+    with pytest.raises(binding.DspkError):
+        binding.qgemm_prefill(dw, t.zeros((4, 132), dtype=t.int16, device="cuda"), 4, y)   # ldx % 8
