@@ -123,11 +123,12 @@ def cpu_baseline(model: str, bits: int, m: int, budget_s: float):
 
 def measured_traffic():
     """HBM bytes per launch of the head kernel from the committed hardware-
-    counter summary, if it was taken on the current kernel source (else None)."""
+    counter summary, if it was taken on the current kernel sources (else None)."""
     import hashlib
     here = os.path.dirname(os.path.abspath(__file__))
     summary = os.path.join(here, "profiles", "vocab_head_traffic.txt")
-    src = os.path.join(here, "speculative_decoding_verify_dspk_amd", "csrc", "qgemm.hip")
+    csrc = os.path.join(here, "speculative_decoding_verify_dspk_amd", "csrc")
+    srcs = [os.path.join(csrc, f) for f in ("qgemm.hip", "decode.h", "dspk_internal.h")]
     if not os.path.exists(summary):
         return None
     kv = {}
@@ -135,7 +136,7 @@ def measured_traffic():
         if "=" in line and not line.startswith("#"):
             k, v = line.strip().split("=", 1)
             kv[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    sha = hashlib.sha256(b"".join(open(f, "rb").read() for f in srcs)).hexdigest()
     if kv.get("kernel_source_sha256") != sha:
         return None
     try:

@@ -20,7 +20,8 @@ import os
 import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SRC = os.path.join(PKG, "csrc", "qgemm.hip")
+# sources of the head kernel (their concatenation is hashed)
+KERNEL_SRCS = [os.path.join(PKG, "csrc", f) for f in ("qgemm.hip", "decode.h", "dspk_internal.h")]
 COPY_BYTES = 256 << 20          # the calibration copy that bench.py --calibrate runs
 
 
@@ -75,7 +76,7 @@ def traffic(fetch_csv: str, write_csv: str, out: str, cmd_fetch: str, cmd_write:
         # bytes per counted KiB, from the copy that reads and writes COPY_BYTES once
         factor = COPY_BYTES / copy
         res[counter] = (sum(head) / len(head), factor)
-    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    sha = hashlib.sha256(b"".join(open(f, "rb").read() for f in KERNEL_SRCS)).hexdigest()
     f_kib, f_fac = res["FETCH_SIZE"]
     w_kib, w_fac = res["WRITE_SIZE"]
     lines = [
