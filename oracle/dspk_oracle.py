@@ -295,11 +295,18 @@ def choose_cap(verify_us, draft_us, alpha: float) -> tuple[int, float]:
     at cap c (none at c = 0) ("mlx-dspark 0.7.0", "The Apple-Silicon
     speedup ceiling": tok/s = A / (drafter + overhead + slope * C); "Tuning":
     the cap is chosen from the measured curves).  Ties keep the smaller cap;
-    cap 0 means speculation is parked.  Returns (cap, tokens per us)."""
+    cap 0 means speculation is parked.  Returns (cap, tokens per us).
+
+    A narrower verify can always run as a wider one (the extra rows are
+    padding and change no commit), so the verify cost of width w is taken as
+    the least measured cost at width w or above: measurement noise that
+    makes a wider pass look cheaper than a narrower one cannot, by itself,
+    select a longer cap."""
     n = len(verify_us)
     best, best_rate = 0, None
     for c in range(n):
-        cost = float(verify_us[c]) + (float(draft_us[c]) if (draft_us is not None and c > 0) else 0.0)
+        verify = min(float(t) for t in verify_us[c:])
+        cost = verify + (float(draft_us[c]) if (draft_us is not None and c > 0) else 0.0)
         rate = expected_committed(c, alpha) / cost
         if best_rate is None or rate > best_rate:
             best, best_rate = c, rate

@@ -41,10 +41,16 @@ extern "C" {
 int32_t dspk_choose_cap(const double *verify_us, const double *draft_us, int32_t n, double alpha,
                         double *tokens_per_us) {
     if (!valid_curve(verify_us, draft_us, n) || !(alpha >= 0.0 && alpha <= 1.0)) return DSPK_EINVAL;
+    // Verify cost of width c + 1: the least measured cost at that width or
+    // wider, since a narrower pass can always run as a wider one with padding
+    // rows (so noise cannot make a longer cap look cheaper than a shorter one).
+    double envelope[DSPK_MAX_ROWS];
+    envelope[n - 1] = verify_us[n - 1];
+    for (int c = n - 2; c >= 0; --c) envelope[c] = fmin(verify_us[c], envelope[c + 1]);
     int best = 0;
     double best_rate = 0.0;
     for (int c = 0; c < n; ++c) {
-        const double cost = verify_us[c] + (c > 0 && draft_us != nullptr ? draft_us[c] : 0.0);
+        const double cost = envelope[c] + (c > 0 && draft_us != nullptr ? draft_us[c] : 0.0);
         const double rate = expected_tokens(c, alpha) / cost;
         if (c == 0 || rate > best_rate) {   // ties keep the smaller cap
             best = c;

@@ -31,6 +31,11 @@ def test_choose_cap_hand_cases():
     assert oracle.choose_cap([10, 11, 12, 30], None, 0.8) == (2, pytest.approx(2.44 / 12))
     # no acceptance: every draft only costs -> parked
     assert oracle.choose_cap([10, 11, 12], None, 0.0)[0] == 0
+    # a wider pass measured cheaper than a narrower one: width 1 costs at most
+    # width 2's 9 us, so with nothing accepted the round stays parked ...
+    assert oracle.choose_cap([10, 9, 12], None, 0.0) == (0, pytest.approx(1 / 9))
+    # ... and a flat-then-cheaper tail prices every narrower width at 8 us
+    assert oracle.choose_cap([10, 11, 8, 40], None, 0.1) == (2, pytest.approx(1.11 / 8))
     # a flat verify curve: the widest round wins for any alpha > 0
     assert oracle.choose_cap([5, 5, 5, 5, 5], None, 0.2)[0] == 4
     # drafter time per round: 1.5/(11+4) = 0.1 ties with 1/10 -> the smaller cap (parked)
@@ -52,6 +57,8 @@ def test_abi_matches_oracle_on_random_curves(lib):
     for _ in range(2000):
         n = int(g.integers(1, 33))
         verify = np.cumsum(g.uniform(0.5, 20.0, n)) + g.uniform(1, 50)
+        if g.random() < 0.5:   # measurement noise: not monotone in width
+            verify = verify * g.uniform(0.7, 1.3, n)
         draft = np.concatenate([[0.0], g.uniform(0, 30, n - 1)]) if g.random() < 0.5 else None
         alpha = float(g.uniform(0, 1))
         want, rate = oracle.choose_cap(verify, draft, alpha)
