@@ -139,7 +139,9 @@ int dspk_qweight_pack(const dspk_qweight *w, void *tiles, size_t tiles_bytes, vo
 
 /*
  * Workspace for dspk_qgemm_verify: bytes needed for a weight of n x k read by
- * m rows, any format (never 0: every call needs one).  It holds arrival counters and the
+ * m rows or fewer, any format (never 0: every call needs one).  A workspace of
+ * this size serves every width 1..m, so one buffer can follow a varying draft
+ * length.  It holds arrival counters and the
  * partial sums of K-split column blocks.  The workspace must be zero-filled
  * before its FIRST use; every completed call leaves its counters at zero
  * again, so it can be reused as is by calls ordered on one stream.
@@ -206,7 +208,8 @@ int dspk_qgemm_verify_grouped(int32_t count, const dspk_tiled_weight *w,
 int dspk_qgemm_prefill(const dspk_tiled_weight *w, const uint16_t *x, int64_t ldx, int32_t m,
                        void *y, int32_t y_dtype, int64_t ldy, void *stream);
 
-/* Workspace for dspk_lmhead_argmax (zero-filled before first use, left zeroed). */
+/* Workspace for dspk_lmhead_argmax at m rows or fewer, any hidden size and
+ * format (zero-filled before first use, left zeroed). */
 size_t dspk_lmhead_workspace_bytes(int32_t v, int32_t m);
 
 /*

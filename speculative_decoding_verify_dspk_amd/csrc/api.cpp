@@ -198,11 +198,14 @@ int dspk_qweight_pack(const dspk_qweight *w, void *tiles, size_t tiles_bytes, vo
 
 size_t dspk_qgemm_workspace_bytes(int32_t n, int32_t k, int32_t m) {
     if (n < 1 || k < DSPK_GROUP || k % DSPK_GROUP || m < 1 || m > DSPK_MAX_ROWS) return 0;
+    // Enough for every width up to m: narrower launches use more workgroups
+    // (two per CU up to 16 rows, one above), so both row-tile classes count.
     size_t most = 0;
-    for (int bits : {2, 3, 4, 8, 16}) {   // the plan depends on the format only through the stage depth
-        const size_t b = dspk::plan_gemm(1, &n, k, m, bits, false).ws_bytes;
-        most = b > most ? b : most;
-    }
+    for (int mm : {m < 16 ? m : 16, m})
+        for (int bits : {2, 3, 4, 8, 16}) {   // the plan depends on the format only through the stage depth
+            const size_t b = dspk::plan_gemm(1, &n, k, mm, bits, false).ws_bytes;
+            most = b > most ? b : most;
+        }
     return most;
 }
 
@@ -222,8 +225,10 @@ int dspk_qgemm_verify_grouped(int32_t count, const dspk_tiled_weight *w, const u
 
 size_t dspk_lmhead_workspace_bytes(int32_t v, int32_t m) {
     if (v < 1 || m < 1 || m > DSPK_MAX_ROWS) return 0;
-    // the largest plan over hidden sizes: one workgroup per CU holds partial sums
-    return dspk::plan_gemm(1, &v, 1 << 20, m, 8, true).ws_bytes;
+    // the largest plan over hidden sizes and over every width up to m
+    const size_t a = dspk::plan_gemm(1, &v, 1 << 20, m < 16 ? m : 16, 8, true).ws_bytes;
+    const size_t b = dspk::plan_gemm(1, &v, 1 << 20, m, 8, true).ws_bytes;
+    return a > b ? a : b;
 }
 
 int dspk_lmhead_argmax(const dspk_tiled_weight *w, const uint16_t *h, int64_t ldh, int32_t m, int32_t *argmax,

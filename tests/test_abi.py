@@ -119,6 +119,20 @@ def test_qgemm_workspace_contract(lib):
     assert rc == EINVAL
 
 
+def test_workspace_for_m_rows_serves_every_narrower_width(lib):
+    # one buffer follows a varying draft length: the size queried at the
+    # widest width is enough at every width below it (narrower launches run
+    # more workgroups, so this is not automatic)
+    for n, k in ((151936, 5120), (5120, 17408), (1024, 5120), (2560, 9728)):
+        for m in (1, 8, 16, 17, 24, 32):
+            big = lib.dspk_qgemm_workspace_bytes(n, k, m)
+            assert all(lib.dspk_qgemm_workspace_bytes(n, k, mm) <= big for mm in range(1, m + 1))
+    for v in (151936, 8192, 1000):
+        for m in (1, 16, 17, 32):
+            big = lib.dspk_lmhead_workspace_bytes(v, m)
+            assert all(lib.dspk_lmhead_workspace_bytes(v, mm) <= big for mm in range(1, m + 1))
+
+
 def test_grouped_rejects_mismatch(lib):
     ds = (binding.TiledDesc * 2)(_desc(k=128), _desc(k=256))
     ys = (ctypes.c_void_p * 2)(Y, Y)
