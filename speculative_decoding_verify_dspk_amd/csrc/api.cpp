@@ -96,6 +96,7 @@ void fill_plan(dspk::GemmLaunch &L, const dspk::GemmPlan &pl, const uint16_t *x,
     L.nq = pl.nq;
     L.quads = pl.quads;
     L.total_cg = pl.total_cg;
+    L.pairs = pl.pairs;
 }
 
 int qgemm_common(int32_t count, const dspk_tiled_weight *w, const uint16_t *x, int64_t ldx, int32_t m,

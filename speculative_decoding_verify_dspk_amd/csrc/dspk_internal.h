@@ -72,6 +72,7 @@ struct GemmLaunch {
     int32_t total_cg;         // blocks of the launch
     int32_t y_bf16;           // store y as bf16 instead of fp32
     // workspace
+    int32_t pairs;            // > 0: workgroups b and b + pairs share a CU (weighted split), else 0
     uint32_t *counters;       // [total_cg][4] arrival counters of split blocks
     float *partial;           // [grid][2][4][MT][64][4] partial sums of split blocks
     // vocabulary-head epilogue (argmax kernel only)
@@ -99,6 +100,7 @@ hipError_t launch_prefill(const PrefillArgs &a, int bits, hipStream_t s);
 // Launch plan of one (possibly grouped) projection call (host side).
 struct GemmPlan {
     int32_t nst, nq, quads, grid, total_cg;
+    int32_t pairs;            // see GemmLaunch::pairs
     bool fits;                // quads * grid < 2^31 (the kernel's index range)
     size_t off_counters, off_keys, off_partial, ws_bytes;
 };

@@ -44,6 +44,7 @@ namespace {
 using namespace dec;
 
 constexpr int NT = kTilesPerWave;
+constexpr uint32_t kSlots = 2;      // whole-block sums in flight per workgroup
 
 // Total order used for the argmax: larger value first, NaN above everything,
 // -0 equal to +0, then the smaller column.  0 is below every real key.
@@ -108,6 +109,37 @@ __device__ __forceinline__ int quad_owner(int quads, int groups, int q) {
     return (int)(((uint32_t)(q + 1) * (uint32_t)groups + (uint32_t)quads - 1u) / (uint32_t)quads) - 1;
 }
 
+// Two workgroups per CU: the dispatcher places workgroups b and b + pairs on
+// one CU, and the one dispatched first (b) is served ahead of the other by the
+// memory pipeline, so with equal shares the later one finishes well after it
+// (measured: 58 vs 70 us medians on the 151936 x 2560 head) and runs its tail
+// at half the CU's loads in flight.  Each CU's pair therefore gets one equal
+// range, which the earlier workgroup splits kLeadNum / kLeadDen : rest with
+// the later one.  Ranks number the workgroups in memory order (pair p: ranks
+// 2p, 2p + 1); with pairs == 0 the split is plain equal.
+#ifndef DSPK_LEAD_NUM
+#define DSPK_LEAD_NUM 10
+#endif
+constexpr uint32_t kLeadNum = DSPK_LEAD_NUM, kLeadDen = 16;
+static_assert(2 * kLeadNum >= kLeadDen && 3 * kLeadNum < 2 * kLeadDen,
+              "a pair's range of >= 2 quads must give both workgroups a non-empty piece");
+__device__ __forceinline__ int split_point(int a, int b) {
+    return a + (int)(((uint32_t)(b - a) * kLeadNum) / kLeadDen);
+}
+__device__ __forceinline__ int range_begin(int quads, int grid, int pairs, int rank) {
+    if (pairs == 0) return quad_begin(quads, grid, rank);
+    const int p = rank >> 1;
+    const int a = quad_begin(quads, pairs, p);
+    if ((rank & 1) == 0) return a;
+    return split_point(a, quad_begin(quads, pairs, p + 1));
+}
+__device__ __forceinline__ int range_owner(int quads, int grid, int pairs, int q) {
+    if (pairs == 0) return quad_owner(quads, grid, q);
+    const int p = quad_owner(quads, pairs, q);
+    const int s = split_point(quad_begin(quads, pairs, p), quad_begin(quads, pairs, p + 1));
+    return 2 * p + (q >= s ? 1 : 0);
+}
+
 __device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) {
     return a > b ? a : b;
 }
@@ -128,6 +160,13 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT)) void qgemm_kernel(const 
         } tail;
     } sh;
     auto &cbuf = sh.cbuf;
+    // Whole-block sums without a workgroup barrier: each wave posts its four
+    // tiles into a slot and counts itself in with an LDS atomic; the fourth
+    // wave to arrive adds the posts in wave order and finishes the block.
+    // A slot word holds (use << 3) | arrivals; a wave waits for the slot's
+    // previous use to be finished (use advanced) before posting into it.
+    __shared__ f32x4 slots[kSlots][kWavesPerWG][NT][MT][kWave];
+    __shared__ uint32_t slot_word[kSlots];
     auto &red = sh.tail.red;
     int &s_flag = sh.tail.flag;
 
@@ -139,16 +178,22 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT)) void qgemm_kernel(const 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15, j = lane >> 4;
-    const int bid = blockIdx.x;
     const int GRID = gridDim.x;
+    const int PAIRS = KL->pairs;
+    // rank of this workgroup in memory order (indexes its range and its
+    // partial-sum slots)
+    const int bid = PAIRS == 0 ? (int)blockIdx.x
+                               : ((int)blockIdx.x < PAIRS ? 2 * (int)blockIdx.x : 2 * ((int)blockIdx.x - PAIRS) + 1);
     const int QU = KL->quads;                 // quads of the launch
     const int NQ = KL->nq;                    // quads per block
     const int NST = KL->nst;                  // units per block
     const int LASTW = NST - 4 * (NQ - 1);     // waves with a unit in a block's last quad (1..4)
     const int K = KL->k;
     const int G = K >> 6;
-    const int Q0 = quad_begin(QU, GRID, bid), Q1 = quad_begin(QU, GRID, bid + 1);
+    const int Q0 = range_begin(QU, GRID, PAIRS, bid), Q1 = range_begin(QU, GRID, PAIRS, bid + 1);
     const int M = KL->m;
+    if (tid < kSlots) slot_word[tid] = 0u;
+    __syncthreads();
 
     // global block -> weight index
     auto weight_of = [&](int gb) __attribute__((always_inline)) {
@@ -333,9 +378,9 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT)) void qgemm_kernel(const 
 
     // Final values of this wave's tile (columns 16*w .. 16*w+15 of block cb):
     // store them, or fold them into the argmax.
-    auto finish_tile = [&](int pi, int cb, const f32x4 (&z)[MT]) __attribute__((always_inline)) {
+    auto finish_tile = [&](int pi, int cb, int t, const f32x4 (&z)[MT]) __attribute__((always_inline)) {
         const GemmProblem &P = KL->p[pi];
-        const int n = cb * kBlockCols + 16 * w + c;
+        const int n = cb * kBlockCols + 16 * t + c;
         const int N = P.n;
         if (n >= N) return;
 #pragma unroll
@@ -361,10 +406,56 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT)) void qgemm_kernel(const 
     // End of the workgroup's piece [a, b) of one block: add the four waves'
     // sums through LDS in wave order (wave w keeps tile w), then finish the
     // tile, or hand the piece to the last workgroup that works on the block.
+    uint32_t seq = 0;     // whole blocks closed so far (the same count in every wave)
     auto close_piece = [&](int a, int b) __attribute__((always_inline)) {
         const int gb = a / NQ;
         const int pi = weight_of(gb);
         const int cb = gb - KL->p[pi].cg_begin;
+        if (a == gb * NQ && b == gb * NQ + NQ) {
+            const uint32_t sl = seq % kSlots, use = seq / kSlots;
+            ++seq;
+            // the slot's previous use has been read out (its last wave moved
+            // it on); waves are at most kSlots blocks apart, so this ends.
+            // The bound only guards against a broken invariant: a wave never
+            // spins forever (results would then be wrong, not the GPU hung).
+            for (int spin = 0; spin < (1 << 20); ++spin) {
+                if ((__hip_atomic_load(&slot_word[sl], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >> 3) == use)
+                    break;
+                __builtin_amdgcn_s_sleep(1);
+            }
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) lds_put(&slots[sl][w][t][mt][lane], y[t][mt]);
+            // LDS operations of a wave complete in order: the posts land before the count
+            __builtin_amdgcn_s_waitcnt(0xc07f);           // lgkmcnt(0) only
+            asm volatile("" ::: "memory");
+            // one arrival per wave: a single lane counts the wave in
+            uint32_t old = 0;
+            if (lane == 0)
+                old = __hip_atomic_fetch_add(&slot_word[sl], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            old = (uint32_t)__builtin_amdgcn_readfirstlane((int)old);
+            if ((old & 7u) != kWavesPerWG - 1) return;
+            asm volatile("" ::: "memory");
+            // one tile at a time (few registers next to the ring)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                f32x4 zt[MT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    zt[mt] = lds_get(&slots[sl][0][t][mt][lane]);
+#pragma unroll
+                    for (int q = 1; q < kWavesPerWG; ++q) zt[mt] += lds_get(&slots[sl][q][t][mt][lane]);
+                }
+                finish_tile(pi, cb, t, zt);
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);           // every read of the slot is done
+            asm volatile("" ::: "memory");
+            if (lane == 0)
+                __hip_atomic_store(&slot_word[sl], (use + 1) << 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            return;
+        }
         f32x4 z[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -382,10 +473,6 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT)) void qgemm_kernel(const 
             }
         }
         const int bq0 = gb * NQ, bq1 = bq0 + NQ;
-        if (a == bq0 && b == bq1) {
-            finish_tile(pi, cb, z);
-            return;
-        }
         // publish: slot 0 for the workgroup's first piece, 1 for its last
         const int side = a == Q0 ? 0 : 1;
         float *mine = KL->partial + (((int64_t)bid * 2 + side) * kWavesPerWG + w) * (MT * kWave * 4);
@@ -394,7 +481,7 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT)) void qgemm_kernel(const 
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) store_agent(mine + (mt * kWave + lane) * 4 + r4, z[mt][r4]);
         wait_vm_all();
-        const int wf = quad_owner(QU, GRID, bq0), wl = quad_owner(QU, GRID, bq1 - 1);
+        const int wf = range_owner(QU, GRID, PAIRS, bq0), wl = range_owner(QU, GRID, PAIRS, bq1 - 1);
         uint32_t ticket = 0;
         uint32_t *ctr = KL->counters + (int64_t)gb * kWavesPerWG + w;
         if (lane == 0) ticket = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -404,7 +491,7 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT)) void qgemm_kernel(const 
         // flight (few: the ring's registers are live here).  Every workgroup after wf starts inside the block (its piece
         // is its first, slot 0); wf's piece is its first only if its range
         // starts at the block start.
-        const int wf_side = quad_begin(QU, GRID, wf) >= bq0 ? 0 : 1;
+        const int wf_side = range_begin(QU, GRID, PAIRS, wf) >= bq0 ? 0 : 1;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) z[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int v0 = wf; v0 <= wl; v0 += XB) {
@@ -432,7 +519,7 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT)) void qgemm_kernel(const 
             }
         }
         if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        finish_tile(pi, cb, z);
+        finish_tile(pi, cb, w, z);
     };
 
     // Pieces not yet closed start at `open`; close every piece that ends at or
@@ -599,6 +686,8 @@ GemmPlan plan_gemm(int count, const int32_t *n, int32_t k, int32_t m, int bits, 
     const int64_t slots = (int64_t)kernel_occ(bits, mt) * device_cus();
     const int64_t grid = quads < slots ? quads : slots;
     p.grid = grid < 1 ? 1 : (int32_t)grid;
+    // a full grid of two workgroups per CU runs as CU pairs (weighted split)
+    p.pairs = (kernel_occ(bits, mt) == 2 && p.grid == 2 * device_cus()) ? device_cus() : 0;
     // the kernel splits quads with 32-bit products
     p.fits = quads * p.grid < ((int64_t)1 << 31);
     p.quads = p.fits ? (int32_t)quads : 0;
