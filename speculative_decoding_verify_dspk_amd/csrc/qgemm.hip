@@ -121,7 +121,9 @@ __device__ __forceinline__ int quad_owner(int quads, int groups, int q) {
 #define DSPK_LEAD_NUM 10
 #endif
 constexpr uint32_t kLeadNum = DSPK_LEAD_NUM, kLeadDen = 16;
-static_assert(2 * kLeadNum >= kLeadDen && 3 * kLeadNum < 2 * kLeadDen,
+// A pair's range has >= 2 quads (quads >= grid); floor(n * f) lies in
+// [1, n - 1] for every n >= 2 when 1/2 <= f < 1, so both pieces are non-empty.
+static_assert(2 * kLeadNum >= kLeadDen && kLeadNum < kLeadDen,
               "a pair's range of >= 2 quads must give both workgroups a non-empty piece");
 __device__ __forceinline__ int split_point(int a, int b) {
     return a + (int)(((uint32_t)(b - a) * kLeadNum) / kLeadDen);
