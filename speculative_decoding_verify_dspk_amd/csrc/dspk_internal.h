@@ -79,7 +79,7 @@ struct GemmLaunch {
     int32_t *argmax;
     float *logits;
     int64_t ldl;
-    unsigned long long *keys; // [grid][kMaxRows] per-workgroup row maxima
+    unsigned long long *keys; // [kMaxRows] row maxima over the grid (atomic max; cleared by the last workgroup)
     uint32_t *done;           // arrival counter over workgroups
 };
 

@@ -592,11 +592,14 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT)) void qgemm_kernel(const 
                 if (c == 0) red[w][16 * mt + 4 * j + r4] = b;
             }
         __syncthreads();
+        // The grid's row maxima accumulate in one key per row with 64-bit
+        // atomic max (exact and order-free, so deterministic); the last
+        // workgroup reads them, writes the ids and clears the keys.
         if (tid < M) {
             unsigned long long b = red[0][tid];
 #pragma unroll
             for (int qq = 1; qq < kWavesPerWG; ++qq) b = umax64(b, red[qq][tid]);
-            __hip_atomic_store(&KL->keys[(int64_t)bid * kMaxRows + tid], b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_max(&KL->keys[tid], b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         wait_vm_all();
         __syncthreads();
@@ -605,35 +608,10 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT)) void qgemm_kernel(const 
                      gridDim.x - 1;
         __syncthreads();
         if (!s_flag) return;
-        // last workgroup: maximum over all workgroups, 8 rows at a time
-        const int nwg = gridDim.x;
-        for (int m0 = 0; m0 < M; m0 += 8) {
-            unsigned long long b8[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) b8[i] = 0ull;
-            for (int g = tid; g < nwg; g += 256) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    if (m0 + i < M)
-                        b8[i] = umax64(b8[i], __hip_atomic_load(&KL->keys[(int64_t)g * kMaxRows + m0 + i],
-                                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) b8[i] = umax64(b8[i], __shfl_xor(b8[i], off));
-            __syncthreads();
-            if (lane == 0) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) red[w][i] = b8[i];
-            }
-            __syncthreads();
-            if (tid < 8 && m0 + tid < M) {
-                unsigned long long b = red[0][tid];
-#pragma unroll
-                for (int qq = 1; qq < kWavesPerWG; ++qq) b = umax64(b, red[qq][tid]);
-                KL->argmax[m0 + tid] = (int32_t)(0xffffffffu - (uint32_t)(b & 0xffffffffull));
-            }
+        if (tid < M) {
+            const unsigned long long b = __hip_atomic_load(&KL->keys[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            KL->argmax[tid] = (int32_t)(0xffffffffu - (uint32_t)(b & 0xffffffffull));
+            __hip_atomic_store(&KL->keys[tid], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         if (tid == 0) __hip_atomic_store(KL->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -697,7 +675,7 @@ GemmPlan plan_gemm(int count, const int32_t *n, int32_t k, int32_t m, int bits, 
     p.off_counters = off;
     off += ((size_t)blocks * kWavesPerWG * 4 + 255) / 256 * 256;
     p.off_keys = off;
-    if (argmax) off += (size_t)p.grid * kMaxRows * 8;
+    if (argmax) off += (size_t)kMaxRows * 8;            // one 64-bit key per row
     off = (off + 255) / 256 * 256;
     p.off_partial = off;
     off += (size_t)p.grid * 2 * kWavesPerWG * mt * kWave * 16;
