@@ -8,7 +8,9 @@ Workload (default): one Qwen3-4B-shaped decoder layer (q 4096x2560, k/v
 greedy acceptance of drafts that match the target's token with probability
 0.7 per position.  One step = one verify round at each width
 M = 1, 2, 4, 6, 8, 12, 16 (the verify-cost curve); each round is
-  4 projection launches per layer + head/argmax + accept + one D2H copy and sync,
+  4 projection launches per layer + head/argmax with the greedy acceptance in
+  its last workgroup (one launch; sampling rounds launch the accept kernels
+  after the head) + one D2H copy and sync,
 launched from the host with arguments marshalled once per width and weight
 copy (--graph replays HIP graphs of the same calls instead).
 
@@ -334,7 +336,15 @@ def main():
                                                       want_logits=sample)
             else:
                 layers, head = stack.prepare_round(B * m, cp, want_logits=sample, stream=stream)
-                prepared[(m, cp)] = (layers, head, accept_call(m, rounds_in[m]))
+                if sample:
+                    prepared[(m, cp)] = (layers, head, accept_call(m, rounds_in[m]))
+                else:
+                    # greedy: the head's last workgroup runs the acceptance
+                    # (dspk_lmhead_argmax_accept_greedy), no accept launch
+                    r = rounds_in[m]
+                    fused = binding.prepare_lmhead_accept_greedy(stack.heads[cp], stack.h, B, m, stack.argmax, None,
+                                                                 r["d"], r["alen"], r["com"], stack.ws_head, stream)
+                    prepared[(m, cp)] = (layers, fused, lambda: None)
 
     # the round's one device-to-host copy: destination views made once
     host_dst = {m: host_res[:B + B * m] for m in sweep}

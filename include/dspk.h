@@ -15,6 +15,7 @@
  *   dspk_qgemm_prefill  - the same projection for many rows (a prompt);
  *   dspk_lmhead_argmax  - the vocabulary projection fused with the row argmax;
  *   dspk_accept_greedy  - longest matching prefix plus the target's token;
+ *   dspk_lmhead_argmax_accept_greedy - the two calls above in one launch;
  *   dspk_accept_sample  - min(1, p/q) acceptance with residual resampling.
  *   dspk_accept_sample_ex - the same over penalised, top-k/top-p truncated distributions.
  *
@@ -232,6 +233,27 @@ size_t dspk_lmhead_workspace_bytes(int32_t v, int32_t m);
 int dspk_lmhead_argmax(const dspk_tiled_weight *w, const uint16_t *h, int64_t ldh, int32_t m,
                        int32_t *argmax, float *logits, int64_t ldl,
                        void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * A greedy round's head and acceptance in one launch: exactly the results of
+ * dspk_lmhead_argmax over m = b * m_rows rows followed by dspk_accept_greedy
+ * on its ids (same argmax, accept_len and committed), with the acceptance run
+ * by the head's last workgroup, so a greedy round needs no separate accept
+ * launch ("mlx-dspark" wiki summary, "Architecture": the drafts are compared
+ * with the target's own logits and the longest accepted prefix committed).
+ *
+ *   b, m_rows  : requests and rows per request, b * m_rows <= DSPK_MAX_ROWS;
+ *                request r owns rows r * m_rows .. r * m_rows + m_rows - 1
+ *   draft_ids  : int32 [b][m_rows - 1] (may be NULL when m_rows == 1)
+ *   accept_len : int32 [b] output;  committed : int32 [b][m_rows] output
+ * Other arguments are as in dspk_lmhead_argmax (argmax [b * m_rows] is still
+ * written).  Errors: as dspk_lmhead_argmax, and DSPK_EINVAL for the rows or
+ * the acceptance pointers.
+ */
+int dspk_lmhead_argmax_accept_greedy(const dspk_tiled_weight *w, const uint16_t *h, int64_t ldh, int32_t b,
+                                     int32_t m_rows, int32_t *argmax, float *logits, int64_t ldl,
+                                     const int32_t *draft_ids, int32_t *accept_len, int32_t *committed,
+                                     void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * Greedy acceptance for b requests of m_rows rows each ("mlx-dspark" wiki

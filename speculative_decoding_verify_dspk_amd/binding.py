@@ -90,6 +90,9 @@ def lib() -> ctypes.CDLL:
         "dspk_lmhead_workspace_bytes": (c_size_t, [c_int32, c_int32]),
         "dspk_lmhead_argmax": (c_int32, [P(TiledDesc), c_void_p, c_int64, c_int32, c_void_p, c_void_p,
                                          c_int64, c_void_p, c_size_t, c_void_p]),
+        "dspk_lmhead_argmax_accept_greedy": (c_int32, [P(TiledDesc), c_void_p, c_int64, c_int32, c_int32,
+                                                       c_void_p, c_void_p, c_int64, c_void_p, c_void_p,
+                                                       c_void_p, c_void_p, c_size_t, c_void_p]),
         "dspk_accept_greedy": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
                                          c_void_p]),
         "dspk_sample_workspace_bytes": (c_size_t, [c_int32, c_int32]),
@@ -287,6 +290,14 @@ def prepare_lmhead(w: DeviceQWeight, h, m: int, argmax, logits, workspace, strea
                     workspace.numel(), _stream(stream))
 
 
+def prepare_lmhead_accept_greedy(w: DeviceQWeight, h, b: int, m_rows: int, argmax, logits, draft_ids, accept_len,
+                                 committed, workspace, stream=None) -> Prepared:
+    return Prepared("dspk_lmhead_argmax_accept_greedy", ctypes.byref(w.desc), h.data_ptr(), _chunks(h, "h"), b,
+                    m_rows, argmax.data_ptr(), _ptr(logits), 0 if logits is None else _rows(logits, "logits"),
+                    _ptr(draft_ids), accept_len.data_ptr(), committed.data_ptr(), workspace.data_ptr(),
+                    workspace.numel(), _stream(stream))
+
+
 def prepare_accept_greedy(target_ids, draft_ids, b: int, m_rows: int, accept_len, committed,
                           stream=None) -> Prepared:
     return Prepared("dspk_accept_greedy", target_ids.data_ptr(), _ptr(draft_ids), b, m_rows, accept_len.data_ptr(),
@@ -370,6 +381,15 @@ def lmhead_argmax(w: DeviceQWeight, h, m: int, argmax, logits=None, workspace=No
     _check(lib().dspk_lmhead_argmax(ctypes.byref(w.desc), h.data_ptr(), _chunks(h, "h"), m, argmax.data_ptr(),
                                     _ptr(logits), ldl, _ptr(workspace),
                                     0 if workspace is None else workspace.numel(), _stream(stream)))
+
+
+def lmhead_argmax_accept_greedy(w: DeviceQWeight, h, b: int, m_rows: int, argmax, draft_ids, accept_len, committed,
+                                logits=None, workspace=None, stream=None) -> None:
+    ldl = 0 if logits is None else _rows(logits, "logits")
+    _check(lib().dspk_lmhead_argmax_accept_greedy(ctypes.byref(w.desc), h.data_ptr(), _chunks(h, "h"), b, m_rows,
+                                                  argmax.data_ptr(), _ptr(logits), ldl, _ptr(draft_ids),
+                                                  accept_len.data_ptr(), committed.data_ptr(), _ptr(workspace),
+                                                  0 if workspace is None else workspace.numel(), _stream(stream)))
 
 
 def accept_greedy(target_ids, draft_ids, b: int, m_rows: int, accept_len, committed, stream=None) -> None:

@@ -232,9 +232,10 @@ size_t dspk_lmhead_workspace_bytes(int32_t v, int32_t m) {
     return a > b ? a : b;
 }
 
-int dspk_lmhead_argmax(const dspk_tiled_weight *w, const uint16_t *h, int64_t ldh, int32_t m, int32_t *argmax,
-                       float *logits, int64_t ldl, void *workspace, size_t ws_bytes, void *stream) {
-    const char *who = "dspk_lmhead_argmax";
+static int lmhead_common(const char *who, const dspk_tiled_weight *w, const uint16_t *h, int64_t ldh, int32_t m,
+                         int32_t *argmax, float *logits, int64_t ldl, const int32_t *draft_ids, int32_t b,
+                         int32_t m_rows, int32_t *accept_len, int32_t *committed, void *workspace, size_t ws_bytes,
+                         void *stream) {
     int rc = check_tiled(w, who);
     if (rc) return rc;
     rc = check_rows(h, ldh, m, w->k, who);
@@ -259,11 +260,37 @@ int dspk_lmhead_argmax(const dspk_tiled_weight *w, const uint16_t *h, int64_t ld
     L.argmax = argmax;
     L.logits = logits;
     L.ldl = ldl;
+    L.draft = draft_ids;
+    L.acc_b = b;
+    L.acc_rows = m_rows;
+    L.accept_len = accept_len;
+    L.committed = committed;
     dspk::GemmProblem &P = L.p[0];
     P.tiles = w->tiles;
     P.n = w->n;
     P.cg_begin = 0;
     return launch_result(dspk::launch_lmhead(L, w->bits, pl.grid, (hipStream_t)stream), who);
+}
+
+int dspk_lmhead_argmax(const dspk_tiled_weight *w, const uint16_t *h, int64_t ldh, int32_t m, int32_t *argmax,
+                       float *logits, int64_t ldl, void *workspace, size_t ws_bytes, void *stream) {
+    return lmhead_common("dspk_lmhead_argmax", w, h, ldh, m, argmax, logits, ldl, nullptr, 0, 0, nullptr, nullptr,
+                         workspace, ws_bytes, stream);
+}
+
+int dspk_lmhead_argmax_accept_greedy(const dspk_tiled_weight *w, const uint16_t *h, int64_t ldh, int32_t b,
+                                     int32_t m_rows, int32_t *argmax, float *logits, int64_t ldl,
+                                     const int32_t *draft_ids, int32_t *accept_len, int32_t *committed,
+                                     void *workspace, size_t ws_bytes, void *stream) {
+    const char *who = "dspk_lmhead_argmax_accept_greedy";
+    if (b < 1 || m_rows < 1 || m_rows > DSPK_MAX_ROWS || (int64_t)b * m_rows > DSPK_MAX_ROWS)
+        return fail(DSPK_EINVAL, "%s: b=%d x m_rows=%d must be 1..%d rows", who, b, m_rows, DSPK_MAX_ROWS);
+    if (accept_len == nullptr || committed == nullptr || !aligned(accept_len, 4) || !aligned(committed, 4))
+        return fail(DSPK_EINVAL, "%s: accept_len or committed NULL or misaligned", who);
+    if (m_rows > 1 && (draft_ids == nullptr || !aligned(draft_ids, 4)))
+        return fail(DSPK_EINVAL, "%s: draft_ids NULL or misaligned", who);
+    return lmhead_common(who, w, h, ldh, b * m_rows, argmax, logits, ldl, draft_ids, b, m_rows, accept_len,
+                         committed, workspace, ws_bytes, stream);
 }
 
 int dspk_accept_greedy(const int32_t *target_ids, const int32_t *draft_ids, int32_t b, int32_t m_rows,

@@ -80,6 +80,11 @@ struct GemmLaunch {
     float *logits;
     int64_t ldl;
     unsigned long long *keys; // [kMaxRows] row maxima over the grid (atomic max; cleared by the last workgroup)
+    // optional greedy acceptance on the ids (head only; accept_len == NULL: none)
+    const int32_t *draft;     // [acc_b][acc_rows - 1]
+    int32_t acc_b, acc_rows;  // acc_b * acc_rows == m
+    int32_t *accept_len;      // [acc_b]
+    int32_t *committed;       // [acc_b][acc_rows]
     uint32_t *done;           // arrival counter over workgroups
 };
 

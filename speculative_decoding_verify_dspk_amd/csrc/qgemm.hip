@@ -610,8 +610,32 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT)) void qgemm_kernel(const 
         if (!s_flag) return;
         if (tid < M) {
             const unsigned long long b = __hip_atomic_load(&KL->keys[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            KL->argmax[tid] = (int32_t)(0xffffffffu - (uint32_t)(b & 0xffffffffull));
+            const int32_t id = (int32_t)(0xffffffffu - (uint32_t)(b & 0xffffffffull));
+            KL->argmax[tid] = id;
             __hip_atomic_store(&KL->keys[tid], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            red[0][tid] = (unsigned long long)(uint32_t)id;
+        }
+        if (KL->accept_len != nullptr) {
+            // Greedy acceptance of each request's drafts against these ids
+            // (the same rule as accept_greedy_kernel): drafts are accepted
+            // while they equal the target's token of the same row, then the
+            // target's token of the first mismatching row (or of the last
+            // row) is committed.
+            __syncthreads();
+            const int R = KL->acc_rows;
+            for (int r = tid; r < KL->acc_b; r += 256) {
+                const int32_t *dr = KL->draft + (int64_t)r * (R - 1);
+                int32_t *cr = KL->committed + (int64_t)r * R;
+                auto t_of = [&](int j) { return (int32_t)(uint32_t)red[0][r * R + j]; };
+                int a = 0;
+                while (a < R - 1 && dr[a] == t_of(a)) {
+                    cr[a] = dr[a];
+                    ++a;
+                }
+                cr[a] = t_of(a);
+                for (int i = a + 1; i < R; ++i) cr[i] = -1;
+                KL->accept_len[r] = a + 1;
+            }
         }
         if (tid == 0) __hip_atomic_store(KL->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }

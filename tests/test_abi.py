@@ -152,6 +152,23 @@ def test_lmhead_rejects(lib):
     assert lib.dspk_lmhead_argmax(ctypes.byref(d), X, 128, 40, Y, None, 0, WS, 1 << 20, None) == EINVAL
 
 
+def test_fused_head_accept_rejects(lib):
+    d = _desc(n=1000, k=128)
+    need = lib.dspk_lmhead_workspace_bytes(1000, 32)
+    f = lib.dspk_lmhead_argmax_accept_greedy
+    # rows: b * m_rows must lie in 1..32
+    assert f(ctypes.byref(d), X, 128, 0, 4, Y, None, 0, X, Y, Y, WS, need, None) == EINVAL
+    assert f(ctypes.byref(d), X, 128, 4, 9, Y, None, 0, X, Y, Y, WS, need, None) == EINVAL
+    assert f(ctypes.byref(d), X, 128, 1, 33, Y, None, 0, X, Y, Y, WS, need, None) == EINVAL
+    # acceptance pointers
+    assert f(ctypes.byref(d), X, 128, 2, 4, Y, None, 0, None, Y, Y, WS, need, None) == EINVAL
+    assert f(ctypes.byref(d), X, 128, 2, 4, Y, None, 0, X, None, Y, WS, need, None) == EINVAL
+    assert f(ctypes.byref(d), X, 128, 2, 4, Y, None, 0, X, Y, None, WS, need, None) == EINVAL
+    # the head's own checks still apply (workspace too small)
+    assert f(ctypes.byref(d), X, 128, 2, 4, Y, None, 0, X, Y, Y, WS, 64, None) == EINVAL
+    assert "workspace" in lib.dspk_last_error().decode()
+
+
 def test_accept_rejects(lib):
     assert lib.dspk_accept_greedy(X, X, 0, 4, Y, Y, None) == EINVAL
     assert lib.dspk_accept_greedy(X, X, 1, 33, Y, Y, None) == EINVAL

@@ -52,6 +52,43 @@ def test_batched_four_requests():
     assert np.array_equal(al[ok_req], ral[ok_req]) and np.array_equal(com[ok_req], rcom[ok_req])
 
 
+@pytest.mark.parametrize("b,rows", [(1, 1), (1, 6), (1, 17), (4, 6), (2, 16), (32, 1)])
+def test_fused_head_accept_equals_separate_calls(b, rows):
+    """dspk_lmhead_argmax_accept_greedy gives exactly the ids of
+    dspk_lmhead_argmax and the acceptance of dspk_accept_greedy on them, and
+    the acceptance matches the oracle's greedy rule on the oracle's ids."""
+    import torch
+    from speculative_decoding_verify_dspk_amd import binding
+    from gpuutil import dev_act
+    m, k, v = b * rows, 2048, 8192
+    head = inputs.make_qweight(v, k, 8, "fused", b, rows)
+    h_bits = inputs.make_activations(m, k, "fused", "h", b, rows)
+    dw = binding.DeviceQWeight.upload(head)
+    h = dev_act(h_bits)
+    ids_sep, _ = run_lmhead(head, h_bits, m, want_logits=False, dw=dw)
+    zref = oracle.qlinear(h_bits, head.codes, head.scales, head.biases, 8, v, k)
+    t_ref, near = assert_argmax_parity(ids_sep, zref, what="fused head")
+    t = t_ref.reshape(b, rows)
+    d = inputs.drafts_match_rate(t, np.full(b, 0.7), v, "fused", b, rows) if rows > 1 else None
+    al_sep, com_sep = gpu_greedy(ids_sep.reshape(b, rows).astype(np.int32), d)
+    ws = binding.alloc_workspace(binding.lmhead_workspace_bytes(v, m))
+    am = torch.full((m,), -7, dtype=torch.int32, device="cuda")
+    al = torch.full((b,), -7, dtype=torch.int32, device="cuda")
+    com = torch.full((b, rows), -7, dtype=torch.int32, device="cuda")
+    dd = torch.from_numpy(np.ascontiguousarray(d, dtype=np.int32)).cuda() if d is not None else None
+    for _ in range(2):      # the workspace is left zeroed: a second call gives the same results
+        binding.lmhead_argmax_accept_greedy(dw, h, b, rows, am, dd, al, com, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(am.cpu().numpy(), ids_sep)
+        assert np.array_equal(al.cpu().numpy(), al_sep) and np.array_equal(com.cpu().numpy(), com_sep)
+    if d is not None:
+        ral, rcom = oracle.accept_greedy(t, d)
+        ok = ~near.reshape(b, rows).any(axis=1)
+        assert np.array_equal(al_sep[ok], ral[ok]) and np.array_equal(com_sep[ok], rcom[ok])
+    else:
+        assert np.all(al_sep == 1) and np.array_equal(com_sep[:, 0], ids_sep)
+
+
 def test_graph_replays_match_eager_round():
     """A round captured into HIP graphs (layers, head, accept) and replayed
     several times, with eager work and synchronisations in between, gives
