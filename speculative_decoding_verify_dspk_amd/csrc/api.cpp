@@ -226,10 +226,15 @@ int dspk_qgemm_verify_grouped(int32_t count, const dspk_tiled_weight *w, const u
 
 size_t dspk_lmhead_workspace_bytes(int32_t v, int32_t m) {
     if (v < 1 || m < 1 || m > DSPK_MAX_ROWS) return 0;
-    // the largest plan over hidden sizes and over every width up to m
-    const size_t a = dspk::plan_gemm(1, &v, 1 << 20, m < 16 ? m : 16, 8, true).ws_bytes;
-    const size_t b = dspk::plan_gemm(1, &v, 1 << 20, m, 8, true).ws_bytes;
-    return a > b ? a : b;
+    // the largest plan over hidden sizes, formats (their grids differ) and
+    // every width up to m
+    size_t most = 0;
+    for (int mm : {m < 16 ? m : 16, m})
+        for (int bits : {2, 3, 4, 8, 16}) {
+            const size_t b = dspk::plan_gemm(1, &v, 1 << 20, mm, bits, true).ws_bytes;
+            most = b > most ? b : most;
+        }
+    return most;
 }
 
 static int lmhead_common(const char *who, const dspk_tiled_weight *w, const uint16_t *h, int64_t ldh, int32_t m,

@@ -36,12 +36,23 @@ hipError_t launch_pack(int32_t n, int32_t k, int bits, const void *codes, const 
                        const uint16_t *biases, void *tiles, hipStream_t s);
 
 // Register-ring depth (units in flight per wave) and workgroups per CU of the
-// projection kernel, by weight format and 16-row tiles.  Two 16-row tiles
-// (17..32 rows) need twice the activation and accumulator registers: one
-// workgroup per CU keeps them out of scratch (measured faster than two
-// workgroups that spill).
-constexpr int kernel_depth(int bits, int mt) { return 2 + 0 * bits * mt; }
-constexpr int kernel_occ(int bits, int mt) { return mt == 2 ? 1 : 2 + 0 * bits; }
+// projection kernel, by weight format, 16-row tiles and kind (head or
+// projection), as measured on MI355X:
+//  * 8-bit and bf16, <= 16 rows: a 2-deep ring at two workgroups per CU
+//    (<= 240 VGPRs, no scratch).  No ring at three per CU: head 77 -> 83 us.
+//  * 2/3/4-bit, <= 16 rows: their units span four groups, and a 2-deep ring
+//    spills (100-260 B/lane); with no ring they fit three workgroups per CU
+//    without scratch: 9B-shaped 4-bit layer 103 -> 83 us, head 88 -> 80 us.
+//  * 17..32 rows (twice the activation and accumulator registers): a 2-deep
+//    ring at one workgroup per CU for projections; the head, whose
+//    workgroups stream many units each, runs with no ring at three per CU:
+//    27B-shaped head 197 -> 162 us (projections 145 -> 164 us that way).
+constexpr int kernel_depth(int bits, int mt, bool argmax) {
+    return mt == 1 ? (bits <= 4 ? 1 : 2) : (argmax && bits >= 8 ? 1 : 2);
+}
+constexpr int kernel_occ(int bits, int mt, bool argmax) {
+    return mt == 1 ? (bits <= 4 ? 3 : 2) : (argmax && bits >= 8 ? 3 : 1);
+}
 
 // Work of a projection launch is a list of quads: (weight, 64-column block,
 // four consecutive units), one unit per wave of a workgroup.  Quads are

@@ -147,9 +147,12 @@ __device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsig
 }
 
 template <int BITS, int MT, bool ARGMAX>
-__global__ __launch_bounds__(256, kernel_occ(BITS, MT)) void qgemm_kernel(const GemmLaunch L) {
+__global__ __launch_bounds__(256, kernel_occ(BITS, MT, ARGMAX)) void qgemm_kernel(const GemmLaunch L) {
     using C = Cfg<BITS>;
-    constexpr int DEPTH = kernel_depth(BITS, MT);
+    constexpr int DEPTH = kernel_depth(BITS, MT, ARGMAX);
+    // LDS slots for whole-block sums: two, unless that would keep the
+    // kernel's workgroups per CU from fitting in the 160 KiB of LDS
+    constexpr uint32_t SL = kernel_occ(BITS, MT, ARGMAX) * (2 * 16 * MT + 16) <= 160 ? kSlots : 1;
     constexpr int XB = MT == 1 ? 8 : 4;        // partial sums in flight when completing a split block
     // In-workgroup sum (each wave posts CTILES of its 16-column tiles per
     // pass, one 16-row tile at a time); after the main loop the same bytes
@@ -167,8 +170,8 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT)) void qgemm_kernel(const 
     // wave to arrive adds the posts in wave order and finishes the block.
     // A slot word holds (use << 3) | arrivals; a wave waits for the slot's
     // previous use to be finished (use advanced) before posting into it.
-    __shared__ f32x4 slots[kSlots][kWavesPerWG][NT][MT][kWave];
-    __shared__ uint32_t slot_word[kSlots];
+    __shared__ f32x4 slots[SL][kWavesPerWG][NT][MT][kWave];
+    __shared__ uint32_t slot_word[SL];
     auto &red = sh.tail.red;
     int &s_flag = sh.tail.flag;
 
@@ -194,7 +197,7 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT)) void qgemm_kernel(const 
     const int G = K >> 6;
     const int Q0 = range_begin(QU, GRID, PAIRS, bid), Q1 = range_begin(QU, GRID, PAIRS, bid + 1);
     const int M = KL->m;
-    if (tid < kSlots) slot_word[tid] = 0u;
+    if (tid < (int)SL) slot_word[tid] = 0u;
     __syncthreads();
 
     // global block -> weight index
@@ -414,10 +417,10 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT)) void qgemm_kernel(const 
         const int pi = weight_of(gb);
         const int cb = gb - KL->p[pi].cg_begin;
         if (a == gb * NQ && b == gb * NQ + NQ) {
-            const uint32_t sl = seq % kSlots, use = seq / kSlots;
+            const uint32_t sl = seq % SL, use = seq / SL;
             ++seq;
             // the slot's previous use has been read out (its last wave moved
-            // it on); waves are at most kSlots blocks apart, so this ends.
+            // it on); waves are at most SL blocks apart, so this ends.
             // The bound only guards against a broken invariant: a wave never
             // spins forever (results would then be wrong, not the GPU hung).
             for (int spin = 0; spin < (1 << 20); ++spin) {
@@ -687,11 +690,11 @@ GemmPlan plan_gemm(int count, const int32_t *n, int32_t k, int32_t m, int bits, 
     const int64_t quads = blocks * p.nq;
     const int mt = m <= 16 ? 1 : 2;
     // OCC workgroups per CU; never more workgroups than quads
-    const int64_t slots = (int64_t)kernel_occ(bits, mt) * device_cus();
+    const int64_t slots = (int64_t)kernel_occ(bits, mt, argmax) * device_cus();
     const int64_t grid = quads < slots ? quads : slots;
     p.grid = grid < 1 ? 1 : (int32_t)grid;
     // a full grid of two workgroups per CU runs as CU pairs (weighted split)
-    p.pairs = (kernel_occ(bits, mt) == 2 && p.grid == 2 * device_cus()) ? device_cus() : 0;
+    p.pairs = (kernel_occ(bits, mt, argmax) == 2 && p.grid == 2 * device_cus()) ? device_cus() : 0;
     // the kernel splits quads with 32-bit products
     p.fits = quads * p.grid < ((int64_t)1 << 31);
     p.quads = p.fits ? (int32_t)quads : 0;
