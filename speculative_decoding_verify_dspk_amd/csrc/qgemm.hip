@@ -92,12 +92,27 @@ __device__ __forceinline__ void st_global_u16(uint16_t *p, uint32_t v) {
     asm volatile("global_store_short %0, %1, off" ::"v"(p), "v"(v) : "memory");
 }
 
-__device__ __forceinline__ void store_agent(float *p, float v) {
-    __hip_atomic_store((uint32_t *)p, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// A lane's four partial sums of one 16-row tile as two device-scope 64-bit
+// accesses, laid out [half][lane][2] so that each wave-wide access covers
+// 512 contiguous bytes (four scattered 4-byte stores per lane wrote 13.6 MB
+// of counted HBM writes per head launch).
+__device__ __forceinline__ void store_pair4(float *tile, int lane, f32x4 v) {
+    unsigned long long *q = (unsigned long long *)tile;
+    const unsigned long long lo = (unsigned long long)__float_as_uint(v[0]) |
+                                  ((unsigned long long)__float_as_uint(v[1]) << 32);
+    const unsigned long long hi = (unsigned long long)__float_as_uint(v[2]) |
+                                  ((unsigned long long)__float_as_uint(v[3]) << 32);
+    __hip_atomic_store(q + lane, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + kWave + lane, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float load_agent(const float *p) {
-    return __uint_as_float(__hip_atomic_load((uint32_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+__device__ __forceinline__ f32x4 load_pair4(const float *tile, int lane) {
+    unsigned long long *q = (unsigned long long *)tile;
+    const unsigned long long lo = __hip_atomic_load(q + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long hi = __hip_atomic_load(q + kWave + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return f32x4{__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)), __uint_as_float((uint32_t)hi),
+                 __uint_as_float((uint32_t)(hi >> 32))};
 }
+
 
 // First quad of workgroup v when `quads` are split over `groups` workgroups
 // (quads * groups < 2^31 is checked on the host).
@@ -484,7 +499,7 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT, ARGMAX)) void qgemm_kerne
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) store_agent(mine + (mt * kWave + lane) * 4 + r4, z[mt][r4]);
+            store_pair4(mine + mt * kWave * 4, lane, z[mt]);
         wait_vm_all();
         const int wf = range_owner(QU, GRID, PAIRS, bq0), wl = range_owner(QU, GRID, PAIRS, bq1 - 1);
         uint32_t ticket = 0;
@@ -509,7 +524,7 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT, ARGMAX)) void qgemm_kerne
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) part[i][mt][r4] = load_agent(src + (mt * kWave + lane) * 4 + r4);
+                    part[i][mt] = load_pair4(src + mt * kWave * 4, lane);
             }
             // every loaded value is consumed (a duplicate past wl adds zero), so
             // no load of this batch is left pending
