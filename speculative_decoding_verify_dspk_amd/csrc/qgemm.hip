@@ -497,9 +497,7 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT, ARGMAX)) void qgemm_kerne
         const int side = a == Q0 ? 0 : 1;
         float *mine = KL->partial + (((int64_t)bid * 2 + side) * kWavesPerWG + w) * (MT * kWave * 4);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            store_pair4(mine + mt * kWave * 4, lane, z[mt]);
+        for (int mt = 0; mt < MT; ++mt) store_pair4(mine + mt * kWave * 4, lane, z[mt]);
         wait_vm_all();
         const int wf = range_owner(QU, GRID, PAIRS, bq0), wl = range_owner(QU, GRID, PAIRS, bq1 - 1);
         uint32_t ticket = 0;
@@ -522,9 +520,7 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT, ARGMAX)) void qgemm_kerne
                 const int sl = v == wf ? wf_side : 0;
                 const float *src = KL->partial + (((int64_t)v * 2 + sl) * kWavesPerWG + w) * (MT * kWave * 4);
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                    part[i][mt] = load_pair4(src + mt * kWave * 4, lane);
+                for (int mt = 0; mt < MT; ++mt) part[i][mt] = load_pair4(src + mt * kWave * 4, lane);
             }
             // every loaded value is consumed (a duplicate past wl adds zero), so
             // no load of this batch is left pending
