@@ -12,7 +12,7 @@
 //   plus their scale/bias dwords, already in the order in which each lane
 //   feeds the matrix cores.  A wave loads a unit straight into registers with
 //   eight fully coalesced 1 KiB global_load_dwordx4 (non-temporal) plus one
-//   16-byte scale/bias load per group, DEPTH units deep, so a workgroup's
+//   16-byte scale/bias load per group, DEPTH units deep (kernel_depth), so a workgroup's
 //   four waves read one contiguous 35 KiB run per step and the whole launch
 //   sweeps memory in order.  Nothing passes through LDS on the way in.
 // * The group is the MFMA contraction unit.  Codes 0..255 (and 128+q for
@@ -27,14 +27,19 @@
 //   call do not depend on M.
 // * Work unit of a workgroup = a "quad": one 64-column block times four
 //   consecutive units, one per wave.  Persistent workgroups (OCC per CU) take
-//   equal contiguous ranges of the quads of the whole launch (stream-K over
-//   workgroups), so small and large weights alike keep every CU streaming.
-//   At the end of each block piece the four waves add their partial sums
-//   through LDS (fixed order), each wave keeping one 16-column tile; a block
-//   split between workgroups is completed by the last of them to arrive,
+//   contiguous ranges of the quads of the whole launch (stream-K over
+//   workgroups), so small and large weights alike keep every CU streaming;
+//   the two workgroups that share a CU split one range unevenly (see
+//   range_begin).  A block inside one range is summed by its four waves
+//   through LDS in wave order without a workgroup barrier; a block split
+//   between workgroups (the first or last piece of a range) is summed
+//   through LDS per piece and completed by the last workgroup to arrive,
 //   which adds the pieces in workgroup order.  Results do not depend on
 //   scheduling.  Pieces and arrival counters move through device-scope
 //   atomic accesses, so no cache flush is needed.
+// * Head: row maxima fold into one 64-bit key per row by atomic max; the
+//   last workgroup writes the ids (and, on request, runs the greedy
+//   acceptance on them).
 #include "decode.h"
 #include "dspk_internal.h"
 
