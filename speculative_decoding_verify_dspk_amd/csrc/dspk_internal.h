@@ -43,15 +43,16 @@ hipError_t launch_pack(int32_t n, int32_t k, int bits, const void *codes, const 
 //  * 2/3/4-bit, <= 16 rows: their units span four groups, and a 2-deep ring
 //    spills (100-260 B/lane); with no ring they fit three workgroups per CU
 //    without scratch: 9B-shaped 4-bit layer 103 -> 83 us, head 88 -> 80 us.
-//  * 17..32 rows (twice the activation and accumulator registers): a 2-deep
-//    ring at one workgroup per CU for projections; the head, whose
-//    workgroups stream many units each, runs with no ring at three per CU:
-//    27B-shaped head 197 -> 162 us (projections 145 -> 164 us that way).
+//  * 17..32 rows (twice the activation and accumulator registers): no ring,
+//    two workgroups per CU for projections (27B-shaped layer 138 -> 120 us
+//    against a 2-deep ring at one per CU); the head, whose workgroups stream
+//    many units each, no ring at three per CU (27B-shaped head 197 -> 162
+//    us); 2/3/4-bit heads keep a 2-deep ring at one per CU.
 constexpr int kernel_depth(int bits, int mt, bool argmax) {
-    return mt == 1 ? (bits <= 4 ? 1 : 2) : (argmax && bits >= 8 ? 1 : 2);
+    return mt == 1 ? (bits <= 4 ? 1 : 2) : (argmax && bits <= 4 ? 2 : 1);
 }
 constexpr int kernel_occ(int bits, int mt, bool argmax) {
-    return mt == 1 ? (bits <= 4 ? 3 : 2) : (argmax && bits >= 8 ? 3 : 1);
+    return mt == 1 ? (bits <= 4 ? 3 : 2) : (!argmax ? 2 : bits >= 8 ? 3 : 1);
 }
 
 // Work of a projection launch is a list of quads: (weight, 64-column block,

@@ -172,7 +172,7 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT, ARGMAX)) void qgemm_kerne
     constexpr int DEPTH = kernel_depth(BITS, MT, ARGMAX);
     // LDS slots for whole-block sums: two, unless that would keep the
     // kernel's workgroups per CU from fitting in the 160 KiB of LDS
-    constexpr uint32_t SL = kernel_occ(BITS, MT, ARGMAX) * (2 * 16 * MT + 16) <= 160 ? kSlots : 1;
+    constexpr uint32_t SL = kernel_occ(BITS, MT, ARGMAX) * (2 * 16 * MT + 16) < 160 ? kSlots : 1;
     constexpr int XB = MT == 1 ? 8 : 4;        // partial sums in flight when completing a split block
     // In-workgroup sum (each wave posts CTILES of its 16-column tiles per
     // pass, one 16-row tile at a time); after the main loop the same bytes
