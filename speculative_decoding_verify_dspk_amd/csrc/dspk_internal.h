@@ -38,8 +38,10 @@ hipError_t launch_pack(int32_t n, int32_t k, int bits, const void *codes, const 
 // Register-ring depth (units in flight per wave) and workgroups per CU of the
 // projection kernel, by weight format, 16-row tiles and kind (head or
 // projection), as measured on MI355X:
-//  * 8-bit and bf16, <= 16 rows: a 2-deep ring at two workgroups per CU
-//    (<= 240 VGPRs, no scratch).  No ring at three per CU: head 77 -> 83 us.
+//  * 8-bit and bf16, <= 16 rows: heads a 2-deep ring at two workgroups per
+//    CU (<= 244 VGPRs, no scratch; no ring at three per CU: head 77 -> 83
+//    us).  8-bit projections no ring at two per CU (Qwen3-4B layer 63.5 ->
+//    61.9 us, 27B-shaped layer 105.7 -> 102.5 us against the 2-deep ring).
 //  * 2/3/4-bit, <= 16 rows: their units span four groups, and a 2-deep ring
 //    spills (100-260 B/lane); with no ring they fit three workgroups per CU
 //    without scratch: 9B-shaped 4-bit layer 103 -> 83 us, head 88 -> 80 us.
@@ -49,7 +51,7 @@ hipError_t launch_pack(int32_t n, int32_t k, int bits, const void *codes, const 
 //    many units each, no ring at three per CU (27B-shaped head 197 -> 162
 //    us); 2/3/4-bit heads keep a 2-deep ring at one per CU.
 constexpr int kernel_depth(int bits, int mt, bool argmax) {
-    return mt == 1 ? (bits <= 4 ? 1 : 2) : (argmax && bits <= 4 ? 2 : 1);
+    return mt == 1 ? (bits <= 4 || (bits == 8 && !argmax) ? 1 : 2) : (argmax && bits <= 4 ? 2 : 1);
 }
 constexpr int kernel_occ(int bits, int mt, bool argmax) {
     return mt == 1 ? (bits <= 4 ? 3 : 2) : (!argmax ? 2 : bits >= 8 ? 3 : 1);
