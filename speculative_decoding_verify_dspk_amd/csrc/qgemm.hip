@@ -141,12 +141,17 @@ __device__ __forceinline__ int quad_owner(int quads, int groups, int q) {
 #define DSPK_LEAD_NUM 10
 #endif
 constexpr uint32_t kLeadNum = DSPK_LEAD_NUM, kLeadDen = 16;
-// A pair's range has >= 2 quads (quads >= grid); floor(n * f) lies in
-// [1, n - 1] for every n >= 2 when 1/2 <= f < 1, so both pieces are non-empty.
+// The earlier workgroup takes max(ceil(n / 2), floor(n * f)) of a pair's n
+// quads: rounding down alone would hand the later one the larger piece of a
+// short range (n = 3: 1 and 2).  A pair's range has n >= 2 quads (quads >=
+// grid), and both terms lie in [1, n - 1] for n >= 2 when 1/2 <= f < 1, so
+// both pieces are non-empty.
 static_assert(2 * kLeadNum >= kLeadDen && kLeadNum < kLeadDen,
               "a pair's range of >= 2 quads must give both workgroups a non-empty piece");
 __device__ __forceinline__ int split_point(int a, int b) {
-    return a + (int)(((uint32_t)(b - a) * kLeadNum) / kLeadDen);
+    const uint32_t n = (uint32_t)(b - a);
+    const uint32_t lead = (n * kLeadNum) / kLeadDen, half = (n + 1) / 2;
+    return a + (int)(lead > half ? lead : half);
 }
 __device__ __forceinline__ int range_begin(int quads, int grid, int pairs, int rank) {
     if (pairs == 0) return quad_begin(quads, grid, rank);
