@@ -148,22 +148,31 @@ constexpr uint32_t kLeadNum = DSPK_LEAD_NUM, kLeadDen = 16;
 // both pieces are non-empty.
 static_assert(2 * kLeadNum >= kLeadDen && kLeadNum < kLeadDen,
               "a pair's range of >= 2 quads must give both workgroups a non-empty piece");
-__device__ __forceinline__ int split_point(int a, int b) {
+// A pair whose range spans at least four blocks (nq quads each) moves the
+// split point to the nearest block boundary inside the range: then neither
+// workgroup has a split piece there (no cross-workgroup exchange, no ring
+// drain), at a cost of at most half a block in the balance (head 75 -> 74 us).
+__device__ __forceinline__ int split_point(int a, int b, int nq) {
     const uint32_t n = (uint32_t)(b - a);
     const uint32_t lead = (n * kLeadNum) / kLeadDen, half = (n + 1) / 2;
-    return a + (int)(lead > half ? lead : half);
+    const int sp = a + (int)(lead > half ? lead : half);
+    if ((int)n >= 4 * nq) {
+        const int al = ((sp + nq / 2) / nq) * nq;
+        if (al > a && al < b) return al;
+    }
+    return sp;
 }
-__device__ __forceinline__ int range_begin(int quads, int grid, int pairs, int rank) {
+__device__ __forceinline__ int range_begin(int quads, int grid, int pairs, int rank, int nq) {
     if (pairs == 0) return quad_begin(quads, grid, rank);
     const int p = rank >> 1;
     const int a = quad_begin(quads, pairs, p);
     if ((rank & 1) == 0) return a;
-    return split_point(a, quad_begin(quads, pairs, p + 1));
+    return split_point(a, quad_begin(quads, pairs, p + 1), nq);
 }
-__device__ __forceinline__ int range_owner(int quads, int grid, int pairs, int q) {
+__device__ __forceinline__ int range_owner(int quads, int grid, int pairs, int q, int nq) {
     if (pairs == 0) return quad_owner(quads, grid, q);
     const int p = quad_owner(quads, pairs, q);
-    const int s = split_point(quad_begin(quads, pairs, p), quad_begin(quads, pairs, p + 1));
+    const int s = split_point(quad_begin(quads, pairs, p), quad_begin(quads, pairs, p + 1), nq);
     return 2 * p + (q >= s ? 1 : 0);
 }
 
@@ -220,7 +229,7 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT, ARGMAX)) void qgemm_kerne
     const int LASTW = NST - 4 * (NQ - 1);     // waves with a unit in a block's last quad (1..4)
     const int K = KL->k;
     const int G = K >> 6;
-    const int Q0 = range_begin(QU, GRID, PAIRS, bid), Q1 = range_begin(QU, GRID, PAIRS, bid + 1);
+    const int Q0 = range_begin(QU, GRID, PAIRS, bid, NQ), Q1 = range_begin(QU, GRID, PAIRS, bid + 1, NQ);
     const int M = KL->m;
     if (tid < (int)SL) slot_word[tid] = 0u;
     __syncthreads();
@@ -509,7 +518,7 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT, ARGMAX)) void qgemm_kerne
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) store_pair4(mine + mt * kWave * 4, lane, z[mt]);
         wait_vm_all();
-        const int wf = range_owner(QU, GRID, PAIRS, bq0), wl = range_owner(QU, GRID, PAIRS, bq1 - 1);
+        const int wf = range_owner(QU, GRID, PAIRS, bq0, NQ), wl = range_owner(QU, GRID, PAIRS, bq1 - 1, NQ);
         uint32_t ticket = 0;
         uint32_t *ctr = KL->counters + (int64_t)gb * kWavesPerWG + w;
         if (lane == 0) ticket = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -519,7 +528,7 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT, ARGMAX)) void qgemm_kerne
         // flight (few: the ring's registers are live here).  Every workgroup after wf starts inside the block (its piece
         // is its first, slot 0); wf's piece is its first only if its range
         // starts at the block start.
-        const int wf_side = range_begin(QU, GRID, PAIRS, wf) >= bq0 ? 0 : 1;
+        const int wf_side = range_begin(QU, GRID, PAIRS, wf, NQ) >= bq0 ? 0 : 1;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) z[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int v0 = wf; v0 <= wl; v0 += XB) {
