@@ -406,8 +406,10 @@ def accept_sample_filtered(logits, q, draft_ids, uniforms, temperature: float, t
     was drawn from q~_j).  Then the rule of accept_sample: accept d_j iff
     u_j * q~_j(d_j) < p~_j(d_j); at the first reject sample the residual
     max(0, p~_j - q~_j) (p~_j if it has no mass); else the bonus from p~_{M-1}.
-    Without truncation (top_k <= 0 and top_p >= 1) q is used as supplied, as
-    in accept_sample.  Faults as accept_sample, plus top_p outside (0, 1],
+    Without truncation q is used as supplied, as in accept_sample; truncation
+    is off when top_p == 1 and top_k keeps everything (top_k <= 0, or
+    top_k >= v: every entry would be kept).  Faults as accept_sample, plus
+    top_p outside (0, 1],
     negative penalties' counts, and counts < 0."""
     z = np.asarray(logits, dtype=np.float64)
     m_rows, v = z.shape
@@ -423,7 +425,7 @@ def accept_sample_filtered(logits, q, draft_ids, uniforms, temperature: float, t
            or (counts is not None and (np.asarray(counts) < 0).any()))
     if bad:
         return -1, committed
-    trunc = top_k > 0 or top_p < 1.0
+    trunc = (0 < top_k < v) or top_p < 1.0
     zp = penalized_logits(z, counts, d, presence, frequency)
 
     def target(j):

@@ -149,3 +149,45 @@ def test_first_token_is_the_truncated_target(top_k, top_p, pen):
     assert hist[~sup].sum() == 0                      # never outside the truncated support
     chi = stats.chisquare(hist[sup], p0[sup] * trials)
     assert chi.pvalue > 1e-3, chi
+
+
+def _golden(name):
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")) as f:
+        return json.load(f)[name]
+
+
+@pytest.mark.parametrize("case", range(4))
+def test_penalized_logits_hand_cases(case):
+    """The penalty arithmetic against hand-worked values (tests/golden): the
+    sign of each term, presence as an indicator, frequency per occurrence, and
+    row j counting the history plus drafts 0..j-1 only."""
+    c = _golden("penalties")[case]
+    z = np.array(c["z"], dtype=np.float64)
+    got = oracle.penalized_logits(z, c["counts"], np.array(c["d"], dtype=np.int64), c["presence"], c["frequency"])
+    assert np.array_equal(got, np.array(c["expected"], dtype=np.float64)), (got, c["why"])
+
+
+def test_top_k_at_least_v_is_no_truncation():
+    """top_k >= v keeps every entry, so (with top_p = 1) truncation is off and
+    q is used as supplied -- also when its rows do not sum to one, where a
+    renormalisation would change the accept test."""
+    g = np.random.default_rng(11)
+    v, m = 7, 4
+    for trial in range(200):
+        z = g.normal(0, 2, size=(m, v))
+        q = g.random((m - 1, v))
+        q = q / q.sum(axis=1, keepdims=True) * g.uniform(0.6, 1.4, size=(m - 1, 1))   # rows not summing to 1
+        d = g.integers(0, v, size=m - 1)
+        u = (g.integers(0, 1 << 24, size=m) / float(1 << 24))
+        want = oracle.accept_sample(z, q, d, u, 0.8) if np.all(np.abs(q.sum(axis=1) - 1) < 1e-5) else None
+        for top_k in (v, v + 1, 1000):
+            a = oracle.accept_sample_filtered(z, q, d, u, 0.8, top_k=top_k)
+            b = oracle.accept_sample_filtered(z, q, d, u, 0.8, top_k=0)
+            assert a[0] == b[0] and np.array_equal(a[1], b[1])
+            if want is not None:
+                assert a[0] == want[0]
+        # with a real top-k (< v) the draft row is renormalised: results may differ, never fault
+        r = oracle.accept_sample_filtered(z, q, d, u, 0.8, top_k=v - 1)
+        assert 1 <= r[0] <= m
