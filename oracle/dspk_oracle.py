@@ -8,11 +8,12 @@ holds none of the method's arithmetic.
 
 What it computes, and the passages it follows (pages quoted by title):
 
-* "mlx-dspark" wiki summary, section "Architecture", first bullet: each round
-  runs the target forward over the anchor plus m draft tokens in one pass,
-  compares the draft with the target's own logits and commits the longest
-  accepted prefix; greedy output equals plain decoding, and temperature > 0 is
-  an exact sample through the Leviathan/Chen rule min(1, p/q).
+* "mlx-dspark" wiki summary, section "Architecture", first bullet: one
+  target pass evaluates the anchor and all m drafts; every draft is checked
+  against what the target itself predicts at its position and the drafts are
+  kept up to the first failed check.  Greedy checks reproduce plain decoding;
+  at temperature > 0 the Leviathan/Chen min(1, p/q) test keeps the output an
+  exact sample of the target.
 * Same page, "Key techniques" (auto-calibration bullet): a round commits
   1 + sum p^i tokens in expectation, i.e. the accepted drafts plus one token of
   the target's own; "Design decisions": a miss costs a plain one-token forward.
@@ -72,17 +73,16 @@ def unpack_codes(codes, bits: int, k: int) -> np.ndarray:
     """
     if bits not in (2, 3, 4, 8):
         raise ValueError("unpack_codes: bits must be 2, 3, 4 or 8")
-    words = np.asarray(codes, dtype=np.uint32)
+    words = np.ascontiguousarray(codes, dtype="<u4")
     n = words.shape[0]
     if words.shape[1] * 32 != k * bits:
         raise ValueError("unpack_codes: packed width does not match K")
-    # the row's bit stream, bit i at column i
-    stream = np.zeros((n, 32 * words.shape[1]), dtype=np.int64)
-    for b in range(32):
-        stream[:, b::32] = (words >> np.uint32(b)) & np.uint32(1)
+    # the row's bit stream, bit i at column i: the words' little-endian bytes,
+    # each byte's bits lowest first
+    stream = np.unpackbits(words.view(np.uint8), axis=1, bitorder="little")
     q = np.zeros((n, k), dtype=np.int64)
     for b in range(bits):
-        q |= stream[:, b::bits][:, :k] << b
+        q |= stream[:, b::bits][:, :k].astype(np.int64) << b
     return q
 
 
@@ -354,10 +354,10 @@ class CapController:
 # -------------------------------------------- truncated / penalised sampling
 def penalized_logits(logits, counts, draft_ids, presence: float, frequency: float) -> np.ndarray:
     """Target logits with presence/frequency penalties, row by row
-    ("mlx-dspark releases", v0.2.0 notes: the penalties are applied to the
-    target logits so that speculative output equals sequential decoding of the
-    penalised target).  Row j is reached only when drafts 0..j-1 were
-    accepted, so its token counts are the history's plus those drafts:
+    ("mlx-dspark releases", v0.2.0 notes: the penalties act on the target
+    logits, and the committed tokens are those one-token decoding of the
+    penalised target would give).  Row j is reached only when drafts 0..j-1
+    were accepted, so its token counts are the history's plus those drafts:
         c_j(v) = counts[v] + #{i < j : d_i = v}
         z'_j(v) = z_j(v) - presence * [c_j(v) > 0] - frequency * c_j(v)
     (the OpenAI definition the pages name)."""
@@ -375,9 +375,9 @@ def penalized_logits(logits, counts, draft_ids, presence: float, frequency: floa
 
 def truncate(prob, top_k: int, top_p: float) -> np.ndarray:
     """Keep-mask of top-k then top-p truncation of one distribution
-    ("mlx-dspark releases", v0.1.0 notes: nucleus / top-k truncation applied
-    to both the draft and the target keeps sampling exact for the truncated
-    target).  Reading: order the entries by probability, larger first, ties by
+    ("mlx-dspark releases", v0.1.0 notes: when the draft and the target are
+    cut down by the same top-k / top-p filter, speculative sampling stays an
+    exact sample of the filtered target).  Reading: order the entries by probability, larger first, ties by
     the smaller index; top-k keeps the first k (k <= 0: all); top-p then keeps
     an entry iff the mass of the kept entries before it is below
     top_p * (mass kept by top-k) -- the smallest leading set whose mass

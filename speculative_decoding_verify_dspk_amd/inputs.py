@@ -83,6 +83,15 @@ def pack_codes(codes_u8: np.ndarray, bits: int) -> np.ndarray:
         raise ValueError("K * bits must be a multiple of 32")
     if c.max(initial=0) >= (1 << bits):
         raise ValueError("code out of range")
+    if 32 % bits == 0:
+        # no code straddles a word: word w holds codes w*per .. w*per + per-1,
+        # code i of the word at bits bits*i ..
+        per = 32 // bits
+        cw = c.reshape(n, k // per, per)
+        words = np.zeros((n, k // per), dtype=np.uint64)
+        for i in range(per):
+            words |= cw[:, :, i] << np.uint64(bits * i)
+        return words.astype(np.uint32)
     words = np.zeros((n, k * bits // 32), dtype=np.uint64)
     pos = np.arange(k, dtype=np.int64) * bits
     w, off = pos // 32, (pos % 32).astype(np.uint64)
@@ -283,10 +292,9 @@ def make_activations_rowmajor_device(m: int, k: int, *labels):
 
 
 def make_activations_device(m: int, k: int, *labels):
-    """bf16 N(0, 1) rows on the GPU (int16 bit patterns), in the library's
-    chunk-major layout ``[K/8][M][8]`` (independent draws, so the layout does
-    not change the distribution)."""
+    """bf16 N(0, 1) rows on the GPU (int16 bit patterns), row-major ``[M][K]``:
+    the layout every projection call reads."""
     import torch
     g = device_generator(*labels, m, k, "act")
-    x = torch.empty((k // 8, m, 8), dtype=torch.float32, device="cuda").normal_(0.0, 1.0, generator=g)
+    x = torch.empty((m, k), dtype=torch.float32, device="cuda").normal_(0.0, 1.0, generator=g)
     return x.to(torch.bfloat16).view(torch.int16)
