@@ -76,6 +76,13 @@ def parse():
                     help="prefill workload instead: one layer's projections over this many prompt rows "
                          "(dspk_qgemm_prefill) plus the head on the last row")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--variant-curves", action="store_true",
+                    help="instead: t(M) of each Qwen3-4B projection launch under each forced decomposition "
+                         "(stream-K and slab on the matrix cores, slab with vector-ALU dot products)")
+    ap.add_argument("--draft-sets", type=int, default=8,
+                    help="independent draft sets per (width, weight copy); rounds cycle through them")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the streaming probe and the 27B-shaped layer + head section")
     ap.add_argument("--cpu-sample-s", type=float, default=20.0)
     ap.add_argument("--graph", action="store_true",
                     help="replay each round as HIP graphs (layers, head, accept) captured once per width and "
@@ -254,8 +261,170 @@ def prefill_cpu_baseline(model: str, bits: int, rows: int, budget_s: float = 15.
                                         f"{bits}-bit, in {t:.1f} s"}
 
 
+def achievable_bandwidth(nbytes: int, reps: int = 12):
+    """In-process streaming-read probe (libdspk_probe.so): the best rate at
+    which this device streams `nbytes` from HBM with the projection kernels'
+    access pattern (16 B per lane, 1 KiB per wave instruction, non-temporal),
+    rotating three buffers so the 256 MB MALL cannot serve a repeat.  Timed
+    with HIP events on the launch stream; best over a few grid sizes."""
+    import ctypes
+    import torch
+    from speculative_decoding_verify_dspk_amd import build as _b
+    if not os.path.exists(_b.PROBE_LIB):
+        return None
+    lib = ctypes.CDLL(_b.PROBE_LIB)
+    f = lib.dspk_probe_stream_read
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    nb = (nbytes + 1023) // 1024 * 1024
+    bufs = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(3)]
+    for b in bufs:
+        b.fill_(1)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(8 * cus, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    best = None
+    for grid in (2 * cus, 4 * cus, 8 * cus):
+        times = []
+        for r in range(reps + 2):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            if f(bufs[r % 3].data_ptr(), nb, grid, sink.data_ptr(), stream.cuda_stream) != 0:
+                return None
+            e1.record(stream)
+            e1.synchronize()
+            if r >= 2:
+                times.append(e0.elapsed_time(e1) * 1e-3)
+        gbs = nb / float(np.median(times)) / 1e9
+        if best is None or gbs > best["GBps"]:
+            best = {"GBps": round(gbs, 1), "grid": grid, "median_us": round(float(np.median(times)) * 1e6, 2)}
+    del bufs
+    best["bytes"] = nb
+    best["frac_of_peak"] = round(best["GBps"] / HBM_PEAK_GBS, 4)
+    return best
+
+
+def dense27b_section(steps: int, warmup: int, widths=(1, 8, 16), copies: int = 2):
+    """One 27B-shaped 8-bit layer (q/k/v, o, gate/up, down in 4 launches) and
+    the 151936 x 5120 head with the greedy acceptance, rotating `copies`
+    weight copies: per-launch device times from HIP events on the launch
+    stream (median over steps), and the weight bytes of layer + head over the
+    round's device time."""
+    import torch
+    from speculative_decoding_verify_dspk_amd import binding, inputs
+    from speculative_decoding_verify_dspk_amd.verify_round import VerifyStack
+    st = VerifyStack("dense-27b", 1, 8, max(widths), copies=copies, seed="bench-27b")
+    stream = torch.cuda.current_stream()
+    out = {"workload": "dense-27b layer x1 (5120 hidden, q 5120, kv 1024, inter 17408) + lm_head 151936x5120, "
+                       f"8-bit g64, greedy, {copies} rotating copies",
+           "weight_bytes_per_round": st.round_weight_bytes(), "widths": {}}
+    names = ["qkv", "o", "gate_up", "down", "head"]
+    for m in widths:
+        calls = {}
+        for cp in range(copies):
+            t = None
+            st.launch_head(m, cp, stream=stream)
+            t = st.argmax[:m].cpu().numpy().reshape(1, m)
+            d = inputs.drafts_match_rate(t, 0.7, st.vocab, "bench-27b", m, cp) if m > 1 else None
+            dd = torch.from_numpy(np.ascontiguousarray(d, dtype=np.int32)).cuda() if m > 1 else None
+            res = torch.empty((1 + m,), dtype=torch.int32, device="cuda")
+            layers, _ = st.prepare_round(m, cp, stream=stream)
+            head = binding.prepare_lmhead_accept_greedy(st.heads[cp], st.h, 1, m, st.argmax, None, dd, res[:1],
+                                                        res[1:].view(1, m), st.ws_head, stream)
+            calls[cp] = (layers + [head], dd, res)
+        recs = []
+        for it in range(warmup + steps):
+            cp = it % copies
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+            ev[0].record(stream)
+            for i, f in enumerate(calls[cp][0]):
+                f()
+                ev[i + 1].record(stream)
+            stream.synchronize()
+            if it >= warmup:
+                recs.append([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(5)])
+        med = np.median(np.array(recs), axis=0)
+        layer_us, head_us = float(med[:4].sum()), float(med[4])
+        lb, hb = st.layer_weight_bytes(), st.head_weight_bytes()
+        out["widths"][str(m)] = {
+            "launch_us": {n: round(float(v), 2) for n, v in zip(names, med)},
+            "layer_us": round(layer_us, 2), "head_us": round(head_us, 2),
+            "layer_hbm_frac": round(lb / (layer_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "head_hbm_frac": round(hb / (head_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "round_hbm_frac": round((lb + hb) / ((layer_us + head_us) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    first = out["widths"][str(widths[0])]
+    for k in out["widths"]:
+        w = out["widths"][k]
+        w["t_over_t1"] = round((w["layer_us"] + w["head_us"]) / (first["layer_us"] + first["head_us"]), 4)
+    del st
+    torch.cuda.empty_cache()
+    return out
+
+
+def variant_curves(args):
+    """t(M) of each Qwen3-4B 8-bit projection launch under each forced
+    decomposition -- stream-K and slab on the matrix cores, and the slab with
+    the K reduction on the vector ALUs (dot2, at most 4 rows) -- from HIP
+    events around single launches on the launch stream, rotating six weight
+    copies per shape so no launch is served from the MALL.  Prints one JSON
+    line; under rocprofv3 --kernel-trace the same launches give the kernel
+    durations (kernel names carry the decomposition and the row class)."""
+    import torch
+    from speculative_decoding_verify_dspk_amd import binding, inputs
+    binding.lib()
+    s = inputs.LAYER_SHAPES["qwen3-4b"]
+    H, Q, KV, F = s["hidden"], s["q"], s["kv"], s["inter"]
+    shapes = {"qkv": ([Q, KV, KV], H), "o": ([H], Q), "gate_up": ([F, F], H), "down": ([H], F)}
+    widths = list(range(1, 17))
+    copies = 6
+    stream = torch.cuda.current_stream()
+    out = {"metric": "per-launch device time t(M) by projection decomposition", "unit": "us",
+           "workload": "qwen3-4b layer projections, 8-bit g64, one launch per call (grouped q/k/v and gate/up), "
+                       f"{copies} rotating weight copies", "curves": {}, "launch_plan": []}
+    names = {binding.VARIANT_STREAMK: "mfma_streamk", binding.VARIANT_SLAB: "mfma_slab",
+             binding.VARIANT_DOT: "dot_slab"}
+    prev = binding.set_projection_variant(binding.VARIANT_AUTO)
+    try:
+        for pname, (ns, k) in shapes.items():
+            ws = [[binding.DeviceQWeight(n, k, 8, *inputs.make_qweight_device(n, k, 8, "curves", pname, i, c))
+                   for i, n in enumerate(ns)] for c in range(copies)]
+            x = inputs.make_activations_device(16, k, "curves", pname)
+            ys = [torch.empty((16, n), dtype=torch.float32, device="cuda") for n in ns]
+            wsp = binding.alloc_workspace(sum(binding.qgemm_workspace_bytes(n, k, 16) for n in ns))
+            for var, vname in names.items():
+                binding.set_projection_variant(var)
+                curve = {}
+                for m in widths:
+                    if var == binding.VARIANT_DOT and m > 4:
+                        continue
+                    calls = [binding.prepare_qgemm_grouped(ws[c], x, m, ys, wsp, stream) for c in range(copies)]
+                    for c in range(args.warmup):
+                        calls[c % copies]()
+                    # back-to-back batches of `copies` launches, as in a round:
+                    # per-launch time = batch time / copies
+                    ts = []
+                    for r in range(args.steps):
+                        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                        e0.record(stream)
+                        for c in range(copies):
+                            calls[c]()
+                        e1.record(stream)
+                        e1.synchronize()
+                        ts.append(e0.elapsed_time(e1) * 1e3 / copies)
+                    curve[m] = round(float(np.median(ts)), 2)
+                    out["launch_plan"].append([pname, vname, m, args.warmup + args.steps * copies])
+                out["curves"].setdefault(pname, {})[vname] = curve
+            del ws
+    finally:
+        binding.set_projection_variant(prev)
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
+    if args.variant_curves:
+        variant_curves(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only (the verify pass is not sharded); "
               "use --gpus 1", file=sys.stderr)
@@ -283,32 +452,42 @@ def main():
     stream = torch.cuda.current_stream()
     V = stack.vocab
 
-    # untimed pre-pass per width: the target's tokens (and logits), then the
-    # drafter's side -- draft ids with the match rates, or (sampling) draft
-    # distributions q from noisy target logits, draft ids drawn from q, and
-    # the round's uniforms
+    # untimed pre-pass per (width, weight copy): that copy's target tokens
+    # (and logits), then the drafter's side for S draft sets -- draft ids with
+    # the match rates, or (sampling) draft distributions q from noisy target
+    # logits, draft ids drawn from q, and the round's uniforms.  Each copy is
+    # a different synthetic target, so each gets drafts of its own; rounds
+    # cycle through the sets, so the committed counts average S x copies
+    # independent draws per width.
+    S = args.draft_sets
+    sample_ws = binding.alloc_workspace(binding.sample_workspace_bytes(V, max_m)) if sample else None
+    counts_t = torch.from_numpy(inputs.history_counts(V, args.history, "bench", args.config)).cuda() \
+        if filtered else None
     rounds_in = {}
     for m in sweep:
         M = B * m
-        stack.launch_head(M, 0, want_logits=sample, stream=stream)
-        t = stack.argmax[:M].cpu().numpy().reshape(B, m)
-        res = torch.empty((B + B * m,), dtype=torch.int32, device="cuda")   # [accept_len | committed]
-        r = dict(res=res, alen=res[:B], com=res[B:].view(B, m))
-        if sample:
-            z = stack.logits[:m].cpu().numpy()
-            q, d = inputs.draft_distribution(z, args.temperature, args.noise, "bench", args.config, m)
-            r["q"] = torch.from_numpy(np.ascontiguousarray(q)).cuda()
-            r["d"] = torch.from_numpy(d).cuda()
-            r["u"] = torch.from_numpy(inputs.make_uniforms(m, "bench", args.config, m)).cuda()
-            r["ws"] = binding.alloc_workspace(binding.sample_workspace_bytes(V, m))
-            if filtered:
-                r["params"] = binding.sample_params(args.temperature, args.top_k, args.top_p, args.presence,
-                                                    args.frequency)
-                r["counts"] = torch.from_numpy(inputs.history_counts(V, args.history, "bench", args.config)).cuda()
-        else:
-            d = inputs.drafts_match_rate(t, alpha, V, "bench", args.config, m) if m > 1 else None
-            r["d"] = torch.from_numpy(np.ascontiguousarray(d, dtype=np.int32)).cuda() if m > 1 else None
-        rounds_in[m] = r
+        for cp in range(args.copies):
+            stack.launch_head(M, cp, want_logits=sample, stream=stream)
+            t = stack.argmax[:M].cpu().numpy().reshape(B, m)
+            z = stack.logits[:m].cpu().numpy() if sample else None
+            for si in range(S):
+                res = torch.empty((B + B * m,), dtype=torch.int32, device="cuda")   # [accept_len | committed]
+                r = dict(res=res, alen=res[:B], com=res[B:].view(B, m))
+                if sample:
+                    q, d = inputs.draft_distribution(z, args.temperature, args.noise, "bench", args.config, m, cp,
+                                                     si)
+                    r["q"] = torch.from_numpy(np.ascontiguousarray(q)).cuda()
+                    r["d"] = torch.from_numpy(d).cuda()
+                    r["u"] = torch.from_numpy(inputs.make_uniforms(m, "bench", args.config, m, cp, si)).cuda()
+                    r["ws"] = sample_ws
+                    if filtered:
+                        r["params"] = binding.sample_params(args.temperature, args.top_k, args.top_p,
+                                                            args.presence, args.frequency)
+                        r["counts"] = counts_t
+                else:
+                    d = inputs.drafts_match_rate(t, alpha, V, "bench", args.config, m, cp, si) if m > 1 else None
+                    r["d"] = torch.from_numpy(np.ascontiguousarray(d, dtype=np.int32)).cuda() if m > 1 else None
+                rounds_in[(m, cp, si)] = r
     host_res = torch.empty((B + max_m,), dtype=torch.int32).pin_memory()
 
     def accept_call(m, r, prepare=True):
@@ -331,38 +510,42 @@ def main():
     prepared, graphs = {}, {}
     for m in sweep:
         for cp in range(args.copies):
-            if args.graph:
-                graphs[(m, cp)] = stack.capture_calls(B * m, cp, accept_call(m, rounds_in[m], prepare=False),
-                                                      want_logits=sample)
-            else:
-                layers, head = stack.prepare_round(B * m, cp, want_logits=sample, stream=stream)
-                if sample:
-                    prepared[(m, cp)] = (layers, head, accept_call(m, rounds_in[m]))
+            layers = None if args.graph else stack.prepare_round(B * m, cp, want_logits=sample, stream=stream)[0]
+            for si in range(S):
+                r = rounds_in[(m, cp, si)]
+                if args.graph:
+                    graphs[(m, cp, si)] = stack.capture_calls(B * m, cp, accept_call(m, r, prepare=False),
+                                                              want_logits=sample)
+                elif sample:
+                    head = binding.prepare_lmhead(stack.heads[cp], stack.h, B * m, stack.argmax, stack.logits,
+                                                  stack.ws_head, stream)
+                    prepared[(m, cp, si)] = (layers, head, accept_call(m, r))
                 else:
                     # greedy: the head's last workgroup runs the acceptance
                     # (dspk_lmhead_argmax_accept_greedy), no accept launch
-                    r = rounds_in[m]
                     fused = binding.prepare_lmhead_accept_greedy(stack.heads[cp], stack.h, B, m, stack.argmax, None,
                                                                  r["d"], r["alen"], r["com"], stack.ws_head, stream)
-                    prepared[(m, cp)] = (layers, fused, lambda: None)
+                    prepared[(m, cp, si)] = (layers, fused, lambda: None)
 
     # the round's one device-to-host copy: destination views made once
     host_dst = {m: host_res[:B + B * m] for m in sweep}
     host_np = host_res.numpy()           # the same pinned memory, read without torch ops
 
-    def run_round(m: int, copy: int, record: list | None):
-        r = rounds_in[m]
+    def run_round(m: int, k: int, record: list | None):
+        """Round number k at width m: weight copy k % copies, draft set (k // copies) % S."""
+        copy, si = k % args.copies, (k // args.copies) % S
+        r = rounds_in[(m, copy, si)]
         e = [ev() for _ in range(4)] if record is not None else None
         if e: e[0].record(stream)
         if args.graph:
-            gl, gh, ga = graphs[(m, copy)]
+            gl, gh, ga = graphs[(m, copy, si)]
             gl.replay()
             if e: e[1].record(stream)
             gh.replay()
             if e: e[2].record(stream)
             ga.replay()
         else:
-            calls, head, accept = prepared[(m, copy)]
+            calls, head, accept = prepared[(m, copy, si)]
             for f in calls:
                 f()
             if e: e[1].record(stream)
@@ -378,7 +561,7 @@ def main():
     step_copy = 0
     for _ in range(args.warmup):
         for m in sweep:
-            run_round(m, step_copy % args.copies, None)
+            run_round(m, step_copy, None)
             step_copy += 1
 
     # A serving loop's long-lived objects (weights, prepared calls, the torch
@@ -391,6 +574,7 @@ def main():
     # Timed region: K steps of rounds as a serving loop runs them -- launch,
     # one copy and sync, read the accept lengths -- with no timing events.
     committed = 0
+    committed_by_width = {m: 0 for m in sweep}
     faults = 0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -398,12 +582,13 @@ def main():
     for _ in range(args.steps):
         for m in sweep:
             tr = time.perf_counter()
-            run_round(m, step_copy % args.copies, None)
+            run_round(m, step_copy, None)
             for a in host_np[:B]:
                 if a < 0:
                     faults += 1
                 else:
                     committed += int(a)
+                    committed_by_width[m] += int(a)
             walls.append(time.perf_counter() - tr)
             step_copy += 1
     torch.cuda.synchronize()
@@ -415,7 +600,7 @@ def main():
     records = []
     for _ in range(args.steps):
         for m in sweep:
-            run_round(m, step_copy % args.copies, records)
+            run_round(m, step_copy, records)
             step_copy += 1
     torch.cuda.synchronize()
 
@@ -472,6 +657,14 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
+    achievable = None if args.no_extras else achievable_bandwidth(head_b)
+    if achievable is not None:
+        roofline["achievable"] = achievable
+        roofline["frac_of_achievable"] = round(achieved / achievable["GBps"], 4)
+    dense = None
+    if not args.no_extras and args.config == "qwen3-4b":
+        dense = dense27b_section(max(args.steps, 5), max(args.warmup, 2))
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.config, args.bits, min(B * max(sweep), 8), args.cpu_sample_s)
@@ -499,9 +692,16 @@ def main():
         "round_wall_us": {"p50": round(float(np.median(walls)) * 1e6, 1), "max": round(max(walls) * 1e6, 1)},
         "rows_per_s": round(B * sum(sweep) * args.steps / wall, 1),
         "committed_tokens_per_round": round(committed / n_rounds, 3),
+        # per request and round at each width: measured, and the closed form
+        # 1 + sum_{i=1..m-1} alpha^i of independent per-position matches
+        "committed_by_width": None if sample else {
+            str(B * m): {"measured": round(committed_by_width[m] / (args.steps * B), 3),
+                         "expected": [round(float(sum(a ** i for i in range(m))), 3) for a in alpha]}
+            for m in sweep},
         "accept_faults": faults,
         "cap_policy": cap_policy,
         "roofline": roofline,
+        "dense27b": dense,
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(0), "host": platform.node(),
     }

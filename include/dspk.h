@@ -2,12 +2,14 @@
  * dspk.h -- C ABI of the MI355X (gfx950) verify pass of lossless speculative
  * decoding.
  *
- * One verify round, as the "mlx-dspark" wiki summary describes it (section
- * "Architecture", first bullet): the target model runs once over the anchor
- * token plus m draft tokens, the drafts are compared with the target's own
- * logits, and the longest accepted prefix is committed.  Greedy rounds give
- * exactly what plain decoding gives; with temperature > 0 the Leviathan/Chen
- * rule min(1, p/q) makes the committed tokens an exact sample of the target.
+ * A verify round ("mlx-dspark" wiki summary, section "Architecture", first
+ * bullet): the target model evaluates the anchor token and the m drafted
+ * tokens together in one pass; each draft is then checked against the token
+ * distribution the target itself produced at that position, and the drafts up
+ * to the first failed check are kept.  With greedy checks the output is what
+ * plain one-token decoding would give; with temperature > 0 the
+ * Leviathan/Chen min(1, p/q) test keeps the output an exact sample of the
+ * target.
  *
  * The library computes the data-parallel part of that round:
  *   dspk_qgemm_verify   - every projection of the target over the M = m + 1
@@ -132,20 +134,33 @@ size_t dspk_tiled_bytes(int32_t n, int32_t k, int32_t bits);
 int dspk_qweight_pack(const dspk_qweight *w, void *tiles, size_t tiles_bytes, void *stream);
 
 /*
- * Activation rows (x, h) are chunk-major: bf16 [k/8][ldm][8], i.e. element
- * (row i, column r) sits at index ((r / 8) * ldm + i) * 8 + r % 8, ldm >= m.
- * The 8-element pieces of all rows are adjacent, so the 16 rows one MFMA
- * operand needs come in one contiguous 256-byte span.
+ * Activation rows (x, h) are row-major bf16 [m][ld]: element (row i, column r)
+ * at index i * ld + r, ld >= k and ld % 8 == 0, base 16-byte aligned.  So a
+ * projection's bf16 output (y_dtype = DSPK_BF16, ldy % 8 == 0) is directly the
+ * next call's input.
  */
 
 /*
- * Workspace for dspk_qgemm_verify: bytes needed for a weight of n x k read by
- * m rows or fewer, any format (never 0: every call needs one).  A workspace of
- * this size serves every width 1..m, so one buffer can follow a varying draft
- * length.  It holds arrival counters and the
- * partial sums of K-split column blocks.  The workspace must be zero-filled
- * before its FIRST use; every completed call leaves its counters at zero
- * again, so it can be reused as is by calls ordered on one stream.
+ * Workspaces of the projection and head calls (dspk_qgemm_verify,
+ * dspk_qgemm_verify_grouped, dspk_lmhead_argmax,
+ * dspk_lmhead_argmax_accept_greedy).  They hold arrival counters, the head's
+ * row keys and the partial sums of column blocks whose K range is split
+ * between workgroups, at offsets that depend only on the device (not on the
+ * call's shape, width or format).  Contract:
+ *  - zero-fill a workspace once, before its first use;
+ *  - every completed call returns the counters and keys to zero (partial sums
+ *    are always written before they are read), so ONE workspace of at least
+ *    the size each call needs serves any sequence of these calls, of any
+ *    shapes, widths and formats;
+ *  - calls that share a workspace must be ordered on one stream: overlapping
+ *    calls on one workspace race and give wrong results;
+ *  - a sampling workspace (dspk_sample_workspace_bytes) is a different kind:
+ *    it keeps per-call statistics, so do not pass it to these calls, nor
+ *    theirs to the sampling calls, without zero-filling it again.
+ * dspk_qgemm_workspace_bytes(n, k, m) is the size for a weight of n columns
+ * (about 12.6 MB of partial-sum space on a 256-CU device, plus 16 bytes per
+ * 64 columns); it is never 0 for valid arguments, and a buffer of that size
+ * serves every width 1..DSPK_MAX_ROWS and format.
  */
 size_t dspk_qgemm_workspace_bytes(int32_t n, int32_t k, int32_t m);
 
@@ -158,22 +173,51 @@ size_t dspk_qgemm_workspace_bytes(int32_t n, int32_t k, int32_t m);
  * the 1-bit counter-example in "mlx-dspark 0.7.0", "PrismML Bonsai 27B").
  *
  *   w         : tiled weight (see dspk_tiled_weight, dspk_qweight_pack).
- *   x         : bf16 activations, chunk-major [k/8][ldx][8] (see above):
- *               ldx = rows per chunk, m <= ldx <= 65536; 16-byte aligned.
+ *   x         : bf16 activations, row-major [m][ldx] (see above): ldx >= k,
+ *               ldx % 8 == 0, 16-byte aligned, m * ldx * 2 < 2^31.
  *   m         : rows, 1 .. DSPK_MAX_ROWS.
  *   y         : output [m][ldy], element type y_dtype (DSPK_F32 | DSPK_BF16),
  *               ldy >= n; 4-byte aligned.
  *   workspace : >= dspk_qgemm_workspace_bytes(n, k, m) bytes, 256-byte
- *               aligned, zero-filled before first use.
+ *               aligned, zero-filled before first use (see the contract above).
  * Results are deterministic: the same call on the same inputs gives the same
  * bits (the K split is fixed by the shapes, not by scheduling).
  * Errors: DSPK_EINVAL (null or misaligned pointer, n < 1, k % 64, ldx/ldy,
  * m out of 1..32, workspace too small), DSPK_EUNSUPPORTED (bits not in
- * {2, 3, 4, 8, 16}, group != 64), DSPK_EDEVICE.
+ * {2, 3, 4, 8, 16}, group != 64, activation rows of 2 GiB or more),
+ * DSPK_EDEVICE.
  */
 int dspk_qgemm_verify(const dspk_tiled_weight *w, const uint16_t *x, int64_t ldx, int32_t m,
                       void *y, int32_t y_dtype, int64_t ldy,
                       void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * How projection launches are decomposed, process-wide (measurement and
+ * tests; results are within the same error bound either way, and each
+ * decomposition is deterministic):
+ *   DSPK_VARIANT_AUTO    (default) the slab kernel -- one workgroup per
+ *                        16-column tile over the whole K range, no
+ *                        cross-workgroup traffic -- for 8-bit and bf16 calls
+ *                        of at most 16 rows whose tiles are short enough
+ *                        (the weights one CU streams stay under a limit that
+ *                        depends on the rows), else stream-K;
+ *   DSPK_VARIANT_STREAMK persistent workgroups over contiguous K ranges, split
+ *                        column blocks completed by the last workgroup to arrive;
+ *   DSPK_VARIANT_SLAB    the slab kernel for every projection;
+ *   DSPK_VARIANT_DOT     the slab decomposition with the K reduction on the
+ *                        vector ALUs (bf16 dot2 instructions) instead of the
+ *                        matrix cores -- 8-bit weights and m <= 4 only, other
+ *                        calls as DSPK_VARIANT_AUTO.
+ * The vocabulary-head calls are always stream-K.  The initial setting comes
+ * from the environment variable DSPK_VARIANT (auto | streamk | slab | dot).
+ * Returns the previous setting, or DSPK_EINVAL for an unknown value.  Not
+ * synchronised with calls in flight on other threads.
+ */
+#define DSPK_VARIANT_AUTO    0
+#define DSPK_VARIANT_STREAMK 1
+#define DSPK_VARIANT_SLAB    2
+#define DSPK_VARIANT_DOT     3
+int dspk_set_projection_variant(int32_t variant);
 
 /*
  * Grouped form for weights that read the same rows (q/k/v, gate/up): one
@@ -209,8 +253,10 @@ int dspk_qgemm_verify_grouped(int32_t count, const dspk_tiled_weight *w,
 int dspk_qgemm_prefill(const dspk_tiled_weight *w, const uint16_t *x, int64_t ldx, int32_t m,
                        void *y, int32_t y_dtype, int64_t ldy, void *stream);
 
-/* Workspace for dspk_lmhead_argmax at m rows or fewer, any hidden size and
- * format (zero-filled before first use, left zeroed). */
+/* Workspace for dspk_lmhead_argmax (and the fused greedy head) over a
+ * vocabulary of v entries: any hidden size, width 1..DSPK_MAX_ROWS and
+ * format; the same contract as dspk_qgemm_workspace_bytes, and one buffer may
+ * serve both kinds of call. */
 size_t dspk_lmhead_workspace_bytes(int32_t v, int32_t m);
 
 /*
@@ -222,12 +268,12 @@ size_t dspk_lmhead_workspace_bytes(int32_t v, int32_t m);
  * project page leaves ties to floating-point rounding.
  *
  *   w         : vocabulary head, tiled like dspk_qgemm_verify's weights.
- *   h         : bf16 final hidden rows, chunk-major [k/8][ldh][8], m <= ldh,
- *               16-byte aligned.
+ *   h         : bf16 final hidden rows, row-major [m][ldh], ldh >= k,
+ *               ldh % 8 == 0, 16-byte aligned.
  *   argmax    : int32 [m] output.
  *   logits    : float32 [m][ldl] output, or NULL to skip writing logits.
  *   workspace : >= dspk_lmhead_workspace_bytes(v, m), 256-byte aligned,
- *               zero-filled before first use.
+ *               zero-filled before first use (contract above).
  * The result is deterministic (independent of workgroup order).
  */
 int dspk_lmhead_argmax(const dspk_tiled_weight *w, const uint16_t *h, int64_t ldh, int32_t m,
@@ -239,8 +285,9 @@ int dspk_lmhead_argmax(const dspk_tiled_weight *w, const uint16_t *h, int64_t ld
  * dspk_lmhead_argmax over m = b * m_rows rows followed by dspk_accept_greedy
  * on its ids (same argmax, accept_len and committed), with the acceptance run
  * by the head's last workgroup, so a greedy round needs no separate accept
- * launch ("mlx-dspark" wiki summary, "Architecture": the drafts are compared
- * with the target's own logits and the longest accepted prefix committed).
+ * launch ("mlx-dspark" wiki summary, "Architecture": each draft is checked
+ * against the target's own prediction and the drafts before the first
+ * mismatch are kept).
  *
  *   b, m_rows  : requests and rows per request, b * m_rows <= DSPK_MAX_ROWS;
  *                request r owns rows r * m_rows .. r * m_rows + m_rows - 1
@@ -257,7 +304,7 @@ int dspk_lmhead_argmax_accept_greedy(const dspk_tiled_weight *w, const uint16_t 
 
 /*
  * Greedy acceptance for b requests of m_rows rows each ("mlx-dspark" wiki
- * summary, "Architecture": commit the longest accepted prefix; "Key
+ * summary, "Architecture": keep the drafts up to the first mismatch; "Key
  * techniques": a round commits 1 + sum p^i tokens, i.e. always the target's
  * own token after the accepted drafts).
  *
@@ -272,8 +319,11 @@ int dspk_accept_greedy(const int32_t *target_ids, const int32_t *draft_ids,
                        int32_t b, int32_t m_rows,
                        int32_t *accept_len, int32_t *committed, void *stream);
 
-/* Workspace for dspk_accept_sample and dspk_accept_sample_ex (zero-filled before
- * first use, left zeroed). */
+/* Workspace for dspk_accept_sample and dspk_accept_sample_ex: zero-filled
+ * before first use; the calls leave their arrival counter at zero, so one
+ * buffer of the largest (v, m_rows) serves any sequence of sampling calls
+ * ordered on one stream.  Not to be shared with projection or head calls
+ * (see the workspace contract above). */
 size_t dspk_sample_workspace_bytes(int32_t v, int32_t m_rows);
 
 /*
@@ -325,10 +375,11 @@ typedef struct dspk_sample_params {
 
 /*
  * Stochastic acceptance over the penalised, truncated target
- * ("mlx-dspark releases", v0.1.0 notes: top-k / nucleus truncation of both
- * the draft and the target keeps speculative sampling exact for the
- * truncated target; v0.2.0 notes: presence/frequency penalties on the target
- * logits, so the output equals sequential decoding of the penalised target).
+ * ("mlx-dspark releases", v0.1.0 notes: one top-k / top-p filter applied to
+ * the draft and to the target keeps speculative sampling an exact sample of
+ * the filtered target; v0.2.0 notes: presence/frequency penalties act on the
+ * target logits, and the committed tokens are those one-token decoding of
+ * the penalised target would give).
  *
  * Row j's penalised logits: z'_j(c) = z_j(c) - presence * [n_j(c) > 0]
  * - frequency * n_j(c), where n_j(c) = counts[c] + #{i < j : draft_i = c}

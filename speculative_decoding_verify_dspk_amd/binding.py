@@ -72,10 +72,18 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                            "`python -m speculative_decoding_verify_dspk_amd.build`")
+    # torch first: the library needs the HIP runtime under the soname
+    # libamdhip64.so.7, and torch's ROCm wheel brings its own copy under that
+    # name.  With torch loaded, the library binds to that same runtime, so the
+    # streams and device pointers this binding passes (torch's) are valid in
+    # it.  Loaded the other way round, the process would hold two HIP/HSA
+    # runtimes and the one initialised second finds no device.
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER
     sig = {
         "dspk_version": (c_int32, []),
+        "dspk_set_projection_variant": (c_int32, [c_int32]),
         "dspk_last_error": (ctypes.c_char_p, []),
         "dspk_tiled_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
         "dspk_qweight_pack": (c_int32, [P(QWeightDesc), c_void_p, c_size_t, c_void_p]),
@@ -146,23 +154,15 @@ def _rows(t, name: str) -> int:
     return t.stride(0)
 
 
-def _chunks(t, name: str) -> int:
-    """Rows per chunk (ldm) of a chunk-major activation tensor [k/8][ldm][8]."""
-    if t.dim() != 3 or t.shape[2] != 8 or t.stride(2) != 1 or t.stride(1) != 8 or t.stride(0) != 8 * t.shape[1]:
-        raise ValueError(f"{name}: expected a contiguous chunk-major tensor [k/8][ldm][8]")
-    return t.shape[1]
-
-
-def to_chunk_major(x, ldm: int | None = None):
-    """Row-major activations [m][k] (a device tensor of bf16 bit patterns) ->
-    the library's chunk-major layout [k/8][ldm][8]; rows m..ldm-1 are zero.
-    A pure layout change: element (i, r) moves to ((r / 8) * ldm + i) * 8 + r % 8."""
-    import torch
-    m, k = x.shape
-    ldm = m if ldm is None else ldm
-    out = torch.zeros((k // 8, ldm, 8), dtype=x.dtype, device=x.device)
-    out[:, :m, :] = x.reshape(m, k // 8, 8).permute(1, 0, 2)
-    return out
+def _acts(t, name: str) -> int:
+    """Leading dimension of row-major bf16 activation rows [rows][ld] (int16 bit
+    patterns or bfloat16): unit column stride, ld % 8 == 0."""
+    if t.element_size() != 2:
+        raise ValueError(f"{name}: expected bf16 activations (2-byte elements)")
+    ld = _rows(t, name)
+    if ld % 8:
+        raise ValueError(f"{name}: leading dimension {ld} must be a multiple of 8")
+    return ld
 
 
 # ---------------------------------------------------------------- weights
@@ -270,7 +270,7 @@ class Prepared:
 
 def prepare_qgemm(w: DeviceQWeight, x, m: int, y, workspace, stream=None) -> Prepared:
     dt = DSPK_BF16 if y.element_size() == 2 else DSPK_F32
-    return Prepared("dspk_qgemm_verify", ctypes.byref(w.desc), x.data_ptr(), _chunks(x, "x"), m, y.data_ptr(), dt,
+    return Prepared("dspk_qgemm_verify", ctypes.byref(w.desc), x.data_ptr(), _acts(x, "x"), m, y.data_ptr(), dt,
                     _rows(y, "y"), workspace.data_ptr(), workspace.numel(), _stream(stream))
 
 
@@ -280,19 +280,19 @@ def prepare_qgemm_grouped(ws: list, x, m: int, ys: list, workspace, stream=None)
     yptr = (c_void_p * cnt)(*[y.data_ptr() for y in ys])
     ldy = (c_int64 * cnt)(*[_rows(y, "y") for y in ys])
     dt = DSPK_BF16 if ys[0].element_size() == 2 else DSPK_F32
-    return Prepared("dspk_qgemm_verify_grouped", cnt, descs, x.data_ptr(), _chunks(x, "x"), m, yptr, dt, ldy,
+    return Prepared("dspk_qgemm_verify_grouped", cnt, descs, x.data_ptr(), _acts(x, "x"), m, yptr, dt, ldy,
                     workspace.data_ptr(), workspace.numel(), _stream(stream))
 
 
 def prepare_lmhead(w: DeviceQWeight, h, m: int, argmax, logits, workspace, stream=None) -> Prepared:
-    return Prepared("dspk_lmhead_argmax", ctypes.byref(w.desc), h.data_ptr(), _chunks(h, "h"), m, argmax.data_ptr(),
+    return Prepared("dspk_lmhead_argmax", ctypes.byref(w.desc), h.data_ptr(), _acts(h, "h"), m, argmax.data_ptr(),
                     _ptr(logits), 0 if logits is None else _rows(logits, "logits"), workspace.data_ptr(),
                     workspace.numel(), _stream(stream))
 
 
 def prepare_lmhead_accept_greedy(w: DeviceQWeight, h, b: int, m_rows: int, argmax, logits, draft_ids, accept_len,
                                  committed, workspace, stream=None) -> Prepared:
-    return Prepared("dspk_lmhead_argmax_accept_greedy", ctypes.byref(w.desc), h.data_ptr(), _chunks(h, "h"), b,
+    return Prepared("dspk_lmhead_argmax_accept_greedy", ctypes.byref(w.desc), h.data_ptr(), _acts(h, "h"), b,
                     m_rows, argmax.data_ptr(), _ptr(logits), 0 if logits is None else _rows(logits, "logits"),
                     _ptr(draft_ids), accept_len.data_ptr(), committed.data_ptr(), workspace.data_ptr(),
                     workspace.numel(), _stream(stream))
@@ -325,6 +325,17 @@ def version() -> int:
     return lib().dspk_version()
 
 
+VARIANT_AUTO, VARIANT_STREAMK, VARIANT_SLAB, VARIANT_DOT = 0, 1, 2, 3
+
+
+def set_projection_variant(variant: int) -> int:
+    """Process-wide projection decomposition; returns the previous setting."""
+    prev = lib().dspk_set_projection_variant(int(variant))
+    if prev < 0:
+        _check(prev)
+    return prev
+
+
 def qgemm_workspace_bytes(n: int, k: int, m: int) -> int:
     return lib().dspk_qgemm_workspace_bytes(n, k, m)
 
@@ -344,8 +355,8 @@ def alloc_workspace(nbytes: int, device="cuda"):
 
 
 def qgemm_verify(w: DeviceQWeight, x, m: int, y, workspace=None, stream=None) -> None:
-    """x: chunk-major activations [k/8][ldm][8] (see to_chunk_major)."""
-    ldx, ldy = _chunks(x, "x"), _rows(y, "y")
+    """x: row-major bf16 activation rows [>= m][ldx]."""
+    ldx, ldy = _acts(x, "x"), _rows(y, "y")
     dt = DSPK_BF16 if y.element_size() == 2 else DSPK_F32
     ws_bytes = 0 if workspace is None else workspace.numel()
     _check(lib().dspk_qgemm_verify(ctypes.byref(w.desc), x.data_ptr(), ldx, m, y.data_ptr(), dt, ldy,
@@ -359,7 +370,7 @@ def qgemm_verify_grouped(ws: list, x, m: int, ys: list, workspace=None, stream=N
     ldy = (c_int64 * cnt)(*[_rows(y, "y") for y in ys])
     dt = DSPK_BF16 if ys[0].element_size() == 2 else DSPK_F32
     ws_bytes = 0 if workspace is None else workspace.numel()
-    _check(lib().dspk_qgemm_verify_grouped(cnt, descs, x.data_ptr(), _chunks(x, "x"), m, yptr, dt, ldy,
+    _check(lib().dspk_qgemm_verify_grouped(cnt, descs, x.data_ptr(), _acts(x, "x"), m, yptr, dt, ldy,
                                            _ptr(workspace), ws_bytes, _stream(stream)))
 
 
@@ -378,7 +389,7 @@ def prepare_qgemm_prefill(w: DeviceQWeight, x, m: int, y, stream=None) -> Prepar
 
 def lmhead_argmax(w: DeviceQWeight, h, m: int, argmax, logits=None, workspace=None, stream=None) -> None:
     ldl = 0 if logits is None else _rows(logits, "logits")
-    _check(lib().dspk_lmhead_argmax(ctypes.byref(w.desc), h.data_ptr(), _chunks(h, "h"), m, argmax.data_ptr(),
+    _check(lib().dspk_lmhead_argmax(ctypes.byref(w.desc), h.data_ptr(), _acts(h, "h"), m, argmax.data_ptr(),
                                     _ptr(logits), ldl, _ptr(workspace),
                                     0 if workspace is None else workspace.numel(), _stream(stream)))
 
@@ -386,7 +397,7 @@ def lmhead_argmax(w: DeviceQWeight, h, m: int, argmax, logits=None, workspace=No
 def lmhead_argmax_accept_greedy(w: DeviceQWeight, h, b: int, m_rows: int, argmax, draft_ids, accept_len, committed,
                                 logits=None, workspace=None, stream=None) -> None:
     ldl = 0 if logits is None else _rows(logits, "logits")
-    _check(lib().dspk_lmhead_argmax_accept_greedy(ctypes.byref(w.desc), h.data_ptr(), _chunks(h, "h"), b, m_rows,
+    _check(lib().dspk_lmhead_argmax_accept_greedy(ctypes.byref(w.desc), h.data_ptr(), _acts(h, "h"), b, m_rows,
                                                   argmax.data_ptr(), _ptr(logits), ldl, _ptr(draft_ids),
                                                   accept_len.data_ptr(), committed.data_ptr(), _ptr(workspace),
                                                   0 if workspace is None else workspace.numel(), _stream(stream)))

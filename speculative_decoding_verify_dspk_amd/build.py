@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdspk.so")
-SOURCES = ["qgemm.hip", "prefill.hip", "pack.hip", "accept.hip", "api.cpp", "policy.cpp"]
+PROBE_LIB = os.path.join(PKG, "libdspk_probe.so")      # measurement only: the streaming-read probe
+SOURCES = ["qgemm.hip", "slab.hip", "prefill.hip", "pack.hip", "accept.hip", "api.cpp", "plan.cpp", "policy.cpp"]
 
 # Packed fp32 instructions are kept out of every HIP object (the compiler
 # would otherwise form them from ordinary float code).
@@ -51,8 +52,17 @@ def build(out: str = LIB, quiet: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, out)
+    # the benchmark's streaming probe, a library of its own
+    pobj = os.path.join(objdir, "probe.hip.o")
+    _compile(os.path.join(CSRC, "probe.hip"), pobj)
+    ptmp = PROBE_LIB + ".tmp"
+    r = subprocess.run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", ptmp, pobj],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link of the probe failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(ptmp, PROBE_LIB)
     if not quiet:
-        print(f"built {out}")
+        print(f"built {out} and {PROBE_LIB}")
     return out
 
 

@@ -3,7 +3,10 @@
 // "Architecture"; "mlx-dspark 0.7.0", "How it works").
 #include <math.h>
 
+#include <hip/hip_runtime.h>
+
 #include "dspk_internal.h"
+#include "sample_layout.h"
 
 namespace dspk {
 namespace {
@@ -31,18 +34,13 @@ __global__ void accept_greedy_kernel(const int32_t *__restrict__ t, const int32_
 }
 
 // -------------------------------------------------------------- sampling
-// Workspace layout (bytes): [0, 256) arrival counter; then per (row, chunk):
-// stats {max of z'/T, sum exp(z'/T - max)}, the fault flag and the max of q;
-// then per chunk the masses {residual, p} of the row that supplies the final
-// draw; then per (row, distribution) the truncation record; then, used only
-// when truncating, per (row, distribution) the first-level histograms of
-// each slice of the row and the first-level bin of every entry.
+// Workspace: see sample_layout.h.
 constexpr int CH = kSampleChunk;
 constexpr int TPB = 256;
 constexpr int EPT = CH / TPB;    // logits per thread per chunk
 constexpr int FT = 1024;         // threads of a truncation workgroup
-constexpr int NB = 2048;         // histogram bins per level
-constexpr int SLICE = 8192;      // entries per workgroup of the binning pass (<= 2^13)
+constexpr int NB = kSampleBins;  // histogram bins per level
+constexpr int SLICE = kSampleSlice;
 constexpr int BT = 512;          // threads of a binning workgroup
 static_assert(SLICE <= 8192, "the binning histogram's 32-bit mass halves hold 2^13 entries");
 
@@ -51,6 +49,7 @@ struct Trunc {
     float mass;                  // kept mass (of p, or of q as supplied)
     int32_t pad;
 };
+static_assert(sizeof(Trunc) == 16, "truncation record size is fixed by the workspace layout");
 
 struct SampleWs {
     uint32_t *counter;
@@ -65,42 +64,8 @@ struct SampleWs {
     int nslices, vpad;
 };
 
-__host__ __device__ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
-
-struct WsLayout {
-    size_t stats, flags, qmax, mass, trunc, pcnt, pmass, bin1, total;
-    int nslices, vpad;
-};
-
-__host__ __device__ inline WsLayout ws_layout(int rows, int v) {
-    const size_t nchunks = (size_t)(v + CH - 1) / CH;
-    WsLayout L;
-    L.nslices = (v + SLICE - 1) / SLICE;
-    L.vpad = (v + 127) / 128 * 128;
-    const size_t nh = (size_t)rows * 2 * L.nslices * NB;
-    size_t o = 256;
-    L.stats = o;
-    o += align256(rows * nchunks * sizeof(float2));
-    L.flags = o;
-    o += align256(rows * nchunks * sizeof(int32_t));
-    L.qmax = o;
-    o += align256(rows * nchunks * sizeof(float));
-    L.mass = o;
-    o += align256(nchunks * sizeof(float2));
-    L.trunc = o;
-    o += align256((size_t)rows * 2 * sizeof(Trunc));
-    L.pcnt = o;
-    o += align256(nh * sizeof(uint32_t));
-    L.pmass = o;
-    o += align256(nh * sizeof(unsigned long long));
-    L.bin1 = o;
-    o += align256((size_t)rows * 2 * L.vpad * sizeof(uint16_t));
-    L.total = o;
-    return L;
-}
-
-__host__ __device__ inline SampleWs carve(void *ws, int rows, int v) {
-    const WsLayout L = ws_layout(rows, v);
+__device__ inline SampleWs carve(void *ws, int rows, int v) {
+    const SampleWsLayout L = sample_ws_layout(rows, v);
     char *p = (char *)ws;
     SampleWs s;
     s.counter = (uint32_t *)p;
@@ -139,9 +104,9 @@ struct SampleArgs {
 
 // Penalised, temperature-scaled logit of column col in row j ("mlx-dspark
 // releases", v0.2.0 notes: OpenAI presence/frequency penalties on the target
-// logits, so that the output equals sequential decoding of the penalised
-// target).  Row j is reached only when drafts 0..j-1 were accepted, so its
-// counts include them; drafts are in LDS (s_d).  bloom (or NULL): a 1024-bit
+// logits; the committed tokens are those one-token decoding of the penalised
+// target would give).  Row j is reached only when drafts 0..j-1 were accepted,
+// so its counts include them; drafts are in LDS (s_d).  bloom (or NULL): a 1024-bit
 // filter of the columns of drafts 0..j-1 -- a clear bit means none of them
 // is col, and the scan over the drafts is skipped.
 // hist: counts[col] (0 without counts), loaded by the caller.
@@ -290,8 +255,8 @@ __global__ __launch_bounds__(TPB) void sample_stats_kernel(const SampleArgs A) {
     }
 }
 
-// Truncation of one distribution ("mlx-dspark releases", v0.1.0 notes:
-// nucleus / top-k truncation of both the draft and the target).  Entries are
+// Truncation of one distribution ("mlx-dspark releases", v0.1.0 notes: the
+// same top-k / top-p filter cuts down the target and the draft).  Entries are
 // ordered by value (larger first, then the smaller column): their order keys
 // are unique 64-bit values, so each bound is one key.  Top-k keeps the first
 // k; top-p then keeps an entry iff the kept mass before it is below top_p
@@ -1195,7 +1160,6 @@ __global__ __launch_bounds__(TPB) void sample_decide_kernel(const SampleArgs A) 
 
 }  // namespace
 
-size_t sample_workspace_bytes(int32_t v, int32_t m_rows) { return ws_layout(m_rows, v).total; }
 
 hipError_t launch_accept_greedy(const int32_t *t, const int32_t *d, int32_t b, int32_t m_rows,
                                 int32_t *accept_len, int32_t *committed, hipStream_t s) {

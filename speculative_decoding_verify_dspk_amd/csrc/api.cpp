@@ -69,15 +69,16 @@ int check_tiled(const dspk_tiled_weight *w, const char *who) {
     return DSPK_OK;
 }
 
-// Activations are chunk-major: [k/8][ldm][8] bf16, ldm >= m rows per chunk.
-int check_rows(const uint16_t *x, int64_t ldm, int32_t m, int32_t k, const char *who) {
+// Activations are row-major bf16 [m][ldx]: ldx >= k, ldx % 8 == 0 and a
+// 16-byte aligned base, so every 8-element piece a lane loads is aligned.
+int check_rows(const uint16_t *x, int64_t ldx, int32_t m, int32_t k, const char *who) {
     if (m < 1 || m > DSPK_MAX_ROWS) return fail(DSPK_EINVAL, "%s: m=%d out of 1..%d", who, m, DSPK_MAX_ROWS);
     if (x == nullptr || !aligned(x, 16))
         return fail(DSPK_EINVAL, "%s: activations must be a non-NULL 16-byte aligned device pointer", who);
-    if (ldm < m || ldm > 65536)
-        return fail(DSPK_EINVAL, "%s: ldm=%lld must be in m=%d .. 65536", who, (long long)ldm, m);
-    if ((int64_t)k * ldm >= ((int64_t)1 << 31))
-        return fail(DSPK_EUNSUPPORTED, "%s: activation buffer too large (k * ldm >= 2^31)", who);
+    if (ldx < k || ldx % 8)
+        return fail(DSPK_EINVAL, "%s: ldx=%lld must be >= k=%d and a multiple of 8", who, (long long)ldx, k);
+    if ((int64_t)m * ldx * 2 >= ((int64_t)1 << 31))
+        return fail(DSPK_EUNSUPPORTED, "%s: activation rows span 2 GiB or more (m * ldx * 2 >= 2^31)", who);
     return DSPK_OK;
 }
 
@@ -143,6 +144,10 @@ int qgemm_common(int32_t count, const dspk_tiled_weight *w, const uint16_t *x, i
         P.cg_begin = cg;
         cg += (w[i].n + dspk::kBlockCols - 1) / dspk::kBlockCols;
     }
+    if (pl.slab_waves > 0 && pl.dot)
+        return launch_result(dspk::launch_qgemm_dot(L, pl.slab_waves, (hipStream_t)stream), who);
+    if (pl.slab_waves > 0)
+        return launch_result(dspk::launch_qgemm_slab(L, w[0].bits, pl.slab_waves, (hipStream_t)stream), who);
     return launch_result(dspk::launch_qgemm(L, w[0].bits, pl.grid, (hipStream_t)stream), who);
 }
 
@@ -150,7 +155,15 @@ int qgemm_common(int32_t count, const dspk_tiled_weight *w, const uint16_t *x, i
 
 extern "C" {
 
-int dspk_version(void) { return 200; }
+int dspk_version(void) { return 300; }
+
+int dspk_set_projection_variant(int32_t variant) {
+    const int prev = dspk::set_projection_variant(variant);
+    if (prev < 0)
+        return fail(DSPK_EINVAL, "dspk_set_projection_variant: variant=%d (0 auto, 1 stream-K, 2 slab, 3 dot)",
+                    variant);
+    return prev;
+}
 
 const char *dspk_last_error(void) { return g_err.c_str(); }
 
@@ -199,15 +212,9 @@ int dspk_qweight_pack(const dspk_qweight *w, void *tiles, size_t tiles_bytes, vo
 
 size_t dspk_qgemm_workspace_bytes(int32_t n, int32_t k, int32_t m) {
     if (n < 1 || k < DSPK_GROUP || k % DSPK_GROUP || m < 1 || m > DSPK_MAX_ROWS) return 0;
-    // Enough for every width up to m: narrower launches use more workgroups
-    // (two per CU up to 16 rows, one above), so both row-tile classes count.
-    size_t most = 0;
-    for (int mm : {m < 16 ? m : 16, m})
-        for (int bits : {2, 3, 4, 8, 16}) {   // the plan depends on the format only through the stage depth
-            const size_t b = dspk::plan_gemm(1, &n, k, mm, bits, false).ws_bytes;
-            most = b > most ? b : most;
-        }
-    return most;
+    // offsets are fixed (the partial-sum region is sized for the largest
+    // grid), so the size depends on n only and serves every width and format
+    return dspk::plan_gemm(1, &n, k, m, 8, false).ws_bytes;
 }
 
 int dspk_qgemm_verify(const dspk_tiled_weight *w, const uint16_t *x, int64_t ldx, int32_t m, void *y,
@@ -226,15 +233,7 @@ int dspk_qgemm_verify_grouped(int32_t count, const dspk_tiled_weight *w, const u
 
 size_t dspk_lmhead_workspace_bytes(int32_t v, int32_t m) {
     if (v < 1 || m < 1 || m > DSPK_MAX_ROWS) return 0;
-    // the largest plan over hidden sizes, formats (their grids differ) and
-    // every width up to m
-    size_t most = 0;
-    for (int mm : {m < 16 ? m : 16, m})
-        for (int bits : {2, 3, 4, 8, 16}) {
-            const size_t b = dspk::plan_gemm(1, &v, 1 << 20, mm, bits, true).ws_bytes;
-            most = b > most ? b : most;
-        }
-    return most;
+    return dspk::plan_gemm(1, &v, DSPK_GROUP, m, 8, true).ws_bytes;
 }
 
 static int lmhead_common(const char *who, const dspk_tiled_weight *w, const uint16_t *h, int64_t ldh, int32_t m,

@@ -1,7 +1,7 @@
 // Internal declarations shared by the C-ABI layer and the HIP kernels.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -75,7 +75,7 @@ struct GemmProblem {
 
 struct GemmLaunch {
     GemmProblem p[kMaxGrouped];
-    const uint16_t *x;        // bf16 rows, chunk-major [k/8][ldx][8]
+    const uint16_t *x;        // bf16 rows, row-major [m][ldx] (ldx % 8 == 0, 16-byte aligned)
     int64_t ldx;
     int32_t count;
     int32_t m;
@@ -88,7 +88,7 @@ struct GemmLaunch {
     // workspace
     int32_t pairs;            // > 0: workgroups b and b + pairs share a CU (weighted split), else 0
     uint32_t *counters;       // [total_cg][4] arrival counters of split blocks
-    float *partial;           // [grid][2][4][MT][64][4] partial sums of split blocks
+    float *partial;           // [grid][2][4][MT][64][4] partial sums of split blocks (MT: this launch's row tiles)
     // vocabulary-head epilogue (argmax kernel only)
     int32_t *argmax;
     float *logits;
@@ -117,16 +117,71 @@ struct PrefillArgs {
 hipError_t launch_prefill(const PrefillArgs &a, int bits, hipStream_t s);
 
 // Launch plan of one (possibly grouped) projection call (host side).
+//
+// Workspace of the projection and head kernels, at offsets that depend on
+// nothing but the device's CU count, so that one buffer can serve any
+// sequence of projection and head calls ordered on one stream:
+//   [0, 256)            head arrival counter (reset by the head's last workgroup)
+//   [256, 512)          row keys of the head argmax, kMaxRows x 8 B (reset likewise)
+//   [512, 512 + P)      partial sums of split blocks, P = partial_region_bytes():
+//                       every piece is written before it is read, so stale
+//                       contents are harmless
+//   [512 + P, ...)      arrival counters, 4 per 64-column block of the call
+//                       (each reset by the last arrival of its block)
+// Every completed call leaves the counters, keys and arrival word at zero.
+constexpr int kMaxOcc = 3;          // most workgroups per CU of any kernel_occ()
+constexpr size_t kWsHead = 512;     // arrival counter + row keys
+static_assert(kernel_occ(2, 1, true) <= kMaxOcc && kernel_occ(8, 1, true) <= kMaxOcc &&
+                  kernel_occ(8, 2, true) <= kMaxOcc && kernel_occ(2, 2, true) <= kMaxOcc &&
+                  kernel_occ(8, 1, false) <= kMaxOcc && kernel_occ(8, 2, false) <= kMaxOcc &&
+                  kernel_occ(2, 1, false) <= kMaxOcc && kernel_occ(2, 2, false) <= kMaxOcc,
+              "the partial-sum region is sized for kMaxOcc workgroups per CU");
+// bytes of the partial-sum region: [grid][2 sides][4 waves][MT <= 2][64 lanes][4 floats]
+constexpr size_t partial_region_bytes(int cus) {
+    return (size_t)kMaxOcc * (size_t)cus * 2 * kWavesPerWG * 2 * kWave * 16;
+}
+// How a projection launch is decomposed (head launches are always stream-K):
+//   kStreamK: persistent workgroups over contiguous quad ranges (qgemm.hip);
+//   kSlab:    one workgroup per 16-column tile over the whole K (slab.hip),
+//             for launches whose tiles all fit on the device at once;
+//   kDot:     the slab decomposition with the K reduction on the vector ALUs
+//             (v_dot2_f32_bf16) instead of the matrix cores: 8-bit weights,
+//             at most kDotMaxRows rows (other calls fall back to kAuto).
+// kAuto picks by shape; the others force a decomposition (measurement, tests).
+enum Variant : int { kAuto = 0, kStreamK = 1, kSlab = 2, kDot = 3 };
+constexpr int kDotMaxRows = 4;
+// Slab kernels: 8-bit and bf16 weights at up to kSlabLdsMaxRows rows stage
+// the activations in LDS; other calls keep them in registers.  kAuto takes
+// the slab kernel for 8-bit and bf16 calls of at most kSlabLdsMaxRows rows
+// when the weights one CU streams for its tiles (tiles per CU x 16 x k) are
+// at most kSlabAutoWeightsNarrow (<= 8 rows) or kSlabAutoWeightsWide (9..16
+// rows).  Per-launch rocprof durations, slab vs stream-K, 1 / 8 / 16 rows:
+//   Qwen3-4B o  (160 tiles, k 4096)   6.8 / 7.4 / 8.0  vs 10.3 / 10.5 / 11.0 us
+//   Qwen3-4B gate/up (1216, k 2560)  16.1 / 17.7 / 19.1 vs 18.0 / 18.7 / 20.0
+//   27B down    (320 tiles, k 17408) 26.2 / 34.6 / 43.2 vs 22.6 / 22.9 / 23.9
+//   9B gate/up  (1536 tiles, k 4096) 25.2 / 28.8 / 32.9 vs 24.6 / 24.6 / 25.7
+constexpr int kSlabLdsMaxRows = 16;
+constexpr int64_t kSlabAutoWeightsNarrow = 320 * 1024;
+constexpr int64_t kSlabAutoWeightsWide = 96 * 1024;
+int projection_variant();               // the process-wide setting (DSPK_VARIANT, or the setter)
+int set_projection_variant(int v);      // previous setting, or -1 if v is not a Variant
+
 struct GemmPlan {
     int32_t nst, nq, quads, grid, total_cg;
+    int32_t slab_waves;       // > 0: slab kernel with this many waves per workgroup (grid = 4 * total_cg)
+    int32_t dot;              // with slab_waves: the dot-product form of the slab kernel
     int32_t pairs;            // see GemmLaunch::pairs
     bool fits;                // quads * grid < 2^31 (the kernel's index range)
     size_t off_counters, off_keys, off_partial, ws_bytes;
 };
 GemmPlan plan_gemm(int count, const int32_t *n, int32_t k, int32_t m, int bits, bool argmax);
+// the same plan for a given CU count (host tests)
+GemmPlan plan_gemm_cus(int count, const int32_t *n, int32_t k, int32_t m, int bits, bool argmax, int cus);
 int device_cus();
 
 hipError_t launch_qgemm(const GemmLaunch &L, int bits, int grid, hipStream_t s);
+hipError_t launch_qgemm_slab(const GemmLaunch &L, int bits, int waves, hipStream_t s);
+hipError_t launch_qgemm_dot(const GemmLaunch &L, int waves, hipStream_t s);   // 8-bit, m <= kDotMaxRows
 hipError_t launch_lmhead(const GemmLaunch &L, int bits, int grid, hipStream_t s);
 
 // Acceptance kernels.

@@ -31,6 +31,8 @@
 // the dword (scale | bias << 16) of group KU/64 * u + g of column
 // 64 b + 16 t + c.  Columns past n and K past k hold zeros (code 0, scale 0,
 // bias 0).
+#include <hip/hip_runtime.h>
+
 #include "dspk_internal.h"
 
 namespace dspk {
@@ -143,12 +145,6 @@ __global__ __launch_bounds__(64) void pack_kernel(int32_t n, int32_t k, const un
 }
 
 }  // namespace
-
-size_t tiled_bytes(int32_t n, int32_t k, int bits) {
-    if (n < 1 || k < 64 || k % 64 || !supported_bits(bits)) return 0;
-    const size_t nb = ((size_t)n + 63) / 64, nst = ((size_t)k + tile_k(bits) - 1) / tile_k(bits);
-    return nb * nst * (size_t)tile_unit_bytes(bits);
-}
 
 hipError_t launch_pack(int32_t n, int32_t k, int bits, const void *codes, const uint16_t *scales,
                        const uint16_t *biases, void *tiles, hipStream_t s) {

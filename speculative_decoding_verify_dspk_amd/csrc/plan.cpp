@@ -1,0 +1,134 @@
+// Host-side planning of the verify-pass launches: workgroup counts, the
+// stream-K split of a projection, workspace offsets and buffer sizes.  No
+// kernel code lives here, so the argument checks and plans of the C ABI can be
+// built and exercised on a host without a GPU (with sanitizers).
+#include <hip/hip_runtime_api.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "dspk_internal.h"
+#include "sample_layout.h"
+
+namespace dspk {
+
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        cached[dev] = cus;
+    }
+    return cached[dev];
+}
+
+namespace {
+int variant_from_env() {
+    const char *e = getenv("DSPK_VARIANT");
+    if (e == nullptr || strcmp(e, "auto") == 0) return kAuto;
+    if (strcmp(e, "streamk") == 0) return kStreamK;
+    if (strcmp(e, "slab") == 0) return kSlab;
+    if (strcmp(e, "dot") == 0) return kDot;
+    return kAuto;
+}
+std::atomic<int> g_variant{-1};
+}  // namespace
+
+int projection_variant() {
+    int v = g_variant.load(std::memory_order_relaxed);
+    if (v < 0) {
+        int expected = -1;
+        g_variant.compare_exchange_strong(expected, variant_from_env());
+        v = g_variant.load(std::memory_order_relaxed);
+    }
+    return v;
+}
+
+int set_projection_variant(int v) {
+    if (v != kAuto && v != kStreamK && v != kSlab && v != kDot) return -1;
+    const int prev = projection_variant();
+    g_variant.store(v, std::memory_order_relaxed);
+    return prev;
+}
+
+// Waves per workgroup of the slab kernel for `slabs` tiles, or 0 when the
+// tiles would not all be resident at once (then stream-K keeps every CU
+// streaming to the end).  At most 128 VGPRs per lane, a CU holds 16 waves:
+// one workgroup of 16, two of 8 or four of 4; the most waves per tile that
+// still fit all tiles are taken, for the most loads in flight per tile.
+static int slab_waves_for(int64_t slabs, int cus) {
+    if (slabs <= cus) return 16;
+    if (slabs <= 2 * (int64_t)cus) return 8;
+    if (slabs <= 4 * (int64_t)cus) return 4;
+    return 0;
+}
+
+// The automatic choice: the slab kernel with activations in LDS (8-bit and
+// bf16, at most 16 rows) when the weights a CU streams for its share of the
+// tiles stay small -- it saves the stream-K kernel's split-block exchange and
+// most of its small loads, but a CU given two long tiles (or many) streams
+// them alone at the end.  Limits from per-launch rocprof durations of the
+// 4B-, 9B- and 27B-shaped layers at 1, 8 and 16 rows (8-bit and bf16).
+static bool slab_pays(int bits, int m, int64_t slabs, int32_t k, int cus) {
+    if (!(bits == 8 || bits == 16) || m > kSlabLdsMaxRows) return false;
+    const int64_t per_cu = (slabs + cus - 1) / cus;               // tiles per CU
+    const int64_t weights = per_cu * 16 * (int64_t)k;             // weights one CU streams
+    return weights <= (m <= 8 ? kSlabAutoWeightsNarrow : kSlabAutoWeightsWide);
+}
+
+GemmPlan plan_gemm_cus(int count, const int32_t *n, int32_t k, int32_t m, int bits, bool argmax, int cus) {
+    GemmPlan p{};
+    p.nst = (k + tile_k(bits) - 1) / tile_k(bits);
+    p.nq = (p.nst + kWavesPerWG - 1) / kWavesPerWG;
+    int64_t blocks = 0;
+    for (int i = 0; i < count; ++i) blocks += (n[i] + kBlockCols - 1) / kBlockCols;
+    p.total_cg = (int32_t)blocks;
+    const int64_t quads = blocks * p.nq;
+    const int mt = m <= 16 ? 1 : 2;
+    // OCC workgroups per CU; never more workgroups than quads
+    const int64_t slots = (int64_t)kernel_occ(bits, mt, argmax) * cus;
+    const int64_t grid = quads < slots ? quads : slots;
+    p.grid = grid < 1 ? 1 : (int32_t)grid;
+    // a full grid of two workgroups per CU runs as CU pairs (weighted split)
+    p.pairs = (kernel_occ(bits, mt, argmax) == 2 && p.grid == 2 * cus) ? cus : 0;
+    // the kernel splits quads with 32-bit products
+    p.fits = quads * p.grid < ((int64_t)1 << 31);
+    p.quads = p.fits ? (int32_t)quads : 0;
+    p.slab_waves = 0;
+    p.dot = 0;
+    if (!argmax) {
+        int v = projection_variant();
+        if (v == kDot && !(bits == 8 && m <= kDotMaxRows)) v = kAuto;
+        const int64_t slabs = 4 * blocks;
+        if (v == kSlab || v == kDot)
+            p.slab_waves = slab_waves_for(slabs, cus) > 0 ? slab_waves_for(slabs, cus) : 4;
+        else if (v == kAuto && slab_pays(bits, m, slabs, k, cus))
+            p.slab_waves = slab_waves_for(slabs, cus) > 0 ? slab_waves_for(slabs, cus) : 4;
+        if (slabs > 0x7fffffff) p.slab_waves = 0;
+        p.dot = (v == kDot && p.slab_waves > 0) ? 1 : 0;
+    }
+    // fixed offsets (see the workspace layout in dspk_internal.h)
+    p.off_keys = 256;
+    p.off_partial = kWsHead;
+    p.off_counters = kWsHead + partial_region_bytes(cus);
+    p.ws_bytes = (p.off_counters + (size_t)blocks * kWavesPerWG * 4 + 255) / 256 * 256;
+    return p;
+}
+
+GemmPlan plan_gemm(int count, const int32_t *n, int32_t k, int32_t m, int bits, bool argmax) {
+    return plan_gemm_cus(count, n, k, m, bits, argmax, device_cus());
+}
+
+size_t tiled_bytes(int32_t n, int32_t k, int bits) {
+    if (n < 1 || k < 64 || k % 64 || !supported_bits(bits)) return 0;
+    const size_t nb = ((size_t)n + 63) / 64, nst = ((size_t)k + tile_k(bits) - 1) / tile_k(bits);
+    return nb * nst * (size_t)tile_unit_bytes(bits);
+}
+
+size_t sample_workspace_bytes(int32_t v, int32_t m_rows) { return sample_ws_layout(m_rows, v).total; }
+
+}  // namespace dspk

@@ -24,6 +24,8 @@
 // * Two workgroups per CU (LDS <= 68 KiB each): one stages while the other
 //   computes.  Row blocks vary fastest in the grid, so the workgroups that
 //   run together share their weight units in L2.
+#include <hip/hip_runtime.h>
+
 #include "decode.h"
 #include "dspk_internal.h"
 

@@ -40,6 +40,8 @@
 // * Head: row maxima fold into one 64-bit key per row by atomic max; the
 //   last workgroup writes the ids (and, on request, runs the greedy
 //   acceptance on them).
+#include <hip/hip_runtime.h>
+
 #include "decode.h"
 #include "dspk_internal.h"
 
@@ -137,10 +139,7 @@ __device__ __forceinline__ int quad_owner(int quads, int groups, int q) {
 // range, which the earlier workgroup splits kLeadNum / kLeadDen : rest with
 // the later one.  Ranks number the workgroups in memory order (pair p: ranks
 // 2p, 2p + 1); with pairs == 0 the split is plain equal.
-#ifndef DSPK_LEAD_NUM
-#define DSPK_LEAD_NUM 10
-#endif
-constexpr uint32_t kLeadNum = DSPK_LEAD_NUM, kLeadDen = 16;
+constexpr uint32_t kLeadNum = 10, kLeadDen = 16;   // swept 8..12 sixteenths on the head: 10 fastest
 // The earlier workgroup takes max(ceil(n / 2), floor(n * f)) of a pair's n
 // quads: rounding down alone would hand the later one the larger piece of a
 // short range (n = 3: 1 and 2).  A pair's range has n >= 2 quads (quads >=
@@ -273,13 +272,16 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT, ARGMAX)) void qgemm_kerne
     // they move to a new block.
     int ib_gb = -1;
     const unsigned char *ib_base = nullptr;
-    // activations: chunk-major [k/8][ldm][8] bf16; byte offset of this lane's
-    // piece (chunk 2*j, row 16*mt + c) within a group's eight chunks
-    const int LDM = (int)KL->ldx;
+    // activations: row-major [m][ldx] bf16.  Lane (c, j) reads the 16-byte
+    // piece of row 16*mt + c (clamped to the last row) at K offset 16*j + 8*h
+    // of each group: a wave-uniform byte offset per (unit, group, half) plus
+    // this fixed lane offset.  The two halves of a group read the two halves
+    // of the same 64-byte span of each row, so the second load hits L1.
+    const uint32_t LDXB = (uint32_t)KL->ldx * 2u;
     const unsigned char *const xbase = (const unsigned char *)KL->x;
     uint32_t xlane[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) xlane[mt] = (uint32_t)(2 * j * LDM + min(16 * mt + c, M - 1)) * 16u;
+    for (int mt = 0; mt < MT; ++mt) xlane[mt] = (uint32_t)min(16 * mt + c, M - 1) * LDXB + 32u * (uint32_t)j;
 
     // Request this wave's unit of quad u and its activation fragments into
     // slot s.  Lane (c, j) takes 16 bytes of each 1 KiB code slot and the
@@ -298,15 +300,15 @@ __global__ __launch_bounds__(256, kernel_occ(BITS, MT, ARGMAX)) void qgemm_kerne
         for (int q = 0; q < C::SBQ; ++q) s.sb[q] = load16(ub + C::SBOFF + c * (16 * C::SBQ) + 16 * q);
         // lane (c, j) takes row 16*mt + c, K offsets 64*g + 16*j (+8): a
         // wave-uniform byte offset per (g, h) plus a fixed lane offset.  The
-        // groups past the end of K (a short last unit) re-read the last one.
+        // groups past the end of K (a short last unit) re-read the last one,
+        // so no load reaches past a row's k entries.
         const int ng = min(C::GS, G - st * C::GS);
 #pragma unroll
         for (int g = 0; g < C::GS; ++g)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int chunk = st * (C::KU / 8) + 8 * min(g, ng - 1) + h;
-                // < 2^32: the host checks k * ldm < 2^31
-                const uint32_t off = (uint32_t)chunk * (uint32_t)LDM * 16u;
+                const int chunk = st * (C::KU / 8) + 8 * min(g, ng - 1) + h;   // 8-element chunk of the row
+                const uint32_t off = (uint32_t)chunk * 16u;
                 const unsigned char *xs = xbase + (uint32_t)__builtin_amdgcn_readfirstlane((int)off);
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) s.a[g][mt][h] = load16(xs + xlane[mt]);
@@ -696,49 +698,6 @@ hipError_t launch_any(const GemmLaunch &L, int bits, int grid, hipStream_t s) {
 }
 
 }  // namespace
-
-int device_cus() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-            cus = 256;
-        cached[dev] = cus;
-    }
-    return cached[dev];
-}
-
-GemmPlan plan_gemm(int count, const int32_t *n, int32_t k, int32_t m, int bits, bool argmax) {
-    GemmPlan p{};
-    p.nst = (k + tile_k(bits) - 1) / tile_k(bits);
-    p.nq = (p.nst + kWavesPerWG - 1) / kWavesPerWG;
-    int64_t blocks = 0;
-    for (int i = 0; i < count; ++i) blocks += (n[i] + kBlockCols - 1) / kBlockCols;
-    p.total_cg = (int32_t)blocks;
-    const int64_t quads = blocks * p.nq;
-    const int mt = m <= 16 ? 1 : 2;
-    // OCC workgroups per CU; never more workgroups than quads
-    const int64_t slots = (int64_t)kernel_occ(bits, mt, argmax) * device_cus();
-    const int64_t grid = quads < slots ? quads : slots;
-    p.grid = grid < 1 ? 1 : (int32_t)grid;
-    // a full grid of two workgroups per CU runs as CU pairs (weighted split)
-    p.pairs = (kernel_occ(bits, mt, argmax) == 2 && p.grid == 2 * device_cus()) ? device_cus() : 0;
-    // the kernel splits quads with 32-bit products
-    p.fits = quads * p.grid < ((int64_t)1 << 31);
-    p.quads = p.fits ? (int32_t)quads : 0;
-    size_t off = 256;                                   // [0, 256): argmax arrival counter
-    p.off_counters = off;
-    off += ((size_t)blocks * kWavesPerWG * 4 + 255) / 256 * 256;
-    p.off_keys = off;
-    if (argmax) off += (size_t)kMaxRows * 8;            // one 64-bit key per row
-    off = (off + 255) / 256 * 256;
-    p.off_partial = off;
-    off += (size_t)p.grid * 2 * kWavesPerWG * mt * kWave * 16;
-    p.ws_bytes = (off + 255) / 256 * 256;
-    return p;
-}
 
 hipError_t launch_qgemm(const GemmLaunch &L, int bits, int grid, hipStream_t s) {
     return launch_any<false>(L, bits, grid, s);

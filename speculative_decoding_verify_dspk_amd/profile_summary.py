@@ -5,6 +5,14 @@ under profiles/.
     python -m speculative_decoding_verify_dspk_amd.profile_summary stats \\
         <kernel_stats.csv> <kernel_trace.csv> <out.md> --cmd "<profiled command>"
 
+    # per-width launch durations of the verify rounds (rocprofv3 --kernel-trace)
+    python -m speculative_decoding_verify_dspk_amd.profile_summary rounds \\
+        <kernel_trace.csv> <out.md> --sweep 1,8,16 --cmd "<profiled command>"
+
+    # t(M) per projection and decomposition (trace of bench.py --variant-curves)
+    python -m speculative_decoding_verify_dspk_amd.profile_summary curves \\
+        <kernel_trace.csv> <curves.json> <out.md> --cmd "<profiled command>"
+
     # HBM bytes of the head kernel (two --pmc passes: FETCH_SIZE, WRITE_SIZE),
     # scaled by what the same counters read for a plain 256 MiB device copy
     python -m speculative_decoding_verify_dspk_amd.profile_summary traffic \\
@@ -26,8 +34,9 @@ COPY_BYTES = 256 << 20          # the calibration copy that bench.py --calibrate
 
 
 def short(name: str) -> str:
-    if "qgemm_kernel" in name:
-        return "qgemm_kernel<" + name.split("<", 1)[1].split(">", 1)[0] + ">"
+    for k in ("qgemm_slab_lds_kernel", "qgemm_slab_kernel", "qgemm_kernel"):
+        if k + "<" in name:
+            return k + "<" + name.split(k + "<", 1)[1].split(">", 1)[0] + ">"
     m = re.search(r"accept_\w+", name)
     if m:
         return m.group(0)
@@ -44,7 +53,7 @@ def stats(stats_csv: str, trace_csv: str, out: str, cmd: str) -> None:
     # per-launch split of the projection kernels by grid (one line per launch shape)
     per = collections.defaultdict(list)
     for r in csv.DictReader(open(trace_csv)):
-        if "qgemm_kernel" in r["Kernel_Name"]:
+        if "qgemm" in r["Kernel_Name"]:
             per[(short(r["Kernel_Name"]), r["Grid_Size_X"])].append(
                 (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     lines += ["", "Projection launches by grid (workgroups x 256 threads):", "",
@@ -52,6 +61,86 @@ def stats(stats_csv: str, trace_csv: str, out: str, cmd: str) -> None:
     for (k, g), v in sorted(per.items()):
         v.sort()
         lines.append(f"| {k} | {g} | {len(v)} | {v[len(v) // 2]:.1f} |")
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
+def _dspk_launches(trace_csv: str):
+    rows = [r for r in csv.DictReader(open(trace_csv)) if "dspk::" in r["Kernel_Name"]
+            and "qgemm" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    return rows
+
+
+def _us(r) -> float:
+    return (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+
+
+def rounds(trace_csv: str, out: str, cmd: str, sweep: list, title: str) -> None:
+    """Per-width launch durations of the benchmark's verify rounds: each round
+    is its layer's four projection launches followed by the head launch; the
+    timed rounds cycle through the sweep, so the last whole cycles of the trace
+    are the rounds at each width in sweep order."""
+    rows = _dspk_launches(trace_csv)
+    rds, cur = [], []
+    for r in rows:
+        cur.append(r)
+        if "qgemm_kernel<" in r["Kernel_Name"] and ", true>" in r["Kernel_Name"]:
+            if len(cur) >= 5:
+                rds.append(cur[-5:])
+            cur = []
+    n = len(rds) // len(sweep) * len(sweep)
+    rds = rds[len(rds) - n:]
+    names = ["qkv", "o", "gate/up", "down", "head"]
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    kern = collections.defaultdict(dict)
+    for i, rd in enumerate(rds):
+        m = sweep[i % len(sweep)]
+        for nm, r in zip(names, rd):
+            per[m][nm].append(_us(r))
+            kern[m][nm] = short(r["Kernel_Name"])
+    med = lambda v: sorted(v)[len(v) // 2]   # noqa: E731
+    lines = [f"# {title}", "", "Command:", "", "    " + cmd, "",
+             f"Median kernel durations (us) over {n // len(sweep)} rounds per width (rocprofv3 kernel trace):", "",
+             "| rows | " + " | ".join(names) + " | layer (4 launches) |", "|---" * (len(names) + 2) + "|"]
+    for m in sweep:
+        v = [med(per[m][nm]) for nm in names]
+        lines.append(f"| {m} | " + " | ".join(f"{x:.2f}" for x in v) + f" | {sum(v[:4]):.2f} |")
+    lines += ["", "Kernels per launch:", ""]
+    for m in sweep:
+        lines.append(f"- {m} rows: " + ", ".join(f"{nm} `{kern[m][nm]}`" for nm in names))
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
+def curves(trace_csv: str, curves_json: str, out: str, cmd: str) -> None:
+    """t(M) per projection and forced decomposition from the kernel trace of
+    `bench.py --variant-curves`: its JSON line lists the launches in order
+    (projection, variant, rows, launches, the first `warmup` untimed)."""
+    import json
+    plan = json.loads(open(curves_json).read().strip().splitlines()[-1])
+    rows = _dspk_launches(trace_csv)
+    pos = 0
+    table = collections.defaultdict(dict)
+    kern = {}
+    for pname, vname, m, count in plan["launch_plan"]:
+        blk = rows[pos:pos + count]
+        pos += count
+        d = sorted(_us(r) for r in blk[count // 8:])        # the warm-up launches come first
+        table[(pname, vname)][m] = d[len(d) // 2]
+        kern[(pname, vname)] = short(blk[-1]["Kernel_Name"])
+    if pos != len(rows):
+        raise SystemExit(f"trace has {len(rows)} projection launches, the plan {pos}")
+    widths = sorted({m for v in table.values() for m in v})
+    lines = ["# Projection launch time t(M) by decomposition (Qwen3-4B shapes, 8-bit)", "", "Command:", "",
+             "    " + cmd, "",
+             "Median kernel duration (us, rocprofv3 kernel trace) of each launch shape at each width;",
+             "`mfma_*` reduce K on the matrix cores (bf16 16x16x32, rows padded to 16), `dot_slab` on the",
+             "vector ALUs (v_dot2_f32_bf16, at most 4 rows), with the same decomposition and data movement",
+             "as `mfma_slab`.", "",
+             "| projection | variant | kernel | " + " | ".join(f"M={m}" for m in widths) + " |",
+             "|---|---|---|" + "---|" * len(widths)]
+    for (pname, vname), c in table.items():
+        lines.append(f"| {pname} | {vname} | `{kern[(pname, vname)]}` | " +
+                     " | ".join(f"{c[m]:.2f}" if m in c else "" for m in widths) + " |")
     open(out, "w").write("\n".join(lines) + "\n")
 
 
@@ -109,9 +198,24 @@ def main() -> None:
     b.add_argument("out")
     b.add_argument("--cmd-fetch", required=True)
     b.add_argument("--cmd-write", required=True)
+    c = sub.add_parser("rounds")
+    c.add_argument("trace_csv")
+    c.add_argument("out")
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--sweep", required=True)
+    c.add_argument("--title", default="Verify-round launch durations by width")
+    d = sub.add_parser("curves")
+    d.add_argument("trace_csv")
+    d.add_argument("curves_json")
+    d.add_argument("out")
+    d.add_argument("--cmd", required=True)
     args = ap.parse_args()
     if args.what == "stats":
         stats(args.stats_csv, args.trace_csv, args.out, args.cmd)
+    elif args.what == "rounds":
+        rounds(args.trace_csv, args.out, args.cmd, [int(x) for x in args.sweep.split(",")], args.title)
+    elif args.what == "curves":
+        curves(args.trace_csv, args.curves_json, args.out, args.cmd)
     else:
         traffic(args.fetch_csv, args.write_csv, args.out, args.cmd_fetch, args.cmd_write)
 

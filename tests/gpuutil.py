@@ -9,6 +9,12 @@ from speculative_decoding_verify_dspk_amd import binding, inputs
 
 # Contract tolerance on logits / projections: per-row normwise relative error.
 RTOL = 2e-3
+# Design bound of the kernels' own arithmetic (fp32 accumulation of exact
+# bf16 x code products, one fp32 scale/bias update per 64-wide group): the
+# largest per-row normwise error measured over every parity case is 1.5e-6;
+# this bound is ten times that and far below what a dropped or doubled term
+# (a group's bias, a K quarter, a row tile) would give (1e-4 and up).
+DESIGN_BOUND = 2e-5
 # Rows whose oracle top-2 margin is below this may legitimately pick either token.
 NEAR_TIE = 1e-3
 
@@ -24,10 +30,15 @@ def dev_u16(a: np.ndarray):
     return t.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
 
 
-def dev_act(a: np.ndarray, ldm: int | None = None):
-    """Row-major uint16 activation rows [m][k] -> the library's chunk-major
-    device layout [k/8][ldm][8]."""
-    return binding.to_chunk_major(dev_u16(a), ldm)
+def dev_act(a: np.ndarray, ld: int | None = None):
+    """Row-major uint16 activation rows [m][k] -> a device tensor [m][ld] of the
+    same bits (columns k..ld-1 zero), the layout the library reads."""
+    t = torch()
+    m, k = a.shape
+    ld = k if ld is None else ld
+    out = t.zeros((m, ld), dtype=t.int16, device="cuda")
+    out[:, :k] = dev_u16(a)
+    return out
 
 
 def dev_i32(a: np.ndarray):
@@ -71,10 +82,15 @@ def rowwise_rel_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
     return num / den
 
 
-def assert_rows_close(got, ref, rtol=RTOL, what=""):
+def assert_rows_close(got, ref, rtol=RTOL, what="", design=DESIGN_BOUND):
+    """Per-row normwise error within the contract tolerance, and (for fp32
+    outputs compared with the oracle on the same inputs) within the design
+    bound of the arithmetic; design=None skips the second check."""
     err = rowwise_rel_err(got, ref)
     assert np.isfinite(got).all(), f"{what}: non-finite output"
     assert (err <= rtol).all(), f"{what}: worst row normwise error {err.max():.3e} > {rtol}"
+    if design is not None:
+        assert (err <= design).all(), f"{what}: worst row normwise error {err.max():.3e} above the design bound {design}"
     return err.max()
 
 

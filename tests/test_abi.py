@@ -92,7 +92,10 @@ def test_pack_sizes_and_rejects_bad_destination(lib):
 
 
 @pytest.mark.parametrize("args,code", [
-    (dict(m=0), EINVAL), (dict(m=33), EINVAL), (dict(ldx=3), EINVAL), (dict(ldx=70000), EINVAL),
+    (dict(m=0), EINVAL), (dict(m=33), EINVAL),
+    (dict(ldx=120), EINVAL),                   # row-major rows: ldx >= k ...
+    (dict(ldx=132), EINVAL),                   # ... and a multiple of 8 (16-byte aligned rows)
+    (dict(ldx=1 << 26, m=32), EUNSUPPORTED),   # rows spanning 2 GiB
     (dict(x=0), EINVAL), (dict(x=X + 8), EINVAL), (dict(ldy=32), EINVAL), (dict(dt=7), EINVAL),
     (dict(y=0), EINVAL),
 ])
@@ -131,6 +134,19 @@ def test_workspace_for_m_rows_serves_every_narrower_width(lib):
         for m in (1, 16, 17, 32):
             big = lib.dspk_lmhead_workspace_bytes(v, m)
             assert all(lib.dspk_lmhead_workspace_bytes(v, mm) <= big for mm in range(1, m + 1))
+
+
+def test_workspace_offsets_do_not_depend_on_the_call(lib):
+    # the counters and keys sit at fixed offsets (the partial-sum region is
+    # sized for the largest grid), so one buffer serves any projection or head
+    # call: the size depends on the column count only
+    for n in (1, 64, 1000, 9728, 151936):
+        sizes = {lib.dspk_qgemm_workspace_bytes(n, k, m) for k in (64, 2560, 17408) for m in (1, 16, 17, 32)}
+        sizes |= {lib.dspk_lmhead_workspace_bytes(n, m) for m in (1, 8, 32)}
+        assert len(sizes) == 1, (n, sizes)
+    # 16 bytes of counters per 64 columns on top of a fixed part
+    a, b = lib.dspk_qgemm_workspace_bytes(64 * 1024, 64, 1), lib.dspk_qgemm_workspace_bytes(64 * 2048, 64, 1)
+    assert b - a == 16 * 1024
 
 
 def test_grouped_rejects_mismatch(lib):

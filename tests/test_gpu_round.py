@@ -147,3 +147,124 @@ def test_measured_curve_drives_the_cap_policy(tmp_path):
     cap, rate = binding.choose_cap(curve, None, 1.0)
     assert cap >= 1 and rate > 1.0 / curve[0]
     assert binding.choose_cap(curve, None, 0.0)[0] == 0
+    # the library's choice on the curve this device measured is the oracle's
+    drafter = [0.0] + [2.0 + 0.5 * i for i in range(1, len(curve))]
+    for a in np.linspace(0.0, 1.0, 21):
+        for dr in (None, drafter):
+            got = binding.choose_cap(curve, dr, float(a))
+            want = oracle.choose_cap(curve, dr, float(a))
+            assert got[0] == want[0], (a, dr is not None, got, want, curve)
+            assert abs(got[1] - want[1]) <= 1e-12 * max(1.0, abs(want[1]))
+
+
+def _sampled_columns(g, n, count=96):
+    return np.unique(np.concatenate([[0, 1, 63, 64, n - 1], g.choice(n, count, replace=False)]))
+
+
+def test_dense27b_sampled_round_on_one_workspace():
+    """A 27B-shaped round at M = 17 (anchor + 16 drafts): two layers' projections
+    (q/k/v grouped, o, gate/up grouped, down; independent N(0, 1) inputs per
+    launch), the 151936 x 5120 head with logits, then speculative sampling at
+    T = 1 against drafts drawn from q = softmax(z + N(0, 0.5)) built from the
+    oracle's logits.  Every projection and head launch shares ONE workspace
+    (different shapes, grouped and single, head last), as the workspace
+    contract allows.  Projections: sampled columns against the oracle; head:
+    full logits and ids; acceptance: equal to the oracle's on the oracle's
+    logits, except decisions within the band the logit difference opens."""
+    import torch
+    from speculative_decoding_verify_dspk_amd import binding
+    from gpuutil import dev_act, dev_f32, dev_i32, oracle_columns
+    from test_gpu_accept import exempt
+    m, T = 17, 1.0
+    s = inputs.LAYER_SHAPES["dense-27b"]
+    H, Q, KV, F, V = s["hidden"], s["q"], s["kv"], s["inter"], s["vocab"]
+    need = max(binding.qgemm_workspace_bytes(Q, H, m) * 3, binding.qgemm_workspace_bytes(F, H, m) * 2,
+               binding.lmhead_workspace_bytes(V, m))
+    ws = binding.alloc_workspace(need)
+    g = np.random.default_rng(27)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    for layer in range(2):
+        mk = lambda n, k, name: inputs.make_qweight(n, k, 8, "c4round", layer, name)   # noqa: E731
+        groups = [([mk(Q, H, "q"), mk(KV, H, "k"), mk(KV, H, "v")], H, "attn_in"),
+                  ([mk(H, Q, "o")], Q, "o_in"),
+                  ([mk(F, H, "gate"), mk(F, H, "up")], H, "mlp_in"),
+                  ([mk(H, F, "down")], F, "down_in")]
+        for ws_, k, src in groups:
+            print(f"27B layer {layer} {src}: {[w.n for w in ws_]} x {k}", flush=True)
+            x = inputs.make_activations(m, k, "c4round", layer, src)
+            dws = [binding.DeviceQWeight.upload(w) for w in ws_]
+            ys = [torch.full((m, w.n), float("nan"), **f32) for w in ws_]
+            if len(ws_) == 1:
+                binding.qgemm_verify(dws[0], dev_act(x), m, ys[0], ws)
+            else:
+                binding.qgemm_verify_grouped(dws, dev_act(x), m, ys, ws)
+            torch.cuda.synchronize()
+            for w, y in zip(ws_, ys):
+                got = y.cpu().numpy()
+                assert np.isfinite(got).all()
+                cols = _sampled_columns(g, w.n)
+                ref = oracle_columns(w, x, cols)
+                assert_rows_close(got[:, cols], ref, what=f"layer {layer} n={w.n}")
+            del dws
+    head = inputs.make_qweight(V, H, 8, "c4round", "lm_head")
+    h = inputs.make_activations(m, H, "c4round", "final_h")
+    dh = binding.DeviceQWeight.upload(head)
+    am = torch.full((m,), -7, dtype=torch.int32, device="cuda")
+    z = torch.empty((m, V), **f32)
+    binding.lmhead_argmax(dh, dev_act(h), m, am, z, ws)
+    torch.cuda.synchronize()
+    assert int(ws[:512].count_nonzero()) == 0, "head words not returned to zero"
+    print("oracle logits of the 27B-shaped head", flush=True)
+    zref = oracle_logits_chunked(head, h)
+    zg = z.cpu().numpy()
+    assert_rows_close(zg, zref, what="27B head logits")
+    assert_argmax_parity(am.cpu().numpy(), zref, what="27B head")
+    q, d = inputs.draft_distribution(zref, T, 0.5, "c4round", "drafter")
+    u = inputs.make_uniforms(m, "c4round", "uniforms")
+    al = torch.full((1,), -9, dtype=torch.int32, device="cuda")
+    com = torch.full((m,), -9, dtype=torch.int32, device="cuda")
+    sws = binding.alloc_workspace(binding.sample_workspace_bytes(V, m))
+    binding.accept_sample(z, dev_f32(q), dev_i32(d), dev_f32(u), m, V, T, al, com, sws)
+    torch.cuda.synchronize()
+    ral, rcom = oracle.accept_sample(zref, q, d, u, T)
+    got_al, got_com = int(al.cpu()[0]), com.cpu().numpy()
+    dz = float(np.abs(zg - zref).max())
+    print(f"27B round: accepted {got_al} (oracle {ral}); max |dz| = {dz:.2e}")
+    if got_al != ral or not np.array_equal(got_com, rcom):
+        band = max(1e-5, 4.0 * dz / T)
+        assert exempt(zref, q.astype(np.float64), d, u.astype(np.float64), T, band=band), \
+            f"gpu ({got_al}, {got_com}) != oracle ({ral}, {rcom})"
+        print(f"27B round: exempt within band {band:.1e}")
+
+
+def test_projections_chain_through_bf16_rows():
+    """The boundary chains: a projection's bf16 output rows (row-major
+    [m][n]) are the next projection's input as they are -- Qwen3-4B q then o
+    shapes, no relayout between the two calls."""
+    import torch
+    from speculative_decoding_verify_dspk_amd import binding
+    from gpuutil import dev_act
+    m, H, Q = 8, 2560, 4096
+    w1 = inputs.make_qweight(Q, H, 8, "chain", "q")
+    w2 = inputs.make_qweight(H, Q, 8, "chain", "o")
+    x = inputs.make_activations(m, H, "chain", "x")
+    d1, d2 = binding.DeviceQWeight.upload(w1), binding.DeviceQWeight.upload(w2)
+    ws = binding.alloc_workspace(binding.qgemm_workspace_bytes(Q, H, m))
+    y1 = torch.empty((m, Q), dtype=torch.int16, device="cuda")        # bf16 bit patterns
+    y2 = torch.empty((m, H), dtype=torch.float32, device="cuda")
+    binding.qgemm_verify(d1, dev_act(x), m, y1, ws)
+    binding.qgemm_verify(d2, y1, m, y2, ws)                            # y1 is x of the second call
+    torch.cuda.synchronize()
+    # the oracle's chain: its own fp64 first stage rounded to bf16 rows, then the second stage
+    r1 = oracle.qlinear(x, w1.codes, w1.scales, w1.biases, 8, Q, H)
+    r1_bits = inputs.f32_to_bf16_bits(r1.astype(np.float32))
+    g1 = y1.cpu().numpy().view(np.uint16)
+    diff = np.abs(inputs.bf16_bits_to_f32(g1).astype(np.float64) - inputs.bf16_bits_to_f32(r1_bits))
+    ulp = np.abs(inputs.bf16_bits_to_f32(r1_bits)).astype(np.float64) * 2.0 ** -7
+    assert (diff <= ulp + 1e-30).all(), "first stage off by more than one bf16 ulp"
+    assert (g1 != r1_bits).mean() < 0.01, "first-stage rounding differs too often"
+    r2 = oracle.qlinear(r1_bits, w2.codes, w2.scales, w2.biases, 8, H, Q)
+    # the two chains round their first stage to bf16 separately (a few
+    # one-ulp differences), so only the contract tolerance applies here
+    worst = assert_rows_close(y2.cpu().numpy(), r2, what="chained second projection", design=None)
+    print(f"chain: {int((g1 != r1_bits).sum())} first-stage bf16 roundings differ; second stage {worst:.2e}")

@@ -98,3 +98,46 @@ def test_row_draft_misalignment_is_caught():
         return a + 1
     c = json.load(open(GOLDEN))["greedy"][0]
     assert bad(np.array(c["t"]), np.array(c["d"])) != c["accept_len"]
+
+
+def _penalty_golden_passes():
+    for c in json.load(open(GOLDEN))["penalties"]:
+        got = dspk_oracle.penalized_logits(np.array(c["z"], np.float64), c["counts"], np.array(c["d"], np.int64),
+                                           c["presence"], c["frequency"])
+        if not np.array_equal(got, np.array(c["expected"], np.float64)):
+            return False
+    return True
+
+
+def test_penalty_pins_pass_and_catch_mistakes(monkeypatch):
+    """Frequency applied as an indicator, and a row counting its own draft,
+    both fail the hand-worked penalty cases."""
+    assert _penalty_golden_passes()
+    real = dspk_oracle.penalized_logits
+
+    def freq_as_indicator(logits, counts, draft_ids, presence, frequency):
+        z = np.asarray(logits, np.float64)
+        c = np.zeros(z.shape[1]) if counts is None else np.asarray(counts, np.float64).copy()
+        d = np.asarray(draft_ids, np.int64).ravel()
+        out = np.empty_like(z)
+        for j in range(z.shape[0]):
+            out[j] = z[j] - presence * (c > 0) - frequency * (c > 0)
+            if j < z.shape[0] - 1:
+                c[d[j]] += 1
+        return out
+    monkeypatch.setattr(dspk_oracle, "penalized_logits", freq_as_indicator)
+    assert not _penalty_golden_passes()
+
+    def counts_own_draft(logits, counts, draft_ids, presence, frequency):
+        z = np.asarray(logits, np.float64)
+        c = np.zeros(z.shape[1]) if counts is None else np.asarray(counts, np.float64).copy()
+        d = np.asarray(draft_ids, np.int64).ravel()
+        out = np.empty_like(z)
+        for j in range(z.shape[0]):
+            if j < z.shape[0] - 1:
+                c[d[j]] += 1
+            out[j] = z[j] - presence * (c > 0) - frequency * c
+        return out
+    monkeypatch.setattr(dspk_oracle, "penalized_logits", counts_own_draft)
+    assert not _penalty_golden_passes()
+    monkeypatch.setattr(dspk_oracle, "penalized_logits", real)
