@@ -234,6 +234,33 @@ int dspk_qgemm_verify_grouped(int32_t count, const dspk_tiled_weight *w,
                               void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * dspk_qgemm_verify_grouped without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  It allocates nothing (no
+ * hipMalloc, no allocating library call); its workspace is a file-scope
+ * device array of the library, one per GPU, which each GPU holds until the
+ * process ends (about 12.7 MB).  Results are those of
+ * dspk_qgemm_verify_grouped on the same arguments, bit for bit.
+ *  - The array's device address is fetched once per device, on the device
+ *    that is current at the first call; the first call on a device also
+ *    enqueues one small clearing kernel on `stream` ahead of the projection.
+ *    `stream` must belong to the current device.
+ *  - Every call on a GPU shares that GPU's array: calls that overlap on one
+ *    GPU (different streams, or host threads without ordering) race and give
+ *    wrong results.  Calls ordered on one stream are safe; each completed
+ *    call leaves the array ready for the next.
+ *  - Limit: the call's counters must fit the array -- at most 4096 64-column
+ *    blocks (262144 columns over all `count` weights) on a device of up to
+ *    256 CUs; larger calls return DSPK_EUNSUPPORTED and enqueue nothing.
+ * Other arguments, checks and errors are those of dspk_qgemm_verify_grouped;
+ * DSPK_EDEVICE also reports a failed scratch set-up.
+ */
+int dspk_qgemm_verify_grouped_noalloc(int32_t count, const dspk_tiled_weight *w,
+                                      const uint16_t *x, int64_t ldx, int32_t m,
+                                      void *const *y, int32_t y_dtype, const int64_t *ldy,
+                                      void *stream);
+
+/*
  * Prefill projection: the same y = x . deq(W)^T for many rows at once -- a
  * prompt's tokens, the wide-row form of the pass ("mlx-dspark" wiki summary,
  * "Key techniques": a weight group dequantised once and reused for all rows).

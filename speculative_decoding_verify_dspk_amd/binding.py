@@ -93,6 +93,8 @@ def lib() -> ctypes.CDLL:
         "dspk_qgemm_verify_grouped": (c_int32, [c_int32, P(TiledDesc), c_void_p, c_int64, c_int32,
                                                 P(c_void_p), c_int32, P(c_int64), c_void_p, c_size_t,
                                                 c_void_p]),
+        "dspk_qgemm_verify_grouped_noalloc": (c_int32, [c_int32, P(TiledDesc), c_void_p, c_int64, c_int32,
+                                                        P(c_void_p), c_int32, P(c_int64), c_void_p]),
         "dspk_qgemm_prefill": (c_int32, [P(TiledDesc), c_void_p, c_int64, c_int32, c_void_p, c_int32, c_int64,
                                          c_void_p]),
         "dspk_lmhead_workspace_bytes": (c_size_t, [c_int32, c_int32]),
@@ -372,6 +374,17 @@ def qgemm_verify_grouped(ws: list, x, m: int, ys: list, workspace=None, stream=N
     ws_bytes = 0 if workspace is None else workspace.numel()
     _check(lib().dspk_qgemm_verify_grouped(cnt, descs, x.data_ptr(), _acts(x, "x"), m, yptr, dt, ldy,
                                            _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def qgemm_verify_grouped_noalloc(ws: list, x, m: int, ys: list, stream=None) -> None:
+    """The grouped projection on the library's own per-GPU scratch (no workspace)."""
+    cnt = len(ws)
+    descs = (TiledDesc * cnt)(*[w.desc for w in ws])
+    yptr = (c_void_p * cnt)(*[y.data_ptr() for y in ys])
+    ldy = (c_int64 * cnt)(*[_rows(y, "y") for y in ys])
+    dt = DSPK_BF16 if ys[0].element_size() == 2 else DSPK_F32
+    _check(lib().dspk_qgemm_verify_grouped_noalloc(cnt, descs, x.data_ptr(), _acts(x, "x"), m, yptr, dt, ldy,
+                                                   _stream(stream)))
 
 
 def qgemm_prefill(w: DeviceQWeight, x, m: int, y, stream=None) -> None:

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdspk.so")
 PROBE_LIB = os.path.join(PKG, "libdspk_probe.so")      # measurement only: the streaming-read probe
-SOURCES = ["qgemm.hip", "slab.hip", "prefill.hip", "pack.hip", "accept.hip", "api.cpp", "plan.cpp", "policy.cpp"]
+SOURCES = ["qgemm.hip", "slab.hip", "prefill.hip", "pack.hip", "accept.hip", "noalloc.hip", "api.cpp", "plan.cpp", "policy.cpp"]
 
 # Packed fp32 instructions are kept out of every HIP object (the compiler
 # would otherwise form them from ordinary float code).

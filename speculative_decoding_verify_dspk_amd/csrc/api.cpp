@@ -231,6 +231,35 @@ int dspk_qgemm_verify_grouped(int32_t count, const dspk_tiled_weight *w, const u
                         "dspk_qgemm_verify_grouped");
 }
 
+int dspk_qgemm_verify_grouped_noalloc(int32_t count, const dspk_tiled_weight *w, const uint16_t *x, int64_t ldx,
+                                      int32_t m, void *const *y, int32_t y_dtype, const int64_t *ldy,
+                                      void *stream) {
+    const char *who = "dspk_qgemm_verify_grouped_noalloc";
+    // the size check first (before any device work), then the scratch
+    if (count >= 1 && count <= DSPK_MAX_GROUPED && w != nullptr) {
+        int32_t ns[DSPK_MAX_GROUPED];
+        bool shapes_ok = true;
+        int64_t blocks = 0;
+        for (int i = 0; i < count; ++i) {
+            if (w[i].n < 1 || w[i].k < DSPK_GROUP || w[i].k % DSPK_GROUP || !dspk::supported_bits(w[i].bits))
+                shapes_ok = false;
+            ns[i] = w[i].n;
+            blocks += ((int64_t)w[i].n + 63) / 64;
+        }
+        if (shapes_ok && m >= 1 && m <= DSPK_MAX_ROWS) {
+            const size_t need = dspk::plan_gemm(count, ns, w[0].k, m, w[0].bits, false).ws_bytes;
+            if (blocks > dspk::kScratchMaxBlocks || need > dspk::static_scratch_bytes())
+                return fail(DSPK_EUNSUPPORTED, "%s: call needs %zu bytes of scratch, more than the %zu this "
+                            "entry point holds (too many columns for one allocation-free call)",
+                            who, need, dspk::static_scratch_bytes());
+        }
+    }
+    void *ptr = nullptr;
+    const hipError_t e = dspk::static_scratch(&ptr, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(DSPK_EDEVICE, "%s: scratch set-up failed: %s", who, hipGetErrorString(e));
+    return qgemm_common(count, w, x, ldx, m, y, y_dtype, ldy, ptr, dspk::static_scratch_bytes(), stream, who);
+}
+
 size_t dspk_lmhead_workspace_bytes(int32_t v, int32_t m) {
     if (v < 1 || m < 1 || m > DSPK_MAX_ROWS) return 0;
     return dspk::plan_gemm(1, &v, DSPK_GROUP, m, 8, true).ws_bytes;

@@ -182,6 +182,15 @@ int device_cus();
 hipError_t launch_qgemm(const GemmLaunch &L, int bits, int grid, hipStream_t s);
 hipError_t launch_qgemm_slab(const GemmLaunch &L, int bits, int waves, hipStream_t s);
 hipError_t launch_qgemm_dot(const GemmLaunch &L, int waves, hipStream_t s);   // 8-bit, m <= kDotMaxRows
+
+// Device address of this GPU's file-scope scratch array (the workspace of the
+// allocation-free projection call), fetched once per device; the first call on
+// a device also enqueues the clearing of its counters on `s`.  The array serves
+// calls of up to kScratchMaxBlocks 64-column blocks on up to kScratchCus CUs.
+constexpr int kScratchCus = 256;
+constexpr int64_t kScratchMaxBlocks = 4096;          // 262144 columns per call
+hipError_t static_scratch(void **ptr, hipStream_t s);
+size_t static_scratch_bytes();
 hipError_t launch_lmhead(const GemmLaunch &L, int bits, int grid, hipStream_t s);
 
 // Acceptance kernels.

@@ -130,6 +130,15 @@ hipError_t launch_accept_sample(const SampleParams &p, hipStream_t) {
     CHECK(p.temperature > 0.f && p.m_rows >= 2 && p.v >= 1);
     return hipSuccess;
 }
+// the allocation-free entry point's scratch: a made-up device address
+static const uintptr_t kScratchAddr = 0x7d0000000000ull;
+hipError_t static_scratch(void **ptr, hipStream_t) {
+    *ptr = (void *)kScratchAddr;
+    g_ws = kScratchAddr;
+    g_ws_bytes = static_scratch_bytes();
+    return hipSuccess;
+}
+size_t static_scratch_bytes() { return kWsHead + partial_region_bytes(kScratchCus) + kScratchMaxBlocks * 16; }
 }  // namespace dspk
 
 // The only HIP runtime calls of the host sources: a device with kCus CUs.
@@ -220,6 +229,39 @@ static void projections() {
             CHECK(dspk_qgemm_verify_grouped(count, ws, (const uint16_t *)fake(X), 2560, m, ys, 0, ld, fake(g_ws),
                                             need, nullptr) == DSPK_OK);
         }
+}
+
+static void noalloc() {
+    // the same plans and carving as the workspace call, on the library's array
+    const int qkv[] = {4096, 1024, 1024};
+    dspk_tiled_weight ws[3];
+    void *ys[3];
+    int64_t ld[3];
+    for (int i = 0; i < 3; ++i) {
+        ws[i] = tiled(qkv[i], 2560, 8);
+        ys[i] = fake(Y + (uintptr_t)i * 0x100000);
+        ld[i] = qkv[i];
+    }
+    for (int m : {1, 8, 16, 17, 32})
+        CHECK(dspk_qgemm_verify_grouped_noalloc(3, ws, (const uint16_t *)fake(X), 2560, m, ys, 0, ld, nullptr) ==
+              DSPK_OK);
+    // the largest call that fits: 4096 blocks; one block more is refused
+    dspk_tiled_weight big = tiled(4096 * 64, 512, 8);
+    int64_t bl = 4096 * 64;
+    void *by = fake(Y);
+    CHECK(dspk_qgemm_verify_grouped_noalloc(1, &big, (const uint16_t *)fake(X), 512, 4, &by, 0, &bl, nullptr) ==
+          DSPK_OK);
+    big.n += 1;
+    bl += 1;
+    const int before = g_launches;
+    expect_error(dspk_qgemm_verify_grouped_noalloc(1, &big, (const uint16_t *)fake(X), 512, 4, &by, 0, &bl, nullptr),
+                 DSPK_EUNSUPPORTED);
+    CHECK(g_launches == before);
+    // argument errors are those of the grouped call
+    expect_error(dspk_qgemm_verify_grouped_noalloc(0, ws, (const uint16_t *)fake(X), 2560, 4, ys, 0, ld, nullptr),
+                 DSPK_EINVAL);
+    expect_error(dspk_qgemm_verify_grouped_noalloc(3, ws, (const uint16_t *)fake(X), 2560, 40, ys, 0, ld, nullptr),
+                 DSPK_EINVAL);
 }
 
 static void variants() {
@@ -346,6 +388,7 @@ static void policy() {
 
 int main() {
     projections();
+    noalloc();
     variants();
     rejections();
     packing_and_prefill();
