@@ -56,7 +56,7 @@ struct SampleWs {
     float2 *stats;   // [rows][nchunks]
     int32_t *flags;  // [rows][nchunks]
     float *qmax;     // [rows][nchunks] (draft rows)
-    float2 *mass;    // [nchunks]
+    float2 *mass;    // [nchunks][chunk / kSampleSeg]: per segment of the drawing row
     Trunc *trunc;    // [rows][2]: target p, draft q
     uint32_t *pcnt;            // [rows][2][nslices][NB]
     unsigned long long *pmass; // [rows][2][nslices][NB]
@@ -98,6 +98,7 @@ struct SampleArgs {
     const int32_t *counts;       // history token counts [v], or NULL
     int32_t pen;                 // any penalty applies
     int32_t trunc;               // top-k or top-p applies
+    bool vec_z, vec_q;           // rows of z / q start on 16-byte boundaries
     int32_t *accept_len, *committed;
     void *ws;
 };
@@ -160,98 +161,160 @@ __device__ inline float2 load_f2(const float2 *p) {
                                                          __HIP_MEMORY_SCOPE_AGENT));
 }
 
-// block-wide reductions in a fixed order (wave butterfly, then waves in order)
-template <int NT>
-__device__ inline float block_sum(float v, float *scratch) {
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    const int w = threadIdx.x >> 6;
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) scratch[w] = v;
-    __syncthreads();
-    float r = scratch[0];
-    for (int i = 1; i < NT / 64; ++i) r += scratch[i];
-    return r;
-}
-
-__device__ inline float block_max(float v, float *scratch) {
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-    const int w = threadIdx.x >> 6;
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) scratch[w] = v;
-    __syncthreads();
-    float r = scratch[0];
-    for (int i = 1; i < TPB / 64; ++i) r = fmaxf(r, scratch[i]);
-    return r;
-}
-
 // Row maximum and normaliser of z'/T from the chunk statistics, eight threads
 // per row (k = tid % 8 takes chunks k, k + 8, ...), then a fixed butterfly.
 __device__ inline float2 row_stats8(const float2 *st, int nchunks, int k) {
+    constexpr int R = 8;     // chunks per thread fetched together (all of them up to 64 chunks)
+    float2 a[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) a[r] = k + 8 * r < nchunks ? st[k + 8 * r] : make_float2(-INFINITY, 0.f);
     float mx = -INFINITY;
-    for (int cc = k; cc < nchunks; cc += 8) mx = fmaxf(mx, st[cc].x);
+#pragma unroll
+    for (int r = 0; r < R; ++r) mx = fmaxf(mx, a[r].x);
+    for (int cc = k + 8 * R; cc < nchunks; cc += 8) mx = fmaxf(mx, st[cc].x);
     for (int off = 1; off < 8; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
     float sm = 0.f;
-    for (int cc = k; cc < nchunks; cc += 8) sm += st[cc].y * expf(st[cc].x - mx);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        if (k + 8 * r < nchunks) sm += a[r].y * expf(a[r].x - mx);
+    for (int cc = k + 8 * R; cc < nchunks; cc += 8) sm += st[cc].y * expf(st[cc].x - mx);
     for (int off = 1; off < 8; off <<= 1) sm += __shfl_xor(sm, off);
     return make_float2(mx, sm);
 }
 
+// Four consecutive entries of a row from col on, entries at or past v1
+// reading as `fill`: one 16-byte load when `full` (in range and 16-byte
+// aligned), else four loads clamped into the row (never a branch per entry,
+// so every load of a batch is in flight at once).
+__device__ inline float4 load4(const float *row, int col, int v1, bool full, float fill) {
+    if (full) return *(const float4 *)(row + col);
+    const int last = v1 - 1;
+    const float a = row[min(col, last)], b = row[min(col + 1, last)];
+    const float c = row[min(col + 2, last)], d = row[min(col + 3, last)];
+    return make_float4(col < v1 ? a : fill, col + 1 < v1 ? b : fill, col + 2 < v1 ? c : fill, col + 3 < v1 ? d : fill);
+}
+__device__ inline float f4(const float4 &a, int e) { return e == 0 ? a.x : e == 1 ? a.y : e == 2 ? a.z : a.w; }
+
+__device__ inline float wave_max(float v) {
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    return v;
+}
+__device__ inline float wave_sum(float v) {
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+// A chunk is read as G4 steps of TPB float4 groups: thread tid's group i holds
+// columns v0 + 4 (tid + TPB i) .. + 3, so wave w's step i covers the SEG
+// columns of segment NW i + w of the chunk.
+constexpr int G4 = EPT / 4;
+constexpr int NW = TPB / 64;
+constexpr int SEG = kSampleSeg;
+constexpr int NSEG = CH / SEG;
+static_assert(EPT % 4 == 0 && SEG == 4 * 64 && NSEG == NW * G4, "chunk, segment and thread layout disagree");
+static_assert(kMaxRows <= 64, "the accept tests and the final writes take one lane of wave 0 per row");
+
+// This thread's NG groups of four of a chunk [v0, v1) of a row, for NT
+// threads (group i of thread t: columns v0 + 4 (t + NT i) .. + 3; entries past
+// v1 read as 0).  One branch for the whole chunk -- 16-byte loads when the
+// chunk is full and the row 16-byte aligned, else clamped loads -- so that
+// all of them are in flight together.
+template <int NT, int NG>
+__device__ inline void load_chunk(float4 (&out)[NG], const float *row, int v0, int v1, bool vec) {
+    const int t = threadIdx.x;
+    if (vec && v0 + CH <= v1) {
+#pragma unroll
+        for (int i = 0; i < NG; ++i) out[i] = *(const float4 *)(row + v0 + 4 * (t + NT * i));
+    } else {
+#pragma unroll
+        for (int i = 0; i < NG; ++i) out[i] = load4(row, v0 + 4 * (t + NT * i), v1, false, 0.f);
+    }
+}
+
+// The decide kernel runs 1024 threads per chunk: one group of four per
+// thread, so wave w covers exactly segment w of the chunk.
+constexpr int DT = 1024;
+constexpr int DW = DT / 64;
+constexpr int DG = CH / (4 * DT);
+static_assert(DG == 1 && DW == NSEG, "decide layout: one wave per segment");
+
 // Pass 1: per (row, chunk) max and sum of exp of z'/T, and the fault flag
 // (non-finite logit; non-finite or negative q on draft rows; negative count).
+// Every load of the chunk is issued before any of them is used.
 __global__ __launch_bounds__(TPB) void sample_stats_kernel(const SampleArgs A) {
-    __shared__ float scratch[TPB / 64];
+    __shared__ float s_mx[NW], s_qm[NW], s_sm[NW];
+    __shared__ int s_bad[NW];
     __shared__ int32_t s_d[kMaxRows];
     __shared__ uint32_t s_bloom[32];
     const int nchunks = (A.v + CH - 1) / CH;
     const SampleWs W = carve(A.ws, A.rows, A.v);
-    const int c = blockIdx.x, j = blockIdx.y, tid = threadIdx.x;
+    const int c = blockIdx.x, j = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave-uniform (scalar branches)
     const int v0 = c * CH, v1 = min(A.v, v0 + CH);
-    if (tid < A.rows - 1) s_d[tid] = A.d[tid];
-    __syncthreads();
-    build_bloom(s_bloom, s_d, j);
+    const bool draft = j < A.rows - 1;
     const float *zr = A.z + (int64_t)j * A.ldz;
-    float a[EPT];
-    float mx = -INFINITY;
+    const float *qr = A.q + (int64_t)j * A.ldq;
+    float4 zv[G4], qv[G4];
+    load_chunk<TPB, G4>(zv, zr, v0, v1, A.vec_z);
+    if (draft) load_chunk<TPB, G4>(qv, qr, v0, v1, A.vec_q);
+    if (A.pen) {
+        if (tid < A.rows - 1) s_d[tid] = A.d[tid];
+        __syncthreads();
+        build_bloom(s_bloom, s_d, j);
+    }
+    float a[G4][4];
+    float mx = -INFINITY, qm = 0.f;
     int bad = 0;
 #pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-        const int col = v0 + tid + TPB * i;
-        a[i] = -INFINITY;
-        if (col < v1) {
-            const float zz = zr[col];
-            bad |= !isfinite(zz);
-            if (A.counts != nullptr) bad |= A.counts[col] < 0;
-            a[i] = scaled_logit(A, s_d, s_bloom, j, col, zz);
-            mx = fmaxf(mx, a[i]);
-        }
-    }
-    float qm = 0.f;
-    if (j < A.rows - 1) {
-        const float *qr = A.q + (int64_t)j * A.ldq;
+    for (int i = 0; i < G4; ++i)
 #pragma unroll
-        for (int i = 0; i < EPT; ++i) {
-            const int col = v0 + tid + TPB * i;
+        for (int e = 0; e < 4; ++e) {
+            const int col = v0 + 4 * (tid + TPB * i) + e;
+            a[i][e] = -INFINITY;
             if (col < v1) {
-                const float qq = qr[col];
-                bad |= !(isfinite(qq) && qq >= 0.f);
-                qm = fmaxf(qm, qq);
+                const float zz = f4(zv[i], e);
+                bad |= !isfinite(zz);
+                if (A.counts != nullptr) bad |= A.counts[col] < 0;
+                a[i][e] = scaled_logit(A, s_d, s_bloom, j, col, zz);
+                mx = fmaxf(mx, a[i][e]);
+                if (draft) {
+                    const float qq = f4(qv[i], e);
+                    bad |= !(isfinite(qq) && qq >= 0.f);
+                    qm = fmaxf(qm, qq);
+                }
             }
         }
+    mx = wave_max(mx);
+    qm = wave_max(qm);
+    const int wbad = __any(bad);
+    if (lane == 0) {
+        s_mx[w] = mx;
+        s_qm[w] = qm;
+        s_bad[w] = wbad;
     }
-    bad = __syncthreads_or(bad);
-    if (A.trunc) {
-        qm = block_max(qm, scratch);
-        if (tid == 0) W.qmax[j * nchunks + c] = qm;
-    }
-    const float cmax = block_max(mx, scratch);
+    __syncthreads();
+    float cmax = s_mx[0];
+    for (int k = 1; k < NW; ++k) cmax = fmaxf(cmax, s_mx[k]);
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < EPT; ++i)
-        if (v0 + tid + TPB * i < v1) s += expf(a[i] - cmax);
-    const float csum = block_sum<TPB>(s, scratch);
+    for (int i = 0; i < G4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (v0 + 4 * (tid + TPB * i) + e < v1) s += expf(a[i][e] - cmax);
+    s = wave_sum(s);
+    if (lane == 0) s_sm[w] = s;
+    __syncthreads();
     if (tid == 0) {
+        float csum = s_sm[0], cq = s_qm[0];
+        int cb = s_bad[0];
+        for (int k = 1; k < NW; ++k) {
+            csum += s_sm[k];
+            cq = fmaxf(cq, s_qm[k]);
+            cb |= s_bad[k];
+        }
         W.stats[j * nchunks + c] = make_float2(cmax, csum);
-        W.flags[j * nchunks + c] = bad;
+        W.flags[j * nchunks + c] = cb;
+        if (A.trunc) W.qmax[j * nchunks + c] = cq;
     }
 }
 
@@ -960,83 +1023,125 @@ __device__ inline RowView row_view(const SampleArgs &A, const SampleWs &W, float
 // Pass 2, one workgroup per chunk.  Every workgroup repeats the (cheap,
 // deterministic) accept decisions from the row statistics of pass 1 -- so all
 // agree on the row jr that supplies the final draw -- and adds up, over its
-// chunk of row jr only, the mass of the residual max(0, p - q) and of p; the
-// last workgroup to finish draws the token.
-__global__ __launch_bounds__(TPB) void sample_decide_kernel(const SampleArgs A) {
-    __shared__ float scratch[TPB / 64];
+// chunk of row jr only, the mass of the residual max(0, p - q) and of p per
+// 256-column segment; the last workgroup to finish finds the segment holding
+// the draw (prefix sums in column order) and draws the token inside it.
+__global__ __launch_bounds__(DT) void sample_decide_kernel(const SampleArgs A) {
     __shared__ float2 s_rows[kMaxRows];
     __shared__ int32_t s_d[kMaxRows];
     __shared__ uint32_t s_bloom[32];
-    __shared__ float s_pref[TPB];
-    __shared__ int s_flag[2];
-    __shared__ int s_jr, s_lastc;
+    __shared__ float s_tot[2][DW], s_scan[DW];
+    __shared__ int s_flag, s_jr, s_lastseg;
     __shared__ unsigned long long s_cut;
     const int rows = A.rows, v = A.v;
-    const int nchunks = (v + CH - 1) / CH;
+    const int nchunks = (v + CH - 1) / CH, nseg = nchunks * NSEG;
     const SampleWs W = carve(A.ws, rows, v);
-    const int c = blockIdx.x, tid = threadIdx.x;
+    const int c = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    {
+    // draft ids and uniforms in range (they index memory below); thread j
+    // fetches the two entries its accept test reads as soon as d_j is known
+    int bad = 0, dj = 0;
+    float uj = 0.f, zd = 0.f, qd = 0.f;
+    const float ulast = A.u[rows - 1];      // the final draw's uniform (checked below by thread rows - 1)
+    if (tid < rows) {
+        uj = A.u[tid];
+        bad |= !(uj >= 0.f && uj < 1.f);
+    }
+    if (tid < rows - 1) {
+        dj = A.d[tid];
+        s_d[tid] = dj;
+        if (dj >= 0 && dj < v) {
+            zd = A.z[(int64_t)tid * A.ldz + dj];
+            qd = A.q[(int64_t)tid * A.ldq + dj];
+        } else {
+            bad = 1;
+        }
+    }
+    if (tid < 8 * kMaxRows) {      // whole waves: eight lanes per row
         const int jj = tid >> 3, k = tid & 7;
         const float2 rs = row_stats8(W.stats + (int64_t)min(jj, rows - 1) * nchunks, nchunks, k);
         if (k == 0 && jj < rows) s_rows[jj] = rs;
     }
-    // draft ids and uniforms in range (they index memory below)
-    int bad = 0;
-    if (tid < rows) {
-        const float uu = A.u[tid];
-        bad |= !(uu >= 0.f && uu < 1.f);
-    }
-    if (tid < rows - 1) {
-        s_d[tid] = A.d[tid];
-        bad |= (A.d[tid] < 0 || A.d[tid] >= v);
-    }
-    if (tid == 0) s_jr = rows - 1;
     bad = __syncthreads_or(bad);
-    // Accept tests of all drafts at once (thread j tests draft j): the first
-    // reject ends the accepted prefix and supplies the final draw, else the
-    // last row does.
-    if (!bad && tid < rows - 1) {
-        const RowView r = row_view(A, W, s_rows[tid], tid);
-        const int dj = s_d[tid];
-        const float pd = p_of(A, s_d, nullptr, r, tid, dj, A.z[(int64_t)tid * A.ldz + dj]);
-        const float qd = q_of(A, r, dj, A.q[(int64_t)tid * A.ldq + dj]);
-        if (!(A.u[tid] * qd < pd)) atomicMin(&s_jr, tid);
+    // Accept tests of all drafts at once (thread j of wave 0 tests draft j):
+    // the first reject ends the accepted prefix and supplies the final draw,
+    // else the last row does.
+    if (w == 0) {
+        bool reject = false;
+        if (!bad && tid < rows - 1) {
+            const RowView r = row_view(A, W, s_rows[tid], tid);
+            const float pd = p_of(A, s_d, nullptr, r, tid, dj, zd);
+            reject = !(uj * q_of(A, r, dj, qd) < pd);
+        }
+        const unsigned long long b = __ballot(reject);
+        if (lane == 0) s_jr = b != 0ull ? __ffsll((long long)b) - 1 : rows - 1;
     }
     __syncthreads();
-    const int jr = s_jr;
-    build_bloom(s_bloom, s_d, jr);
+    const int jr = __builtin_amdgcn_readfirstlane(s_jr);     // the same on every thread
+    if (A.pen) build_bloom(s_bloom, s_d, jr);
     const bool draft_row = jr < rows - 1;
     const RowView rv = row_view(A, W, s_rows[jr], jr);
+    const float *zj = A.z + (int64_t)jr * A.ldz;
+    const float *qj = A.q + (int64_t)jr * A.ldq;
     {
         const int v0 = c * CH, v1 = min(v, v0 + CH);
-        const float *zr = A.z + (int64_t)jr * A.ldz;
-        const float *qr = A.q + (int64_t)jr * A.ldq;
-        float res = 0.f, pm = 0.f;
+        float4 zv[DG], qv[DG];
+        load_chunk<DT, DG>(zv, zj, v0, v1, A.vec_z);
+        if (draft_row) load_chunk<DT, DG>(qv, qj, v0, v1, A.vec_q);
 #pragma unroll
-        for (int i = 0; i < EPT; ++i) {
-            const int col = v0 + tid + TPB * i;
-            if (col < v1) {
-                const float p = p_of(A, s_d, s_bloom, rv, jr, col, zr[col]);
-                pm += p;
-                if (draft_row) res += fmaxf(0.f, p - q_of(A, rv, col, qr[col]));
+        for (int i = 0; i < DG; ++i) {
+            float res = 0.f, pm = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int col = v0 + 4 * (tid + DT * i) + e;
+                if (col < v1) {
+                    const float p = p_of(A, s_d, s_bloom, rv, jr, col, f4(zv[i], e));
+                    pm += p;
+                    if (draft_row) res += fmaxf(0.f, p - q_of(A, rv, col, f4(qv[i], e)));
+                }
             }
+            res = wave_sum(res);
+            pm = wave_sum(pm);
+            if (lane == 0) store_f2(&W.mass[(int64_t)c * NSEG + DW * i + w], make_float2(res, pm));
         }
-        const float rmass = block_sum<TPB>(res, scratch);
-        const float pmass = block_sum<TPB>(pm, scratch);
-        // arrival: thread 0 wrote this workgroup's masses and waits for them
-        // to complete before it signals
-        if (tid == 0) {
-            store_f2(&W.mass[c], make_float2(rmass, pmass));
-            __builtin_amdgcn_s_waitcnt(0x0f70);     // vmcnt(0)
-            s_flag[0] = atomicAdd(W.counter, 1u) == (uint32_t)(nchunks - 1);
-        }
+        // arrival: each wave's stores complete before the workgroup signals
+        __builtin_amdgcn_s_waitcnt(0x0f70);     // vmcnt(0)
     }
     __syncthreads();
-    if (!s_flag[0]) return;
+    if (tid == 0) s_flag = atomicAdd(W.counter, 1u) == (uint32_t)(nchunks - 1);
+    __syncthreads();
+    if (!s_flag) return;
 
-    // faults: any flagged chunk (non-finite logit, bad q or count), a uniform or draft id out of range
-    for (int i = tid; i < rows * nchunks; i += TPB) bad |= W.flags[i] != 0;
+    // The last workgroup.  Faults (any flagged chunk; ids and uniforms were
+    // checked above) and this thread's run of consecutive segments, read
+    // together; the first kRun masses stay in registers.
+    constexpr int kRun = 2;
+    const int per = (nseg + DT - 1) / DT;
+    const int s0 = min(nseg, tid * per), s1 = min(nseg, s0 + per);
+    {
+        constexpr int F = 2;     // flag words per thread fetched together
+        const int nf = rows * nchunks;
+        int32_t fl[F];
+#pragma unroll
+        for (int f = 0; f < F; ++f) fl[f] = W.flags[min(tid + DT * f, nf - 1)];     // no branch: one wait
+        for (int i = tid + DT * F; i < nf; i += DT) bad |= W.flags[i] != 0;
+#pragma unroll
+        for (int f = 0; f < F; ++f) bad |= fl[f] != 0;
+    }
+    float2 mr[kRun];
+    float tr = 0.f, tp = 0.f;
+#pragma unroll
+    for (int k = 0; k < kRun; ++k) {
+        mr[k] = s0 + k < s1 ? load_f2(&W.mass[s0 + k]) : make_float2(0.f, 0.f);
+        tr += mr[k].x;
+        tp += mr[k].y;
+    }
+    for (int s = s0 + kRun; s < s1; ++s) {
+        const float2 mm = load_f2(&W.mass[s]);
+        tr += mm.x;
+        tp += mm.y;
+    }
     bad = __syncthreads_or(bad);
     if (bad) {
         if (tid < rows) A.committed[tid] = -1;
@@ -1046,113 +1151,139 @@ __global__ __launch_bounds__(TPB) void sample_decide_kernel(const SampleArgs A) 
         }
         return;
     }
-    if (tid < jr) A.committed[tid] = s_d[tid];
+    // totals over the segments in a fixed order (runs in thread order)
+    {
+        const float a = wave_sum(tr), b = wave_sum(tp);
+        if (lane == 0) {
+            s_tot[0][w] = a;
+            s_tot[1][w] = b;
+        }
+    }
     if (tid == 0) {
-        s_lastc = -1;
         s_cut = ~0ull;
+        s_lastseg = -1;
+    }
+    __syncthreads();
+    float total_res = s_tot[0][0], total_p = s_tot[1][0];
+    for (int k = 1; k < DW; ++k) {
+        total_res += s_tot[0][k];
+        total_p += s_tot[1][k];
     }
     // mass to sample from: the residual on a reject (p if it has none), p for
-    // the bonus; totals over the chunks in a fixed order
-    float tr = 0.f, tp = 0.f;
-    for (int cc = tid; cc < nchunks; cc += TPB) {
-        const float2 mm = load_f2(&W.mass[cc]);
-        tr += mm.x;
-        tp += mm.y;
+    // the bonus
+    const bool use_res = __builtin_amdgcn_readfirstlane(draft_row && total_res > 0.f);
+    const float thr = ulast * (use_res ? total_res : total_p);
+    // exclusive prefix of the run totals in thread order (wave scan, then the
+    // waves before), then the first segment whose inclusive prefix exceeds thr
+    const float mine = use_res ? tr : tp;
+    float incl = mine;
+    for (int off = 1; off < 64; off <<= 1) {
+        const float t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
     }
-    const float total_res = block_sum<TPB>(tr, scratch);
-    const float total_p = block_sum<TPB>(tp, scratch);
-    const int use_res = draft_row && total_res > 0.f;
-    const float thr = A.u[rows - 1] * (use_res ? total_res : total_p);
-    // chunk holding the draw: the first whose inclusive prefix of masses
-    // exceeds thr (prefix sums in chunk order, TPB chunks per round); its
-    // exclusive prefix travels with it in one 64-bit key
-    float carry = 0.f;
-    for (int b0 = 0; b0 < nchunks; b0 += TPB) {
-        const int cc = b0 + tid;
-        float mc = 0.f;
-        if (cc < nchunks) {
-            const float2 mm = load_f2(&W.mass[cc]);
-            mc = use_res ? mm.x : mm.y;
+    float run = __shfl_up(incl, 1);
+    if (lane == 0) run = 0.f;
+    if (lane == 63) s_scan[w] = incl;
+    __syncthreads();
+    for (int k = 0; k < w; ++k) run += s_scan[k];
+    // this thread's first crossing (segment and exclusive prefix) and its last
+    // segment with mass
+    bool found = false;
+    int lastseg = -1;
+    unsigned long long key = ~0ull;
+#pragma unroll
+    for (int k = 0; k < kRun; ++k) {
+        const float m = use_res ? mr[k].x : mr[k].y;
+        if (s0 + k < s1 && !found) {
+            if (run + m > thr) {
+                key = ((unsigned long long)(s0 + k) << 32) | __float_as_uint(run);
+                found = true;
+            }
+            run += m;
         }
-        s_pref[tid] = mc;
-        __syncthreads();
-        for (int off = 1; off < TPB; off <<= 1) {
-            const float add = tid >= off ? s_pref[tid - off] : 0.f;
-            __syncthreads();
-            s_pref[tid] += add;
-            __syncthreads();
-        }
-        const float incl = carry + s_pref[tid];
-        if (cc < nchunks && incl > thr)
-            atomicMin(&s_cut, ((unsigned long long)cc << 32) | __float_as_uint(incl - mc));
-        if (cc < nchunks && mc > 0.f) atomicMax(&s_lastc, cc);
-        carry += s_pref[TPB - 1];
-        __syncthreads();
+        if (s0 + k < s1 && m > 0.f) lastseg = s0 + k;
     }
+    for (int s = s0 + kRun; s < s1; ++s) {
+        const float2 mm = load_f2(&W.mass[s]);
+        const float m = use_res ? mm.x : mm.y;
+        if (!found) {
+            if (run + m > thr) {
+                key = ((unsigned long long)s << 32) | __float_as_uint(run);
+                found = true;
+            }
+            run += m;
+        }
+        if (m > 0.f) lastseg = s;
+    }
+    // segments grow with the lane, so the wave's first crossing is its lowest
+    // finding lane and its last segment with mass its highest lane that has
+    // one: one LDS atomic per wave each
+    {
+        const unsigned long long bf = __ballot(found), bl = __ballot(lastseg >= 0);
+        if (bf != 0ull && lane == __ffsll((long long)bf) - 1) atomicMin(&s_cut, key);
+        if (bl != 0ull && lane == 63 - __clzll((long long)bl)) atomicMax(&s_lastseg, lastseg);
+    }
+    __syncthreads();
+    if (w != 0) return;
     const unsigned long long cut = s_cut;
-    int cstar, last_pos;
+    int sstar;
+    bool last_pos;
     float thr_local;
     if (cut != ~0ull) {
-        cstar = (int)(cut >> 32);
-        last_pos = 0;
+        sstar = (int)(cut >> 32);
+        last_pos = false;
         thr_local = thr - __uint_as_float((uint32_t)cut);
     } else {
-        // no chunk crosses the threshold (rounding): the last chunk with mass
-        cstar = s_lastc >= 0 ? s_lastc : nchunks - 1;
-        last_pos = 1;
+        // no segment crosses the threshold (rounding): the last one with mass
+        sstar = s_lastseg >= 0 ? s_lastseg : nseg - 1;
+        last_pos = true;
         thr_local = 0.f;
     }
-    __syncthreads();
-
-    // inverse CDF inside chunk cstar: thread t owns EPT consecutive logits
-    const int base = cstar * CH + tid * EPT;
-    const float *zj = A.z + (int64_t)jr * A.ldz;
-    const float *qj = A.q + (int64_t)jr * A.ldq;
-    float wv[EPT];
+    sstar = __builtin_amdgcn_readfirstlane(sstar);
+    // inverse CDF inside segment sstar: one wave, four consecutive columns per
+    // lane, prefix sums in column order
+    const int col0 = sstar * SEG + 4 * lane;
+    const bool in = sstar * SEG + SEG <= v;
+    const float4 z4 = load4(zj, col0, v, in && A.vec_z, 0.f);
+    float4 q4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (use_res) q4 = load4(qj, col0, v, in && A.vec_q, 0.f);
+    float wv[4];
     float tot = 0.f;
 #pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-        const int col = base + i;
+    for (int e = 0; e < 4; ++e) {
+        const int col = col0 + e;
         float wgt = 0.f;
         if (col < v) {
-            const float p = p_of(A, s_d, s_bloom, rv, jr, col, zj[col]);
-            wgt = use_res ? fmaxf(0.f, p - q_of(A, rv, col, qj[col])) : p;
+            const float p = p_of(A, s_d, s_bloom, rv, jr, col, f4(z4, e));
+            wgt = use_res ? fmaxf(0.f, p - q_of(A, rv, col, f4(q4, e))) : p;
         }
-        wv[i] = wgt;
+        wv[e] = wgt;
         tot += wgt;
     }
-    // exclusive prefix of the per-thread totals, in thread order
-    s_pref[tid] = tot;
-    __syncthreads();
-    for (int off = 1; off < TPB; off <<= 1) {
-        const float add = tid >= off ? s_pref[tid - off] : 0.f;
-        __syncthreads();
-        s_pref[tid] += add;
-        __syncthreads();
+    float incl2 = tot;
+    for (int off = 1; off < 64; off <<= 1) {
+        const float t = __shfl_up(incl2, off);
+        if (lane >= off) incl2 += t;
     }
-    float run = s_pref[tid] - tot;   // exclusive prefix
+    float run2 = __shfl_up(incl2, 1);
+    if (lane == 0) run2 = 0.f;
     int pick = 0x7fffffff, lastp = -1;
 #pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-        run += wv[i];
-        if (!last_pos && pick == 0x7fffffff && run > thr_local) pick = base + i;
-        if (wv[i] > 0.f) lastp = base + i;
+    for (int e = 0; e < 4; ++e) {
+        run2 += wv[e];
+        if (!last_pos && pick == 0x7fffffff && run2 > thr_local) pick = col0 + e;
+        if (wv[e] > 0.f) lastp = col0 + e;
     }
-    // smallest pick over threads; largest positive index as the rounding fallback
-    __shared__ int s_pick, s_last;
-    if (tid == 0) {
-        s_pick = 0x7fffffff;
-        s_last = -1;
+    // the smallest pick over the wave; the largest positive column as the
+    // rounding fallback
+    for (int off = 32; off > 0; off >>= 1) {
+        pick = min(pick, __shfl_xor(pick, off));
+        lastp = max(lastp, __shfl_xor(lastp, off));
     }
-    __syncthreads();
-    atomicMin(&s_pick, pick);
-    atomicMax(&s_last, lastp);
-    __syncthreads();
-    if (tid == 0) {
-        int tok = s_pick;
-        if (tok == 0x7fffffff) tok = s_last >= 0 ? s_last : min(v - 1, cstar * CH + CH - 1);
-        A.committed[jr] = tok;
-        for (int i = jr + 1; i < rows; ++i) A.committed[i] = -1;
+    // the accepted drafts, the drawn token, -1 after it (rows <= 64 = one wave)
+    const int tok = pick != 0x7fffffff ? pick : lastp >= 0 ? lastp : min(v - 1, sstar * SEG + SEG - 1);
+    if (lane < rows) A.committed[lane] = lane < jr ? s_d[lane] : lane == jr ? tok : -1;
+    if (lane == 0) {
         A.accept_len[0] = jr + 1;
         atomicExch(W.counter, 0u);
     }
@@ -1187,6 +1318,8 @@ hipError_t launch_accept_sample(const SampleParams &P, hipStream_t s) {
     A.counts = P.counts;
     A.pen = P.presence != 0.f || P.frequency != 0.f;
     A.trunc = (P.top_k > 0 && P.top_k < P.v) || P.top_p < 1.f;
+    A.vec_z = ((uintptr_t)P.z % 16) == 0 && P.ldz % 4 == 0;
+    A.vec_q = ((uintptr_t)P.q % 16) == 0 && P.ldq % 4 == 0;
     A.accept_len = P.accept_len;
     A.committed = P.committed;
     A.ws = P.ws;
@@ -1202,7 +1335,7 @@ hipError_t launch_accept_sample(const SampleParams &P, hipStream_t s) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(sample_decide_kernel, dim3(nchunks), dim3(TPB), 0, s, A);
+    hipLaunchKernelGGL(sample_decide_kernel, dim3(nchunks), dim3(DT), 0, s, A);
     return hipGetLastError();
 }
 

@@ -11,6 +11,7 @@ namespace dspk {
 
 constexpr int kSampleSlice = 8192;   // entries per workgroup of the binning pass (<= 2^13)
 constexpr int kSampleBins = 2048;    // histogram bins per level
+constexpr int kSampleSeg = 256;      // columns per segment of the drawing row's masses
 
 struct SampleWsLayout {
     size_t stats, flags, qmax, mass, trunc, pcnt, pmass, bin1, total;
@@ -20,8 +21,8 @@ struct SampleWsLayout {
 constexpr size_t sample_align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // [0, 256) arrival counter; then per (row, chunk) {max, sum exp} (8 B), the
-// fault flag (4 B) and the max of q (4 B); per chunk the {residual, p} masses
-// of the drawing row (8 B); per (row, distribution) the truncation record
+// fault flag (4 B) and the max of q (4 B); per 256-column segment the
+// {residual, p} masses of the drawing row (8 B); per (row, distribution) the truncation record
 // (16 B); and, used only when truncating, per (row, distribution, slice) the
 // first-level histograms (NB x u32 counts, NB x u64 masses) and per (row,
 // distribution) the first-level bin of every entry (u16).
@@ -39,7 +40,7 @@ constexpr SampleWsLayout sample_ws_layout(int rows, int v) {
     L.qmax = o;
     o += sample_align256(rows * nchunks * 4);
     L.mass = o;
-    o += sample_align256(nchunks * 8);
+    o += sample_align256(nchunks * (kSampleChunk / kSampleSeg) * 8);
     L.trunc = o;
     o += sample_align256((size_t)rows * 2 * 16);
     L.pcnt = o;
