@@ -24,9 +24,13 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Every data pointer is DEVICE memory (hipMalloc / torch) owned by the
- *   caller.  The library never allocates, frees or synchronises; every call
- *   only enqueues kernels on `stream` (a hipStream_t, NULL = default stream)
- *   and returns.  Results are valid once the stream reaches that point.
+ *   caller, except that the acceptance results (accept_len, committed) may
+ *   also be pinned host memory mapped for the device (hipHostMalloc, torch
+ *   pin_memory): the kernels only write them, so a round's result can land on
+ *   the host with no copy launch.  The library never allocates, frees or
+ *   synchronises; every call only enqueues kernels on `stream` (a
+ *   hipStream_t, NULL = default stream) and returns.  Results are valid once
+ *   the stream reaches that point.
  * - Return value: DSPK_OK (0) on success, a negative DSPK_E* code otherwise;
  *   dspk_last_error() then holds a message (thread-local).  Nothing is
  *   enqueued when a call fails its argument checks.  There is no fallback

@@ -89,6 +89,47 @@ def test_fused_head_accept_equals_separate_calls(b, rows):
         assert np.all(al_sep == 1) and np.array_equal(com_sep[:, 0], ids_sep)
 
 
+def test_results_written_to_pinned_host_memory():
+    """The acceptance outputs may be pinned host memory mapped for the device:
+    the fused greedy head and the sampling accept write there exactly what
+    they write to device memory, with no copy launch."""
+    import torch
+    from speculative_decoding_verify_dspk_amd import binding
+    from gpuutil import dev_act
+    b, rows, k, v = 2, 6, 2048, 8192
+    m = b * rows
+    head = inputs.make_qweight(v, k, 8, "pinned", "head")
+    h_bits = inputs.make_activations(m, k, "pinned", "h")
+    dw = binding.DeviceQWeight.upload(head)
+    h = dev_act(h_bits)
+    ids, z = run_lmhead(head, h_bits, m, want_logits=True, dw=dw)
+    d = inputs.drafts_match_rate(ids.reshape(b, rows), np.full(b, 0.7), v, "pinned", "d")
+    dd = torch.from_numpy(np.ascontiguousarray(d, dtype=np.int32)).cuda()
+    ws = binding.alloc_workspace(binding.lmhead_workspace_bytes(v, m))
+    am = torch.empty((m,), dtype=torch.int32, device="cuda")
+    q, ds = inputs.draft_distribution(z[:rows], 1.0, 0.5, "pinned", "q")
+    u = inputs.make_uniforms(rows, "pinned", "u")
+    zt = torch.from_numpy(np.ascontiguousarray(z[:rows])).cuda()
+    qt = torch.from_numpy(np.ascontiguousarray(q)).cuda()
+    dst = torch.from_numpy(ds).cuda()
+    ut = torch.from_numpy(u).cuda()
+    sws = binding.alloc_workspace(binding.sample_workspace_bytes(v, rows))
+    got = {}
+    for where in ("device", "pinned"):
+        kw = dict(device="cuda") if where == "device" else dict(pin_memory=True)
+        al = torch.full((b,), -7, dtype=torch.int32, **kw)
+        com = torch.full((b, rows), -7, dtype=torch.int32, **kw)
+        binding.lmhead_argmax_accept_greedy(dw, h, b, rows, am, dd, al, com, workspace=ws)
+        sal = torch.full((1,), -7, dtype=torch.int32, **kw)
+        scom = torch.full((rows,), -7, dtype=torch.int32, **kw)
+        binding.accept_sample(zt, qt, dst, ut, rows, v, 1.0, sal, scom, sws)
+        torch.cuda.synchronize()
+        got[where] = [x.cpu().numpy().copy() for x in (al, com, sal, scom)]
+    for a, c in zip(got["device"], got["pinned"]):
+        assert np.array_equal(a, c)
+    assert np.all(got["pinned"][0] >= 1) and 1 <= got["pinned"][2][0] <= rows
+
+
 def test_graph_replays_match_eager_round():
     """A round captured into HIP graphs (layers, head, accept) and replayed
     several times, with eager work and synchronisations in between, gives
