@@ -53,7 +53,7 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
 SWEEP = (1, 2, 4, 6, 8, 12, 16)
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
@@ -91,7 +91,7 @@ def parse():
     ap.add_argument("--calibrate", action="store_true",
                     help="after the timed region, run one plain device copy of 256 MiB (the reference "
                          "dispatch for scaling hardware byte counters)")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 def cpu_baseline(model: str, bits: int, m: int, budget_s: float):
@@ -433,6 +433,49 @@ def main():
     if args.prefill > 0:
         prefill_bench(args)
         return
+    out = run_workload(args)
+    if not args.no_extras and args.config == "qwen3-4b" and args.layers == 1 and args.batch == 1:
+        out["other_configs"] = other_configs(args)
+    print(json.dumps(out))
+
+
+# The scope's other workloads, run after the headline one through the same
+# round machinery (fewer steps, no extras): their wall-clock weight-GB/s and
+# per-width device curve.
+OTHER_CONFIGS = [
+    ("ornith-9b 4-bit knee", ["--config", "ornith-9b", "--bits", "4", "--sweep", "1,2,4,8,12,16", "--copies", "2"]),
+    ("ornith-9b 8-bit knee", ["--config", "ornith-9b", "--bits", "8", "--sweep", "1,2,4,8,12,16", "--copies", "2"]),
+    ("ornith-9b bf16 knee", ["--config", "ornith-9b", "--bits", "16", "--sweep", "1,2,4,8,12,16", "--copies", "2"]),
+    ("dense-27b 64 layers, 17 rows, speculative sampling T=1",
+     ["--config", "dense-27b", "--layers", "64", "--sweep", "17", "--copies", "1", "--accept", "sample"]),
+    ("qwen3-8b, 4 requests x 6 rows, greedy per request",
+     ["--config", "qwen3-8b", "--batch", "4", "--sweep", "6", "--alpha", "0.3,0.5,0.7,0.9", "--copies", "2"]),
+]
+
+
+def other_configs(args):
+    import torch
+    res = {}
+    for name, extra in OTHER_CONFIGS:
+        sub = parse(extra + ["--steps", str(max(3, args.steps // 2)), "--warmup", "1", "--no-extras",
+                             "--no-cpu-baseline", "--draft-sets", "2"])
+        o = run_workload(sub)
+        torch.cuda.empty_cache()
+        res[name] = {"workload": o["config"]["workload"], "weight_bytes_per_round": o["config"]["weight_bytes_per_round"],
+                     "value_weight_GBps": o["value"], "hbm_frac": o["hbm_frac"],
+                     "round_wall_us_p50": o["round_wall_us"]["p50"],
+                     "committed_tokens_per_round": o["committed_tokens_per_round"],
+                     "committed_by_width": o["committed_by_width"],
+                     "curve": {k: {kk: v[kk] for kk in ("round_us", "layer_us", "head_us", "accept_us",
+                                                          "hbm_frac", "t_over_t1")}
+                               for k, v in o["curve"].items()},
+                     "head_avg_launch_us": o["roofline"]["avg_launch_us"]}
+    return res
+
+
+def run_workload(args) -> dict:
+    """The verify rounds of one workload: the timed serving loop, then the
+    event-instrumented pass; returns the result line as a dict."""
     import torch
     from speculative_decoding_verify_dspk_amd import binding, inputs
     from speculative_decoding_verify_dspk_amd.verify_round import VerifyStack
@@ -704,7 +747,8 @@ def main():
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(0), "host": platform.node(),
     }
-    print(json.dumps(out))
+    del stack
+    return out
 
 
 if __name__ == "__main__":
