@@ -10,8 +10,9 @@ greedy acceptance of drafts that match the target's token with probability
 M = 1, 2, 4, 6, 8, 12, 16 (the verify-cost curve); each round is
   4 projection launches per layer + head/argmax with the greedy acceptance in
   its last workgroup (one launch; sampling rounds launch the accept kernels
-  after the head), which write the result to pinned host memory directly,
-  + one stream sync,
+  after the head), which write the result to pinned host memory directly;
+  the host waits for the result words themselves (no copy launch, no stream
+  sync),
 launched from the host with arguments marshalled once per width and weight
 copy (--graph replays HIP graphs of the same calls instead).
 
@@ -157,6 +158,23 @@ def measured_traffic():
 
 
 MFMA_BF16_PEAK_TFS = 2500.0   # MI355X dense bf16 matrix peak, published
+
+PENDING = -12345   # no accept_len or committed entry ever takes this value
+
+
+def wait_result(res_np, stream, spin_s: float = 2.0):
+    """Wait for a round's result by watching its pinned buffer: the
+    acceptance writes every accept_len and committed entry exactly once, so
+    the round is complete (for the host) once no entry still holds PENDING,
+    whatever order the writes arrive in.  After spin_s of spinning, fall back
+    to a stream sync and fail if an entry is still missing."""
+    t0 = time.perf_counter()
+    while (res_np == PENDING).any():
+        if time.perf_counter() - t0 > spin_s:
+            stream.synchronize()
+            if (res_np == PENDING).any():
+                raise RuntimeError("bench.py: a round's result never arrived in host memory")
+            break
 
 
 def prefill_bench(args):
@@ -519,6 +537,7 @@ def run_workload(args) -> dict:
                 # writes the round's result straight to the host (no copy launch)
                 res = torch.empty((B + B * m,), dtype=torch.int32, pin_memory=True)
                 r = dict(res=res, res_np=res.numpy(), alen=res[:B], com=res[B:].view(B, m))
+                r["res_np"][:] = PENDING
                 if sample:
                     q, d = inputs.draft_distribution(z, args.temperature, args.noise, "bench", args.config, m, cp,
                                                      si)
@@ -576,6 +595,7 @@ def run_workload(args) -> dict:
         """Round number k at width m: weight copy k % copies, draft set (k // copies) % S."""
         copy, si = k % args.copies, (k // args.copies) % S
         r = rounds_in[(m, copy, si)]
+        r["res_np"][:] = PENDING
         e = [ev() for _ in range(4)] if record is not None else None
         if e: e[0].record(stream)
         if args.graph:
@@ -594,10 +614,13 @@ def run_workload(args) -> dict:
             if e: e[2].record(stream)
             accept()
         if e: e[3].record(stream)
-        stream.synchronize()       # the round's one device sync
+        if e is None:
+            wait_result(r["res_np"], stream)
+        else:
+            stream.synchronize()   # the event-instrumented pass
         if record is not None:
             record.append((m, e))
-        return r["res_np"]         # the round's result, already in host memory
+        return r["res_np"]         # the round's result, in host memory
 
     step_copy = 0
     for _ in range(args.warmup):
@@ -613,8 +636,8 @@ def run_workload(args) -> dict:
     gc.collect()
     gc.freeze()
     # Timed region: K steps of rounds as a serving loop runs them -- launch,
-    # one sync, read the accept lengths from host memory -- with no timing
-    # events.
+    # wait for the result words in pinned host memory, read the accept
+    # lengths -- with no timing events.
     committed = 0
     committed_by_width = {m: 0 for m in sweep}
     faults = 0
