@@ -127,6 +127,34 @@ def test_sample_matches_oracle(v, m_rows, T):
     assert n_exempt <= max(1, trials // 10)
 
 
+@pytest.mark.parametrize("v,ldz,offset", [(8194, 8196, 0), (8194, 8200, 1), (12288, 12292, 2), (4096, 4100, 3)])
+def test_sample_padded_and_unaligned_rows(v, ldz, offset):
+    """Row strides past v and base pointers off 16-byte boundaries take the
+    kernels' clamped-load path; the decisions are those of contiguous rows
+    exactly (same arithmetic per entry), and match the oracle."""
+    tt = torch()
+    g = np.random.default_rng(v + ldz + offset)
+    m_rows = 9
+    for i in range(6):
+        z, q, d, u = make_block(g, v, m_rows, 1.0)
+        al0, com0 = gpu_sample(z, q, d, u, 1.0)
+
+        def strided(a):
+            buf = tt.zeros(offset + a.shape[0] * ldz, dtype=tt.float32, device="cuda")
+            view = buf[offset:offset + a.shape[0] * ldz].view(a.shape[0], ldz)
+            view[:, :v] = tt.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+            return view[:, :v]
+        al = tt.full((1,), -9, dtype=tt.int32, device="cuda")
+        com = tt.full((m_rows,), -9, dtype=tt.int32, device="cuda")
+        ws = binding.alloc_workspace(binding.sample_workspace_bytes(v, m_rows))
+        binding.accept_sample(strided(z), strided(q), dev_i32(d), dev_f32(u), m_rows, v, 1.0, al, com, ws)
+        tt.cuda.synchronize()
+        assert int(al.cpu()[0]) == al0 and np.array_equal(com.cpu().numpy(), com0), f"trial {i}"
+        ral, rcom = oracle.accept_sample(z.astype(np.float64), q, d, u, 1.0)
+        if al0 != ral or not np.array_equal(com0, rcom):
+            assert exempt(z, q.astype(np.float64), d, u.astype(np.float64), 1.0), f"trial {i} vs oracle"
+
+
 def test_sample_golden_hand_cases():
     for c in json.load(open(GOLDEN))["sample"]:
         if not (c["T"] > 0):
