@@ -445,7 +445,7 @@ def main():
         variant_curves(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only (the verify pass is not sharded); "
+        print("bench.py: the verify pass runs on one GPU here (it is not sharded); "
               "use --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.prefill > 0:

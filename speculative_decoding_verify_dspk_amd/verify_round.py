@@ -2,9 +2,10 @@
 
 A round ("mlx-dspark" wiki summary, "Architecture"): every projection of the
 target over the M rows (anchor + drafts, or B requests x rows), the vocabulary
-head with the row argmax (or logits for sampling), the acceptance step, and one
-device-to-host copy of the round's result ("mlx-dspark releases", v0.2.0 notes:
-one device sync per round).
+head with the row argmax (or logits for sampling), and the acceptance step,
+whose few result words the caller may have written straight into pinned host
+memory ("mlx-dspark releases", v0.2.0 notes: at most one device sync per
+round).
 
 Weights and activations are seeded synthetic tensors of the workload's shapes
 (``inputs.LAYER_SHAPES``).  Each decoder layer contributes four launches, as a
