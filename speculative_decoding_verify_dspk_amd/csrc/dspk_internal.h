@@ -154,15 +154,23 @@ constexpr int kDotMaxRows = 4;
 // the activations in LDS; other calls keep them in registers.  kAuto takes
 // the slab kernel for 8-bit and bf16 calls of at most kSlabLdsMaxRows rows
 // when the weights one CU streams for its tiles (tiles per CU x 16 x k) are
-// at most kSlabAutoWeightsNarrow (<= 8 rows) or kSlabAutoWeightsWide (9..16
-// rows).  Per-launch rocprof durations, slab vs stream-K, 1 / 8 / 16 rows:
+// at most kSlabAutoWeightsNarrow (<= 8 rows), or, at 9..16 rows, at most
+// kSlabAutoWeightsWide with k <= kSlabAutoMaxKWide and the tiles filling at
+// least three quarters of the CUs' last round.  Per-launch rocprof
+// durations, slab vs stream-K, 1 / 8 / 16 rows:
 //   Qwen3-4B o  (160 tiles, k 4096)   6.8 / 7.4 / 8.0  vs 10.3 / 10.5 / 11.0 us
 //   Qwen3-4B gate/up (1216, k 2560)  16.1 / 17.7 / 19.1 vs 18.0 / 18.7 / 20.0
 //   27B down    (320 tiles, k 17408) 26.2 / 34.6 / 43.2 vs 22.6 / 22.9 / 23.9
 //   9B gate/up  (1536 tiles, k 4096) 25.2 / 28.8 / 32.9 vs 24.6 / 24.6 / 25.7
+// and at 9 / 12 / 16 rows:
+//   27B q/k/v   (448 tiles, k 5120)  13.7 / 14.9 / 16.1 vs 16.7 / 16.8 / 17.1
+//   27B o       (320 tiles, k 5120)  12.7 / 13.6 / 15.4 vs 13.2 / 13.0 / 13.0
+//   Qwen3-4B down (160, k 9728)      12.1 / 13.0 / 14.4 vs 13.2 / 13.4 / 13.5
+//   9B down     (256 tiles, k 12288) 16.4 / 17.5 / 18.6 vs 15.7 / 15.1 / 15.7
 constexpr int kSlabLdsMaxRows = 16;
 constexpr int64_t kSlabAutoWeightsNarrow = 320 * 1024;
-constexpr int64_t kSlabAutoWeightsWide = 96 * 1024;
+constexpr int64_t kSlabAutoWeightsWide = 200 * 1024;
+constexpr int32_t kSlabAutoMaxKWide = 5120;
 int projection_variant();               // the process-wide setting (DSPK_VARIANT, or the setter)
 int set_projection_variant(int v);      // previous setting, or -1 if v is not a Variant
 
