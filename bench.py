@@ -95,6 +95,26 @@ def parse(argv=None):
     return ap.parse_args(argv)
 
 
+def host_cpu() -> dict:
+    """The host's CPU model and numpy's BLAS library, for the CPU baseline."""
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = ""
+    try:
+        cfg = np.show_config(mode="dicts")
+        blas = cfg.get("Build Dependencies", {}).get("blas", {}).get("name", "")
+    except Exception:     # older numpy: no dict form
+        pass
+    return {"cpu_model": model, "blas": blas}
+
+
 def cpu_baseline(model: str, bits: int, m: int, budget_s: float):
     """The oracle, as it stands, on one verify round of the same workload:
     every projection of one layer at width m, then as many 8192-entry slices
@@ -127,7 +147,7 @@ def cpu_baseline(model: str, bits: int, m: int, budget_s: float):
         done_bytes += inputs.weight_bytes(n, h, bits)
         slices += 1
     return {"value": round(done_bytes / t_total / 1e9, 4), "unit": "weight-GB/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", **host_cpu(),
             "sample": f"one {model} layer (7 projections) + {slices} x {sl}-row slices of the {v}x{h} head, "
                       f"{bits}-bit, M={m}; {done_bytes / 1e6:.1f} MB of weights in {t_total:.1f} s "
                       f"(numpy fp64, {threads} threads)"}
@@ -380,6 +400,60 @@ def dense27b_section(steps: int, warmup: int, widths=(1, 8, 16), copies: int = 2
     return out
 
 
+def single_linear_section(steps: int, warmup: int, copies: int = 24):
+    """The correctness-sized workload: one 2048 x 2048 8-bit linear over 6
+    rows, then the 8192 x 2048 8-bit head with the greedy acceptance of 5
+    drafts (the first 3 equal to the head's own tokens, the rest uniform),
+    rotating `copies` weight copies (22 MB per round, so the copies exceed the
+    MALL).  Device time per round from events around the two launches; its
+    weight-GB/s is reported, but launch latency bounds it."""
+    import torch
+    from speculative_decoding_verify_dspk_amd import binding, inputs
+    m, k, n, v = 6, 2048, 2048, 8192
+    stream = torch.cuda.current_stream()
+
+    def qw(rows, *lab):
+        c, sc, bi = inputs.make_qweight_device(rows, k, 8, "bench-c1", *lab)
+        return binding.DeviceQWeight(rows, k, 8, c, sc, bi)
+    lins = [qw(n, "linear", cp) for cp in range(copies)]
+    heads = [qw(v, "head", cp) for cp in range(copies)]
+    x = inputs.make_activations_device(m, k, "bench-c1", "x")
+    h = inputs.make_activations_device(m, k, "bench-c1", "h")
+    y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    am = torch.empty((m,), dtype=torch.int32, device="cuda")
+    ws_l = binding.alloc_workspace(binding.qgemm_workspace_bytes(n, k, m))
+    ws_h = binding.alloc_workspace(binding.lmhead_workspace_bytes(v, m))
+    calls = []
+    for cp in range(copies):
+        binding.lmhead_argmax(heads[cp], h, m, am, None, ws_h, stream)
+        d = inputs.drafts_first_equal(am.cpu().numpy(), 3, v, "bench-c1", cp)
+        dd = torch.from_numpy(np.ascontiguousarray(d, dtype=np.int32)).cuda()
+        res = torch.empty((1 + m,), dtype=torch.int32, pin_memory=True)
+        calls.append((binding.prepare_qgemm(lins[cp], x, m, y, ws_l, stream),
+                      binding.prepare_lmhead_accept_greedy(heads[cp], h, 1, m, am, None, dd, res[:1],
+                                                           res[1:].view(1, m), ws_h, stream), dd, res))
+    times, committed = [], []
+    for it in range(warmup + steps):
+        lin, head, _, res = calls[it % copies]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        lin()
+        head()
+        e1.record(stream)
+        e1.synchronize()
+        if it >= warmup:
+            times.append(e0.elapsed_time(e1) * 1e3)
+            committed.append(int(res[0]))
+    wb = inputs.weight_bytes(n, k, 8) + inputs.weight_bytes(v, k, 8)
+    med = float(np.median(times))
+    return {"workload": "one 2048x2048 8-bit g64 linear at 6 rows + lm_head 8192x2048 8-bit with greedy accept of 5 "
+                        f"drafts (first 3 = the head's tokens), {copies} rotating copies",
+            "weight_bytes_per_round": wb, "round_us": round(med, 2),
+            "round_us_p10_p90": [round(float(np.percentile(times, 10)), 2),
+                                 round(float(np.percentile(times, 90)), 2)],
+            "weight_GBps": round(wb / (med * 1e-6) / 1e9, 1), "committed_tokens_per_round": float(np.mean(committed))}
+
+
 def variant_curves(args):
     """t(M) of each Qwen3-4B 8-bit projection launch under each forced
     decomposition -- stream-K and slab on the matrix cores, and the slab with
@@ -473,7 +547,8 @@ OTHER_CONFIGS = [
 
 def other_configs(args):
     import torch
-    res = {}
+    res = {"single linear + 8192-vocab head, 6 rows": single_linear_section(max(30, args.steps), 5)}
+    torch.cuda.empty_cache()
     for name, extra in OTHER_CONFIGS:
         sub = parse(extra + ["--steps", str(max(3, args.steps // 2)), "--warmup", "1", "--no-extras",
                              "--no-cpu-baseline", "--draft-sets", "2"])
@@ -681,13 +756,17 @@ def run_workload(args) -> dict:
     for m in sweep:
         M = B * m
         rs = [e for (mm, e) in records if mm == m]
-        t_round = np.median([e[0].elapsed_time(e[3]) for e in rs])
+        t_rounds = [e[0].elapsed_time(e[3]) for e in rs]
+        t_round = np.median(t_rounds)
         t_layer = np.median([e[0].elapsed_time(e[1]) for e in rs])
         t_head = [e[1].elapsed_time(e[2]) for e in rs]
         t_acc = np.median([e[2].elapsed_time(e[3]) for e in rs])
         head_ms_all += t_head
         head_bytes_all += [head_b + M * stack.hidden * 2 + (M * V * 4 if sample else M * 4)] * len(t_head)
-        curve[M] = {"round_us": round(float(t_round) * 1e3, 2), "layer_us": round(float(t_layer) * 1e3, 2),
+        curve[M] = {"round_us": round(float(t_round) * 1e3, 2),
+                    "round_us_p10_p90": [round(float(np.percentile(t_rounds, 10)) * 1e3, 2),
+                                         round(float(np.percentile(t_rounds, 90)) * 1e3, 2)],
+                    "layer_us": round(float(t_layer) * 1e3, 2),
                     "head_us": round(float(np.median(t_head)) * 1e3, 2),
                     "accept_us": round(float(t_acc) * 1e3, 2),
                     "weight_GBps": round(round_b / (t_round * 1e-3) / 1e9, 1),
@@ -757,6 +836,7 @@ def run_workload(args) -> dict:
         "round_wall_us": {"p50": round(float(np.median(walls)) * 1e6, 1), "max": round(max(walls) * 1e6, 1)},
         "rows_per_s": round(B * sum(sweep) * args.steps / wall, 1),
         "committed_tokens_per_round": round(committed / n_rounds, 3),
+        "committed_tokens_per_s": round(committed / wall, 1),
         # per request and round at each width: measured, and the closed form
         # 1 + sum_{i=1..m-1} alpha^i of independent per-position matches
         "committed_by_width": None if sample else {
