@@ -19,7 +19,10 @@
 // LDS in wave order.  No workspace, no cross-workgroup traffic, results
 // deterministic (the order of every sum is fixed by the shapes).  The launch
 // has one workgroup per tile; the host picks W (16, 8 or 4 waves) so that all
-// of them are resident at once, and uses this kernel only then.
+// of them are resident at once where they fit (16, 8 or 4 workgroups per CU
+// for up to 1, 2 or 4 tiles per CU); with more tiles than that it takes 4
+// waves and the rest run as a second round, which its automatic choice only
+// accepts while the weights per CU stay small.
 //
 // The arithmetic per group is that of the stream-K kernel: exact-product bf16
 // MFMAs on the codes (8-bit codes, or 128 + q below 8 bits) and on a ones
@@ -68,8 +71,9 @@ __device__ __forceinline__ void st_global_u16(uint16_t *p, uint32_t v) {
     asm volatile("global_store_short %0, %1, off" ::"v"(p), "v"(v) : "memory");
 }
 
-// four waves per SIMD (16 per CU) at every W: the plan assumes 16 / W
-// workgroups per CU
+// Every W runs four waves per SIMD (16 per CU): the plan assumes 16 / W
+// workgroups per CU.
+//
 // The register ring of a wave's n units: requests run DEPTH - 1 units ahead
 // of the computation.  The steady-state loop issues without a condition, so
 // the compiler's own count of outstanding loads places each wait just before
