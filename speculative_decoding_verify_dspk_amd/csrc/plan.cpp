@@ -56,10 +56,11 @@ int set_projection_variant(int v) {
 }
 
 // Waves per workgroup of the slab kernel for `slabs` tiles, or 0 when the
-// tiles would not all be resident at once (then stream-K keeps every CU
-// streaming to the end).  At most 128 VGPRs per lane, a CU holds 16 waves:
-// one workgroup of 16, two of 8 or four of 4; the most waves per tile that
-// still fit all tiles are taken, for the most loads in flight per tile.
+// tiles would not all be resident at once (a slab launch then takes 4 waves
+// per workgroup and runs its tiles in more than one round).  At most 128
+// VGPRs per lane, a CU holds 16 waves: one workgroup of 16, two of 8 or four
+// of 4; the most waves per tile that still fit all tiles are taken, for the
+// most loads in flight per tile.
 static int slab_waves_for(int64_t slabs, int cus) {
     if (slabs <= cus) return 16;
     if (slabs <= 2 * (int64_t)cus) return 8;
