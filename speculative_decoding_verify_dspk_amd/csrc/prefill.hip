@@ -4,16 +4,18 @@
 // each weight group is dequantised once and reused for every row of the
 // pass; prefill is the wide-row case of that pass).
 //
-// With hundreds of rows the work is bound by the matrix cores, not by HBM,
-// so this kernel is tiled for MFMA reuse rather than for streaming:
+// With hundreds of rows the work is bound by the matrix cores and the vector
+// ALUs, not by HBM, so this kernel is tiled for MFMA reuse rather than for
+// streaming:
 // * A workgroup computes a 128-row x 128-column block of y: four waves, each
 //   64 rows (four 16-row tiles) x one 64-column weight block (four 16-column
-//   tiles), K walked one tiled unit at a time.
-// * Per unit the workgroup stages its 128 activation rows into LDS (row-major,
-//   rows padded by 16 bytes so the 16 rows one MFMA operand reads fall into
-//   different banks); each wave loads its weight unit straight from the tiled
-//   layout into registers, where every lane already holds its own operand
-//   bytes.
+//   tiles), K walked in stages of 128 (a whole 8-bit unit, half of a 2/3/4-bit
+//   unit, one bf16 unit of 64).
+// * Activations reach LDS by direct global-to-LDS loads (no staging
+//   registers), double-buffered: the next stage is in flight while the
+//   current one is computed.  Each wave loads its weight codes straight from
+//   the tiled layout into registers, where every lane already holds its own
+//   operand bytes, one unit ahead into a second register set.
 // * Codes are exact in bf16, so per group and per 16x16 tile
 //     sum_{r in group} x*w = s * sum x*q + b * sum x
 //   comes from exact-product MFMAs on the codes (fp32 accumulation) plus a
@@ -21,10 +23,12 @@
 //   come from an MFMA against a ones operand.  No dequantised weight is
 //   rounded.  Each activation operand read from LDS serves the four column
 //   tiles, each decoded weight operand the four row tiles.
-// * Two workgroups per CU (LDS <= 68 KiB each): one stages while the other
-//   computes.  Row blocks vary fastest in the grid, so the workgroups that
-//   run together share their weight units in L2.
+// * Two workgroups per CU (64 KiB of LDS each, 32 KiB for bf16).  Row blocks
+//   vary fastest in the grid, so the workgroups that run together share their
+//   weight units in L2.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "decode.h"
 #include "dspk_internal.h"
@@ -37,27 +41,48 @@ using namespace dec;
 constexpr int PBM = 128;                 // rows per workgroup
 constexpr int PT = 256;                  // threads per workgroup
 
+// One stage of K: SK = min(KU, 128) (a whole unit, or half of a 256-K
+// unit) for the workgroup's 128 rows, unpadded (a row is SK bf16 = CH
+// 16-byte chunks), filled by direct global-to-LDS loads.  Such a load writes
+// 16 bytes per lane at consecutive LDS addresses, so bank spreading cannot
+// come from padding: chunk ch of row R sits at position ch ^ (R & SWM) of
+// its row instead, and the load of that position fetches that chunk.  The 16
+// rows that one MFMA operand read touches (same chunk, rows R..R+15 with R a
+// multiple of 16) then fall on distinct positions.
 template <int BITS>
-struct PCfg {
+struct SCfg {
     static constexpr int KU = Cfg<BITS>::KU;
-    static constexpr int LDSW = KU + 8;                    // bf16 per staged row (16-byte pad)
-    static constexpr int CPT = PBM * KU / 8 / PT;          // 16-byte activation chunks per thread per unit
+    static constexpr int SK = KU < 128 ? KU : 128;          // K per stage
+    static constexpr int HALVES = KU / SK;                  // stages per unit
+    static constexpr int GH = SK / 64;                      // groups per stage
+    static constexpr int NSB = BITS == 16 ? 1 : GH;         // scale/bias loads per lane and stage
+    static constexpr int CH = SK / 8;                       // 16-byte chunks per row
+    static constexpr int SWM = CH >= 16 ? 15 : CH - 1;      // position swizzle mask
+    static constexpr int STAGE = PBM * SK;                  // bf16 per stage
+    static constexpr int NI = STAGE / 512;                  // 1 KiB loads per stage (512 bf16)
+    static constexpr int RPI = 64 / CH;                     // rows per 1 KiB load
+    static_assert(NI % (PT / 64) == 0, "stage loads must split evenly over the waves");
+    static_assert(HALVES * GH == Cfg<BITS>::GS, "stages must tile the unit's groups");
 };
-
-// One unit's share of a wave: 64 rows (four 16-row tiles r) x one 64-column
-// weight block (four 16-column tiles t), K = the unit's groups.  xb: the
-// unit's staged activations (row-major, LDSW bf16 per row); wv / sbv: this
-// wave's code slots and scale/bias dwords of the unit.
+// bf16 index of chunk ch of row R in a stage
 template <int BITS>
-__device__ __forceinline__ void prefill_unit(const uint16_t *__restrict__ xb, const u32x4 (&wv)[Cfg<BITS>::NS],
-                                             const u32x4 (&sbv)[Cfg<BITS>::SBQ > 0 ? Cfg<BITS>::SBQ : 1], int ng,
-                                             int wr, int c, int j, f32x4 (&y)[4][4]) {
-    using C = Cfg<BITS>;
-    using P = PCfg<BITS>;
+__device__ __forceinline__ int swz_index(int R, int ch) {
+    using S = SCfg<BITS>;
+    return R * S::SK + 8 * (ch ^ (R & S::SWM));
+}
+
+// One stage's share of a wave: 64 rows (four 16-row tiles r) x one 64-column
+// weight block (four 16-column tiles t), K = the unit's groups G0..G1-1 (the
+// stage's).  xb: the stage; wv: this wave's code slots of the unit; sbv: its
+// scale/bias dwords of the stage's groups; ng: valid groups of the unit.
+template <int BITS, int G0, int G1>
+__device__ __forceinline__ void prefill_stage(const uint16_t *__restrict__ xb, const u32x4 (&wv)[Cfg<BITS>::NS],
+                                              const u32x4 (&sbv)[SCfg<BITS>::NSB], int ng, int wr, int c, int j,
+                                              f32x4 (&y)[4][4]) {
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const bf16x8 ones = as_bf16x8(u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 #pragma unroll
-    for (int g = 0; g < C::GS; ++g) {
+    for (int g = G0; g < G1; ++g) {
         if (g >= ng) break;
         // the four column tiles' weight operands of group g
         bf16x8 bw0[4], bw1[4];
@@ -84,7 +109,7 @@ __device__ __forceinline__ void prefill_unit(const uint16_t *__restrict__ xb, co
                     const uint32_t hd = wv[4 + (t >> 1)][2 * (t & 1) + (g >> 1)];
                     codes3_to_bf16(wv[t][g], hd >> (8 * (g & 1)), bw0[t], bw1[t]);
                 }
-                const uint32_t sbd = sbv[g][t];
+                const uint32_t sbd = sbv[g - G0][t];
                 sc[t] = h2f(sbd & 0xffffu);
                 bi[t] = h2f(sbd >> 16);
                 if constexpr (BITS <= 4) bi[t] = fmaf(-128.f, sc[t], bi[t]);   // codes carry +128
@@ -93,8 +118,9 @@ __device__ __forceinline__ void prefill_unit(const uint16_t *__restrict__ xb, co
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             // lane (c, j): row 64 wr + 16 r + c, K offsets 64 g + 16 j + 0..15
-            const uint16_t *xp = xb + (64 * wr + 16 * r + c) * P::LDSW + 64 * g + 16 * j;
-            const u32x4 x0 = *(const u32x4 *)xp, x1 = *(const u32x4 *)(xp + 8);
+            const int R = 64 * wr + 16 * r + c;
+            const u32x4 x0 = *(const u32x4 *)(xb + swz_index<BITS>(R, 8 * (g - G0) + 2 * j));
+            const u32x4 x1 = *(const u32x4 *)(xb + swz_index<BITS>(R, 8 * (g - G0) + 2 * j + 1));
             bf16x8 a0, a1;
             if constexpr (BITS == 4) {
                 a0 = as_bf16x8(perm_x_for4(x0));
@@ -130,44 +156,49 @@ __device__ __forceinline__ void prefill_unit(const uint16_t *__restrict__ xb, co
     }
 }
 
-// Unit u's activations of this workgroup's rows into registers (rows past m
-// and K past k read as zero), and their store into a staging buffer.
+// The activations of K [kb, kb + SK) of this workgroup's rows into a stage,
+// by direct global-to-LDS loads (wave w issues loads w, w + 4, ...; load i
+// fills bf16 [512 i, 512 i + 512) of the stage, lane l the 8 at 512 i + 8 l).
+// Rows past m read row m - 1 and K past k reads K offset 0: those values
+// reach only rows that are never stored and groups that are never computed.
 template <int BITS>
-__device__ __forceinline__ void prefill_fetch_x(const PrefillArgs &A, int row0, int u,
-                                                u32x4 (&stage)[PCfg<BITS>::CPT]) {
-    using C = Cfg<BITS>;
-    using P = PCfg<BITS>;
+__device__ __forceinline__ void prefill_dma_x(const PrefillArgs &A, int row0, int kb, uint16_t *stage, int w,
+                                              int lane) {
+    using S = SCfg<BITS>;
+    const int rl = lane / S::CH, pos = lane % S::CH;
 #pragma unroll
-    for (int i = 0; i < P::CPT; ++i) {
-        const int q = threadIdx.x + PT * i;
-        const int r = q / (C::KU / 8), ch = q % (C::KU / 8);
-        const int row = row0 + r, kk = C::KU * u + 8 * ch;
-        stage[i] = (row < A.m && kk < A.k) ? *(const u32x4 *)(A.x + (int64_t)row * A.ldx + kk)
-                                           : u32x4{0u, 0u, 0u, 0u};
+    for (int ii = 0; ii < S::NI / (PT / 64); ++ii) {
+        const int i = w + (PT / 64) * ii;
+        const int R = i * S::RPI + rl;
+        const int ch = pos ^ (R & S::SWM);
+        const int row = min(row0 + R, A.m - 1);
+        const int kk = kb + 8 * ch;
+        const uint16_t *src = A.x + (int64_t)row * A.ldx + (kk < A.k ? kk : 0);
+        __builtin_amdgcn_global_load_lds((const void *)src,
+                                         (__attribute__((address_space(3))) void *)(stage + 512 * i), 16, 0, 0);
     }
 }
+// This wave's code slots of unit u.
 template <int BITS>
-__device__ __forceinline__ void prefill_put_x(uint16_t *xb, const u32x4 (&stage)[PCfg<BITS>::CPT]) {
-    using C = Cfg<BITS>;
-    using P = PCfg<BITS>;
-#pragma unroll
-    for (int i = 0; i < P::CPT; ++i) {
-        const int q = threadIdx.x + PT * i;
-        const int r = q / (C::KU / 8), ch = q % (C::KU / 8);
-        *(u32x4 *)(xb + r * P::LDSW + 8 * ch) = stage[i];
-    }
-}
-// This wave's code slots and scale/bias dwords of unit u.
-template <int BITS>
-__device__ __forceinline__ void prefill_fetch_w(const unsigned char *ub0, int u, int lane, int c,
-                                                u32x4 (&wv)[Cfg<BITS>::NS],
-                                                u32x4 (&sbv)[Cfg<BITS>::SBQ > 0 ? Cfg<BITS>::SBQ : 1]) {
+__device__ __forceinline__ void prefill_fetch_codes(const unsigned char *ub0, int u, int lane,
+                                                    u32x4 (&wv)[Cfg<BITS>::NS]) {
     using C = Cfg<BITS>;
     const unsigned char *ub = ub0 + (size_t)u * C::UNIT;
 #pragma unroll
     for (int i = 0; i < C::NS; ++i) wv[i] = *(const u32x4 *)(ub + i * 1024 + 16 * lane);
+}
+// This lane's scale/bias dwords (its column of each of the four tiles) of
+// the groups of stage h of unit u.
+template <int BITS>
+__device__ __forceinline__ void prefill_fetch_sb(const unsigned char *ub0, int u, int h, int c,
+                                                 u32x4 (&sbv)[SCfg<BITS>::NSB]) {
+    using C = Cfg<BITS>;
+    using S = SCfg<BITS>;
+    if constexpr (BITS != 16) {
+        const unsigned char *ub = ub0 + (size_t)u * C::UNIT + C::SBOFF + c * (16 * C::SBQ);
 #pragma unroll
-    for (int q = 0; q < C::SBQ; ++q) sbv[q] = *(const u32x4 *)(ub + C::SBOFF + c * (16 * C::SBQ) + 16 * q);
+        for (int q = 0; q < S::GH; ++q) sbv[q] = *(const u32x4 *)(ub + 16 * (S::GH * h + q));
+    }
 }
 
 // Final values of this wave's 64 x 64 block of y.
@@ -193,11 +224,21 @@ __device__ __forceinline__ void prefill_store(const PrefillArgs &A, int row0, in
         }
 }
 
+// Software pipeline over the stages of K: while a workgroup computes one
+// stage (from LDS, with its unit's code registers and the stage's
+// scale/bias registers), the direct loads of the next stage fill the other
+// LDS buffer, its scale/bias dwords a second register set and, at a unit's
+// first stage, the next unit's codes a second code set; one barrier per
+// stage.  Stages, code sets and scale/bias sets are each two distinct
+// arrays used alternately and the loop handles two units per trip, so no
+// LDS read of a stage can alias the buffer being filled and no register set
+// is ever copied.
 template <int BITS>
 __global__ __launch_bounds__(PT, 2) void prefill_kernel(const PrefillArgs A) {
     using C = Cfg<BITS>;
-    using P = PCfg<BITS>;
-    __shared__ __attribute__((aligned(16))) uint16_t xt[PBM * P::LDSW];
+    using S = SCfg<BITS>;
+    __shared__ __attribute__((aligned(1024))) uint16_t xs0[S::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t xs1[S::STAGE];
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wr = w >> 1, wc = w & 1;
@@ -206,6 +247,7 @@ __global__ __launch_bounds__(PT, 2) void prefill_kernel(const PrefillArgs A) {
     const int b = 2 * blockIdx.y + wc;                     // this wave's 64-column block
     const bool has_block = b < A.nblocks;
     const unsigned char *ub0 = (const unsigned char *)A.tiles + (size_t)b * A.nst * C::UNIT;
+    const int NST = A.nst;
 
     f32x4 y[4][4];
 #pragma unroll
@@ -213,16 +255,53 @@ __global__ __launch_bounds__(PT, 2) void prefill_kernel(const PrefillArgs A) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) y[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int u = 0; u < A.nst; ++u) {
-        u32x4 stage[P::CPT];
-        prefill_fetch_x<BITS>(A, row0, u, stage);
-        u32x4 wv[C::NS];
-        u32x4 sbv[C::SBQ > 0 ? C::SBQ : 1];
-        if (has_block) prefill_fetch_w<BITS>(ub0, u, lane, c, wv, sbv);
-        prefill_put_x<BITS>(xt, stage);
+    u32x4 wa[C::NS], wb[C::NS];                 // code sets: even units, odd units
+    u32x4 s0[S::NSB], s1[S::NSB];               // scale/bias sets: with stage xs0, with xs1
+    prefill_dma_x<BITS>(A, row0, 0, xs0, w, lane);
+    if (has_block) {
+        prefill_fetch_codes<BITS>(ub0, 0, lane, wa);
+        prefill_fetch_sb<BITS>(ub0, 0, 0, c, s0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // Stage h of unit u: computed from (cur, scur) with the unit's codes wcur
+    // while the next stage fills (nxt, snxt) and, at h = 0, unit u + 1's
+    // codes fill wnxt.
+    auto stage = [&](auto hc, int u, const uint16_t *cur, uint16_t *nxt, const u32x4 (&wcur)[C::NS],
+                     u32x4 (&wnxt)[C::NS], const u32x4 (&scur)[S::NSB], u32x4 (&snxt)[S::NSB])
+        __attribute__((always_inline)) {
+        constexpr int h = decltype(hc)::value;
+        const int nu = h + 1 < S::HALVES ? u : u + 1, nh = h + 1 < S::HALVES ? h + 1 : 0;
+        if (nu < NST) {
+            prefill_dma_x<BITS>(A, row0, C::KU * nu + S::SK * nh, nxt, w, lane);
+            if (has_block) {
+                if (h == 0 && u + 1 < NST) prefill_fetch_codes<BITS>(ub0, u + 1, lane, wnxt);
+                prefill_fetch_sb<BITS>(ub0, nu, nh, c, snxt);
+            }
+        }
+        if (has_block)
+            prefill_stage<BITS, h * S::GH, (h + 1) * S::GH>(cur, wcur, scur, min(C::GS, (A.k - C::KU * u) / 64),
+                                                            wr, c, j, y);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (has_block) prefill_unit<BITS>(xt, wv, sbv, min(C::GS, (A.k - C::KU * u) / 64), wr, c, j, y);
-        __syncthreads();
+    };
+    using H0 = std::integral_constant<int, 0>;
+    using H1 = std::integral_constant<int, 1>;
+    for (int u = 0; u < NST; u += 2) {
+        if constexpr (S::HALVES == 1) {
+            // one stage per unit: unit u on xs0, unit u + 1 on xs1
+            stage(H0{}, u, xs0, xs1, wa, wb, s0, s1);
+            if (u + 1 < NST) stage(H0{}, u + 1, xs1, xs0, wb, wa, s1, s0);
+        } else {
+            // two stages per unit: every unit starts on xs0
+            stage(H0{}, u, xs0, xs1, wa, wb, s0, s1);
+            stage(H1{}, u, xs1, xs0, wa, wb, s1, s0);
+            if (u + 1 < NST) {
+                stage(H0{}, u + 1, xs0, xs1, wb, wa, s0, s1);
+                stage(H1{}, u + 1, xs1, xs0, wb, wa, s1, s0);
+            }
+        }
     }
     if (has_block) prefill_store(A, row0, wr, b, c, j, y);
 }

@@ -72,7 +72,7 @@ def test_prefill_deterministic():
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
-@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("bits", [8, 4, 16])
 def test_prefill_full_shape_sampled_rows(bits):
     """Qwen3-4B gate projection (9728 x 2560) over 2048 prompt rows on the
     device; the oracle recomputes 12 sampled rows in full."""
