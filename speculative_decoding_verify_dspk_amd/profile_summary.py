@@ -13,6 +13,11 @@ under profiles/.
     python -m speculative_decoding_verify_dspk_amd.profile_summary curves \\
         <kernel_trace.csv> <curves.json> <out.md> --cmd "<profiled command>"
 
+    # per-launch SQ counters of one kernel (one or more --pmc passes)
+    python -m speculative_decoding_verify_dspk_amd.profile_summary counters <out.md> \\
+        --csv <pass1 counter_collection.csv> --cmd "<pass1>" [--csv ... --cmd ...] \\
+        --kernel prefill_kernel --title "<title>"
+
     # HBM bytes of the head kernel (two --pmc passes: FETCH_SIZE, WRITE_SIZE),
     # scaled by what the same counters read for a plain 256 MiB device copy
     python -m speculative_decoding_verify_dspk_amd.profile_summary traffic \\
@@ -34,7 +39,7 @@ COPY_BYTES = 256 << 20          # the calibration copy that bench.py --calibrate
 
 
 def short(name: str) -> str:
-    for k in ("qgemm_slab_lds_kernel", "qgemm_slab_kernel", "qgemm_kernel"):
+    for k in ("qgemm_slab_lds_kernel", "qgemm_slab_kernel", "qgemm_kernel", "prefill_kernel"):
         if k + "<" in name:
             return k + "<" + name.split(k + "<", 1)[1].split(">", 1)[0] + ">"
     m = re.search(r"accept_\w+", name)
@@ -53,14 +58,14 @@ def stats(stats_csv: str, trace_csv: str, out: str, cmd: str) -> None:
     # per-launch split of the projection kernels by grid (one line per launch shape)
     per = collections.defaultdict(list)
     for r in csv.DictReader(open(trace_csv)):
-        if "qgemm" in r["Kernel_Name"]:
-            per[(short(r["Kernel_Name"]), r["Grid_Size_X"])].append(
+        if "qgemm" in r["Kernel_Name"] or "prefill_kernel" in r["Kernel_Name"]:
+            per[(short(r["Kernel_Name"]), r["Grid_Size_X"], r.get("Grid_Size_Y", "1"))].append(
                 (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    lines += ["", "Projection launches by grid (workgroups x 256 threads):", "",
-              "| kernel | grid threads | launches | median us |", "|---|---|---|---|"]
-    for (k, g), v in sorted(per.items()):
+    lines += ["", "Projection launches by grid (threads in x, workgroups in y; 256 threads per workgroup):", "",
+              "| kernel | grid x | grid y | launches | median us |", "|---|---|---|---|---|"]
+    for (k, gx, gy), v in sorted(per.items()):
         v.sort()
-        lines.append(f"| {k} | {g} | {len(v)} | {v[len(v) // 2]:.1f} |")
+        lines.append(f"| {k} | {gx} | {gy} | {len(v)} | {v[len(v) // 2]:.1f} |")
     open(out, "w").write("\n".join(lines) + "\n")
 
 
@@ -184,6 +189,27 @@ def traffic(fetch_csv: str, write_csv: str, out: str, cmd_fetch: str, cmd_write:
     open(out, "w").write("\n".join(lines) + "\n")
 
 
+def counters(csv_paths: list, out: str, cmds: list, kernel: str, title: str) -> None:
+    """Per-launch means of SQ counters (rocprofv3 --pmc passes) of the
+    launches of `kernel` with the largest grid, one row per counter."""
+    vals = collections.defaultdict(list)
+    for path in csv_paths:
+        rows = [r for r in csv.DictReader(open(path)) if kernel in r["Kernel_Name"]]
+        if not rows:
+            raise SystemExit(f"{path}: no {kernel} launches")
+        big = max(int(r["Grid_Size"]) for r in rows)
+        for r in rows:
+            if int(r["Grid_Size"]) == big:
+                vals[r["Counter_Name"]].append(float(r["Counter_Value"]))
+    lines = [f"# {title}", "", "Commands (one --pmc pass each):", ""] + ["    " + c for c in cmds] + [
+        "", f"Mean per launch of the largest-grid `{kernel}` launches (sums over the device):", "",
+        "| counter | value |", "|---|---|"]
+    for name in sorted(vals):
+        v = vals[name]
+        lines.append(f"| {name} | {sum(v) / len(v):.0f} |")
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -209,8 +235,16 @@ def main() -> None:
     d.add_argument("curves_json")
     d.add_argument("out")
     d.add_argument("--cmd", required=True)
+    e = sub.add_parser("counters")
+    e.add_argument("out")
+    e.add_argument("--csv", action="append", required=True)
+    e.add_argument("--cmd", action="append", required=True)
+    e.add_argument("--kernel", required=True)
+    e.add_argument("--title", required=True)
     args = ap.parse_args()
-    if args.what == "stats":
+    if args.what == "counters":
+        counters(args.csv, args.out, args.cmd, args.kernel, args.title)
+    elif args.what == "stats":
         stats(args.stats_csv, args.trace_csv, args.out, args.cmd)
     elif args.what == "rounds":
         rounds(args.trace_csv, args.out, args.cmd, [int(x) for x in args.sweep.split(",")], args.title)
