@@ -115,6 +115,22 @@ def host_cpu() -> dict:
     return {"cpu_model": model, "blas": blas}
 
 
+def device_info() -> dict:
+    """What the numbers were measured on: the device's name, architecture,
+    compute units, clock and memory, the HIP runtime torch was built with,
+    and the library's version."""
+    import torch
+    from speculative_decoding_verify_dspk_amd import binding
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2 ** 30, 1), "hip": torch.version.hip,
+            "torch": torch.__version__, "dspk_version": binding.version()}
+    clock = getattr(p, "clock_rate", None)
+    if clock:
+        info["clock_mhz"] = round(clock / 1000)
+    return info
+
+
 def cpu_baseline(model: str, bits: int, m: int, budget_s: float):
     """The oracle, as it stands, on one verify round of the same workload:
     every projection of one layer at width m, then as many 8192-entry slices
@@ -275,7 +291,7 @@ def prefill_bench(args):
                      "kernel": f"prefill_kernel<{args.bits}> (gate projection {F}x{H})",
                      "avg_launch_us": round(gate_us, 2), "flops_per_launch": gate_flops},
         "cpu_baseline": None if args.no_cpu_baseline else prefill_cpu_baseline(args.config, args.bits, P),
-        "device": torch.cuda.get_device_name(0), "host": platform.node(),
+        "device": torch.cuda.get_device_name(0), "device_info": device_info(), "host": platform.node(),
     }
     print(json.dumps(out))
 
@@ -848,7 +864,7 @@ def run_workload(args) -> dict:
         "roofline": roofline,
         "dense27b": dense,
         "cpu_baseline": cpu,
-        "device": torch.cuda.get_device_name(0), "host": platform.node(),
+        "device": torch.cuda.get_device_name(0), "device_info": device_info(), "host": platform.node(),
     }
     del stack
     return out
