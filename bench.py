@@ -277,6 +277,7 @@ def prefill_bench(args):
     gate_flops = 2 * P * F * H
     achieved = gate_flops / (gate_us * 1e-6) / 1e12
     value = flops * args.steps / wall / 1e12
+    lib_tfs = library_bf16_gemm_tflops(P, F, H)
     out = {
         "metric": "prefill projection throughput (TFLOP/s) over a prompt",
         "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -290,10 +291,33 @@ def prefill_bench(args):
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
                      "kernel": f"prefill_kernel<{args.bits}> (gate projection {F}x{H})",
                      "avg_launch_us": round(gate_us, 2), "flops_per_launch": gate_flops},
+        # context: the box's own library GEMM (torch.matmul, bf16 in and out)
+        # on the gate shape; the quantised kernel's share of it is the
+        # figure comparable with a wide-GEMM's fraction of a bf16 GEMM
+        "library_bf16_gemm": {"tflops": round(lib_tfs, 1), "shape": f"{P}x{H} @ {H}x{F}",
+                              "gate_fraction": round(achieved / lib_tfs, 3)},
         "cpu_baseline": None if args.no_cpu_baseline else prefill_cpu_baseline(args.config, args.bits, P),
         "device": torch.cuda.get_device_name(0), "device_info": device_info(), "host": platform.node(),
     }
     print(json.dumps(out))
+
+
+def library_bf16_gemm_tflops(p: int, n: int, k: int, reps: int = 20) -> float:
+    """TFLOP/s of torch.matmul (the ROCm BLAS library) on a plain bf16
+    [p, k] x [k, n] product, both operands contiguous, timed with events."""
+    import torch
+    a = torch.randn(p, k, device="cuda").to(torch.bfloat16)
+    b = torch.randn(k, n, device="cuda").to(torch.bfloat16).contiguous()
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2.0 * p * n * k * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
 
 
 def prefill_cpu_baseline(model: str, bits: int, rows: int, budget_s: float = 15.0):
