@@ -34,14 +34,26 @@ __device__ __forceinline__ bf16x8 codes8_to_bf16(uint32_t w0, uint32_t w1) {
     return as_bf16x8(r);
 }
 
+// The constant 0x43004300 (two bf16 128.0) in a vector register, opaque to
+// the compiler.  A gfx9 VOP3 instruction reads at most one scalar or literal
+// operand, so with the mask and this constant both literal the compiler
+// splits (x & mask) | c into an and and an or; with c in a vector register
+// it forms one v_and_or_b32.  Only ordinary VALU instructions read the
+// result.
+__device__ __forceinline__ uint32_t bf16_128_pair() {
+    uint32_t r;
+    asm("v_mov_b32 %0, 0x43004300" : "=v"(r));
+    return r;
+}
 // eight 4-bit codes (one dword) -> bf16 values 128 + q in the order
 // q0,q4,q1,q5,q2,q6,q3,q7 (0x4300 is bf16 128.0; q fills the low mantissa bits)
 __device__ __forceinline__ bf16x8 codes4_to_bf16(uint32_t w) {
+    const uint32_t c = bf16_128_pair();
     u32x4 r;
-    r[0] = (w & 0x000F000Fu) | 0x43004300u;
-    r[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-    r[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-    r[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+    r[0] = (w & 0x000F000Fu) | c;
+    r[1] = ((w >> 4) & 0x000F000Fu) | c;
+    r[2] = ((w >> 8) & 0x000F000Fu) | c;
+    r[3] = ((w >> 12) & 0x000F000Fu) | c;
     return as_bf16x8(r);
 }
 
@@ -49,10 +61,11 @@ __device__ __forceinline__ bf16x8 codes4_to_bf16(uint32_t w) {
 // 128 + q in the order q0,q8,q1,q9,q2,q10,q3,q11 | q4,q12,...,q7,q15
 __device__ __forceinline__ void codes2_to_bf16(uint32_t w, bf16x8 &b0, bf16x8 &b1) {
     u32x4 r0, r1;
+    const uint32_t c = bf16_128_pair();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        r0[i] = ((w >> (2 * i)) & 0x00030003u) | 0x43004300u;
-        r1[i] = ((w >> (2 * i + 8)) & 0x00030003u) | 0x43004300u;
+        r0[i] = ((w >> (2 * i)) & 0x00030003u) | c;
+        r1[i] = ((w >> (2 * i + 8)) & 0x00030003u) | c;
     }
     b0 = as_bf16x8(r0);
     b1 = as_bf16x8(r1);
