@@ -47,14 +47,17 @@ hipError_t launch_pack(int32_t n, int32_t k, int bits, const void *codes, const 
 //    without scratch: 9B-shaped 4-bit layer 103 -> 83 us, head 88 -> 80 us.
 //  * 17..32 rows (twice the activation and accumulator registers): no ring,
 //    two workgroups per CU for projections (27B-shaped layer 138 -> 120 us
-//    against a 2-deep ring at one per CU); the head, whose workgroups stream
-//    many units each, no ring at three per CU (27B-shaped head 197 -> 162
-//    us); 2/3/4-bit heads keep a 2-deep ring at one per CU.
+//    against a 2-deep ring at one per CU) and for the 8-bit head (170
+//    VGPRs; against three per CU, 27B-shaped head at 17 / 24 / 32 rows
+//    173-178 / 188-190 / 201 -> 170-171 / 178-180 / 186-187 us, Qwen3-8B-
+//    shaped 139-141 / 149-150 / 161 -> 139-141 / 143-144 / 149 us; a
+//    2-deep ring there spills 388 B/lane); the bf16 head no ring at three
+//    per CU; 2/3/4-bit heads keep a 2-deep ring at one per CU.
 constexpr int kernel_depth(int bits, int mt, bool argmax) {
     return mt == 1 ? (bits <= 4 || (bits == 8 && !argmax) ? 1 : 2) : (argmax && bits <= 4 ? 2 : 1);
 }
 constexpr int kernel_occ(int bits, int mt, bool argmax) {
-    return mt == 1 ? (bits <= 4 ? 3 : 2) : (!argmax ? 2 : bits >= 8 ? 3 : 1);
+    return mt == 1 ? (bits <= 4 ? 3 : 2) : (!argmax || bits == 8 ? 2 : bits > 8 ? 3 : 1);
 }
 
 // Work of a projection launch is a list of quads: (weight, 64-column block,
