@@ -422,14 +422,6 @@ __device__ inline void trunc_entry_raw(const SampleArgs &A, const RowCtx &R, int
     mfx = (y > 0.f && u == 0ull) ? 1ull : (y > 0.f ? u : 0ull);
 }
 
-__device__ inline void trunc_entry(const SampleArgs &A, const RowCtx &R, int dist, int j, int col,
-                                   const int32_t *s_d, const uint32_t *bloom, unsigned long long &key,
-                                   uint32_t &fi, unsigned long long &mfx) {
-    const float raw = dist == 0 ? A.z[(int64_t)j * A.ldz + col] : A.q[(int64_t)j * A.ldq + col];
-    const int hist = dist == 0 && A.pen && A.counts != nullptr ? A.counts[col] : 0;
-    trunc_entry_raw(A, R, dist, j, col, raw, hist, s_d, bloom, key, fi, mfx);
-}
-
 // Add (1, mfx) to bin b of (cnt, mass) for the lanes with take set.  When
 // every taking lane of the wave has the same bin (crowded bins: equal or
 // nearly equal values, runs of columns), one lane adds the wave's sums: LDS
@@ -562,7 +554,7 @@ __global__ __launch_bounds__(FT) void sample_trunc_kernel(const SampleArgs A) {
     __shared__ int32_t s_d[kMaxRows];
     __shared__ uint32_t s_bloom[32];
     __shared__ float2 s_rs;
-    __shared__ int s_bin, s_n, s_idx;
+    __shared__ int s_bin, s_n;
     __shared__ unsigned long long s_acnt, s_amass;
     __shared__ Found s_found;
     const int j = blockIdx.x, dist = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -575,14 +567,20 @@ __global__ __launch_bounds__(FT) void sample_trunc_kernel(const SampleArgs A) {
     const uint16_t *bins = W.bin1 + (size_t)(j * 2 + dist) * W.vpad;
     const size_t slot0 = (size_t)(j * 2 + dist) * W.nslices * NB;
 
-    auto entry = [&](int col, unsigned long long &key, uint32_t &fi, unsigned long long &mfx)
-        __attribute__((always_inline)) { trunc_entry(A, R, dist, j, col, s_d, s_bloom, key, fi, mfx); };
+    // An entry's key, fine index and weight from its value (and count).
+    auto entry = [&](int col, float raw, int hist, unsigned long long &key, uint32_t &fi, unsigned long long &mfx)
+        __attribute__((always_inline)) { trunc_entry_raw(A, R, dist, j, col, raw, hist, s_d, s_bloom, key, fi, mfx); };
+    const float *vrow = dist == 0 ? A.z + (int64_t)j * A.ldz : A.q + (int64_t)j * A.ldq;
+    const bool with_hist = dist == 0 && A.pen && A.counts != nullptr;
 
-    // Calls visit(match, col) until every entry of first-level bin b1 has
-    // been visited once with match set (col < v); the calls are
-    // wave-uniform, so visit may use wave-wide operations.  The stored bins
-    // are read 16 bytes (8 entries) at a time, 4 loads in flight per thread;
-    // each thread then visits the matches of its 32 entries, lowest first.
+    // Calls visit(match, col, raw, hist) until every entry of first-level bin
+    // b1 has been visited once with match set (col < v; raw its value, hist
+    // its count); the calls are wave-uniform, so visit may use wave-wide
+    // operations.  The stored bins are read 16 bytes (8 entries) at a time,
+    // 4 loads in flight per thread; each thread then takes the matches of its
+    // 32 entries VB at a time, lowest first, with the values of all VB
+    // loaded together (a crowded bin gives a thread many matches, and one
+    // dependent load per visit made them a chain of round trips).
     auto scan_bin = [&](int b1, auto &&visit) __attribute__((always_inline)) {
         const uint4 *bv = reinterpret_cast<const uint4 *>(bins);
         const int ng = (A.v + 7) >> 3;
@@ -605,16 +603,27 @@ __global__ __launch_bounds__(FT) void sample_trunc_kernel(const SampleArgs A) {
                     if (col < A.v && bb == (uint32_t)b1) mask |= 1u << (i * 8 + e);
                 }
             }
+            constexpr int VB = 8;
             for (;;) {
-                const bool has = mask != 0u;
-                if (__ballot(has) == 0ull) break;
-                int col = 0;
-                if (has) {
-                    const int e = __ffs(mask) - 1;
+                if (__ballot(mask != 0u) == 0ull) break;
+                bool has[VB];
+                int cols[VB];
+#pragma unroll
+                for (int t = 0; t < VB; ++t) {
+                    has[t] = mask != 0u;
+                    const int e = has[t] ? __ffs(mask) - 1 : 0;
                     mask &= mask - 1u;
-                    col = (g0 + FT * (e >> 3) + tid) * 8 + (e & 7);
+                    cols[t] = has[t] ? (g0 + FT * (e >> 3) + tid) * 8 + (e & 7) : 0;   // column 0: a valid address
                 }
-                visit(has, col);
+                float raw[VB];
+                int hist[VB];
+#pragma unroll
+                for (int t = 0; t < VB; ++t) {
+                    raw[t] = vrow[cols[t]];
+                    hist[t] = with_hist ? A.counts[cols[t]] : 0;
+                }
+#pragma unroll
+                for (int t = 0; t < VB; ++t) visit(has[t], cols[t], raw[t], hist[t]);
             }
         }
     };
@@ -700,20 +709,22 @@ __global__ __launch_bounds__(FT) void sample_trunc_kernel(const SampleArgs A) {
     };
 
     // Gather the entries of first-level bin b1 with key >= lo and fi in
-    // [f0, f1] into LDS (at most CAP of them), sort them by key
-    // (descending), and find the first at which base + running weight
-    // reaches target; result in s_found.
-    auto gather_sort_find = [&](int b1, unsigned long long lo, uint32_t f0, uint32_t f1, bool by_mass,
+    // [f0, f1] into LDS (at most CAP of them) and find the first, in
+    // descending key order, at which base + running weight reaches target;
+    // result in s_found.  base is below target (the sums before the bin that
+    // find_bin chose), so the selection below never settles on an empty
+    // digit.
+    auto gather_select_find = [&](int b1, unsigned long long lo, uint32_t f0, uint32_t f1, bool by_mass,
                                 unsigned long long target, unsigned long long base_cnt,
                                 unsigned long long base_mass) __attribute__((always_inline)) {
         if (tid == 0) s_n = 0;
         __syncthreads();
-        scan_bin(b1, [&](bool match, int col) __attribute__((always_inline)) {
+        scan_bin(b1, [&](bool match, int col, float raw, int hist) __attribute__((always_inline)) {
             bool take = false;
             unsigned long long key = 0, mfx = 0;
             if (match) {
                 uint32_t fi;
-                entry(col, key, fi, mfx);
+                entry(col, raw, hist, key, fi, mfx);
                 take = key >= lo && fi >= f0 && fi <= f1;
             }
             const unsigned long long bal = __ballot(take);
@@ -731,74 +742,117 @@ __global__ __launch_bounds__(FT) void sample_trunc_kernel(const SampleArgs A) {
         });
         __syncthreads();
         const int n = min(s_n, CAP);
-        int np = 1;
-        while (np < n) np <<= 1;
-        for (int i = n + tid; i < np; i += FT) {
-            c_key[i] = 0ull;      // below every real key
-            c_mass[i] = 0ull;
-        }
-        __syncthreads();
-        // bitonic sort, descending
-        for (int k = 2; k <= np; k <<= 1) {
-            for (int jj = k >> 1; jj > 0; jj >>= 1) {
-                for (int i = tid; i < np; i += FT) {
-                    const int ixj = i ^ jj;
-                    if (ixj > i) {
-                        const unsigned long long a = c_key[i], b = c_key[ixj];
-                        const bool desc = (i & k) == 0;
-                        if (desc ? (a < b) : (a > b)) {
-                            c_key[i] = b;
-                            c_key[ixj] = a;
-                            const unsigned long long t = c_mass[i];
-                            c_mass[i] = c_mass[ixj];
-                            c_mass[ixj] = t;
+        // The bound among the gathered entries, without sorting them: a
+        // radix selection over the 64-bit keys, one 8-bit digit per pass from
+        // the top.  Each pass histograms (count, mass) by digit the entries
+        // that share the digits chosen so far and takes the largest digit at
+        // which base + the weight of every larger key reaches target; the
+        // digits above it join the base.  After eight passes the digits are
+        // the bound's key (keys are unique) and the base counts every larger
+        // key.  (A bitonic sort of up to 4096 entries by one workgroup was
+        // most of the selection's time.)
+        static_assert(CAP == 4 * FT, "four gathered entries per thread");
+        if (n <= 64) {
+            // few entries (the usual case): wave 0 sorts them across its
+            // lanes with shuffles (bitonic, descending, no barriers) and
+            // scans the running weight
+            if (wv == 0) {
+                unsigned long long k1 = lane < n ? c_key[lane] : 0ull, m1 = lane < n ? c_mass[lane] : 0ull;
+                for (int k = 2; k <= 64; k <<= 1)
+                    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+                        const unsigned long long pk = __shfl_xor(k1, jj), pm = __shfl_xor(m1, jj);
+                        const bool keep_max = ((lane & k) == 0) == ((lane & jj) == 0);
+                        if (keep_max ? pk > k1 : pk < k1) {
+                            k1 = pk;
+                            m1 = pm;
                         }
                     }
-                }
-                __syncthreads();
-            }
-        }
-        // running weight: thread t owns entries [t*PT, t*PT + PT)
-        constexpr int PT = CAP / FT;
-        unsigned long long lc = 0, lm = 0;
-        for (int i = 0; i < PT; ++i) {
-            const int e = tid * PT + i;
-            if (e < n) {
-                lc += 1;
-                lm += c_mass[e];
-            }
-        }
-        const unsigned long long ic = wave_incl_scan(lc, lane), im = wave_incl_scan(lm, lane);
-        if (lane == 63) {
-            s_wsum[wv][0] = ic;
-            s_wsum[wv][1] = im;
-        }
-        if (tid == 0) s_idx = 0x7fffffff;
-        __syncthreads();
-        unsigned long long pc = base_cnt + ic - lc, pm = base_mass + im - lm;
-        for (int w = 0; w < wv; ++w) {
-            pc += s_wsum[w][0];
-            pm += s_wsum[w][1];
-        }
-        int hit = 0x7fffffff;
-        for (int i = 0; i < PT; ++i) {
-            const int e = tid * PT + i;
-            if (e < n) {
-                pc += 1;
-                pm += c_mass[e];
-                if ((by_mass ? pm : pc) >= target) {
-                    hit = e;
-                    break;
+                const unsigned long long ic = wave_incl_scan(lane < n ? 1ull : 0ull, lane) + base_cnt;
+                const unsigned long long im = wave_incl_scan(lane < n ? m1 : 0ull, lane) + base_mass;
+                const unsigned long long hit = __ballot(lane < n && (by_mass ? im : ic) >= target);
+                if (hit != 0ull && lane == __ffsll((long long)hit) - 1) {
+                    s_found.key = k1;
+                    s_found.cnt = ic;
+                    s_found.mass = im;
+                    s_found.ok = 1;
                 }
             }
+            __syncthreads();
+            return;
         }
-        if (hit != 0x7fffffff) atomicMin(&s_idx, hit);
-        __syncthreads();
-        if (hit != 0x7fffffff && hit == s_idx) {
-            s_found.key = c_key[hit];
-            s_found.cnt = pc;
-            s_found.mass = pm;
-            s_found.ok = 1;
+        unsigned long long kv[4], mv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int e = 4 * tid + r;
+            kv[r] = e < n ? c_key[e] : 0ull;
+            mv[r] = e < n ? c_mass[e] : 0ull;
+        }
+        unsigned long long prefix = 0, acnt = base_cnt, amass = base_mass;
+        bool found = true;
+        for (int shift = 56; shift >= 0; shift -= 8) {
+            __syncthreads();            // the previous pass's histogram has been read
+            for (int b = tid; b < 256; b += FT) {
+                h_cnt[b] = 0u;
+                h_mass[b] = 0ull;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int e = 4 * tid + r;
+                const bool take = e < n && (shift == 56 || (kv[r] >> (shift + 8)) == (prefix >> (shift + 8)));
+                hist_add(h_cnt, h_mass, take, (int)((kv[r] >> shift) & 255u), mv[r]);
+            }
+            __syncthreads();
+            if (wv == 0) {
+                // digits in descending order, four per lane
+                unsigned long long lc = 0, lm = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int b = 255 - (4 * lane + i);
+                    lc += h_cnt[b];
+                    lm += h_mass[b];
+                }
+                const unsigned long long ic = wave_incl_scan(lc, lane), im = wave_incl_scan(lm, lane);
+                const unsigned long long reach = by_mass ? amass + im : acnt + ic;
+                const unsigned long long mask = __ballot(reach >= target);
+                if (lane == 0) s_bin = -1;
+                if (mask != 0ull && lane == __ffsll((long long)mask) - 1) {
+                    unsigned long long c = acnt + ic - lc, m = amass + im - lm;
+                    int bin = -1;
+                    for (int i = 0; i < 4; ++i) {
+                        const int b = 255 - (4 * lane + i);
+                        const unsigned long long nc = c + h_cnt[b], nm = m + h_mass[b];
+                        if ((by_mass ? nm : nc) >= target) {
+                            bin = b;
+                            break;
+                        }
+                        c = nc;
+                        m = nm;
+                    }
+                    s_bin = bin;
+                    s_acnt = c;
+                    s_amass = m;
+                }
+            }
+            __syncthreads();
+            if (s_bin < 0) {            // not reached (only possible in the first pass)
+                found = false;
+                break;
+            }
+            prefix |= (unsigned long long)s_bin << shift;
+            acnt = s_acnt;
+            amass = s_amass;
+        }
+        if (found) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (4 * tid + r < n && kv[r] == prefix) {
+                    s_found.key = prefix;
+                    s_found.cnt = acnt + 1;
+                    s_found.mass = amass + mv[r];
+                    s_found.ok = 1;
+                }
+            }
         }
         __syncthreads();
     };
@@ -814,12 +868,12 @@ __global__ __launch_bounds__(FT) void sample_trunc_kernel(const SampleArgs A) {
             const int width = pass < 5 ? 11 : 9;
             const int top = shift + width;
             clear_hist();
-            scan_bin(b1, [&](bool match, int col) __attribute__((always_inline)) {
+            scan_bin(b1, [&](bool match, int col, float raw, int hist) __attribute__((always_inline)) {
                 unsigned long long key = 0, mfx = 0;
                 bool take = false;
                 if (match) {
                     uint32_t fi;
-                    entry(col, key, fi, mfx);
+                    entry(col, raw, hist, key, fi, mfx);
                     take = key >= lo && fi == f && (top >= 64 || (key >> top) == (prefix >> top));
                 }
                 hist_add(h_cnt, h_mass, take, (int)((key >> shift) & ((1u << width) - 1u)), mfx);
@@ -832,11 +886,11 @@ __global__ __launch_bounds__(FT) void sample_trunc_kernel(const SampleArgs A) {
         }
         // acnt / amass count the keys above 'prefix'; add the entry itself
         // (one entry has this key)
-        scan_bin(b1, [&](bool match, int col) __attribute__((always_inline)) {
+        scan_bin(b1, [&](bool match, int col, float raw, int hist) __attribute__((always_inline)) {
             if (match) {
                 unsigned long long key, mfx;
                 uint32_t fi;
-                entry(col, key, fi, mfx);
+                entry(col, raw, hist, key, fi, mfx);
                 if (key == prefix) {
                     s_found.key = prefix;
                     s_found.cnt = acnt + 1;
@@ -875,16 +929,16 @@ __global__ __launch_bounds__(FT) void sample_trunc_kernel(const SampleArgs A) {
             return;
         }
         if (h_cnt[b1] <= (uint32_t)CAP) {
-            gather_sort_find(b1, lo, (uint32_t)b1 << 11, ((uint32_t)b1 << 11) | 2047u, by_mass, target, acnt, amass);
+            gather_select_find(b1, lo, (uint32_t)b1 << 11, ((uint32_t)b1 << 11) | 2047u, by_mass, target, acnt, amass);
             return;
         }
         clear_hist();
-        scan_bin(b1, [&](bool match, int col) __attribute__((always_inline)) {
+        scan_bin(b1, [&](bool match, int col, float raw, int hist) __attribute__((always_inline)) {
             unsigned long long key = 0, mfx = 0;
             uint32_t fi = 0;
             bool take = false;
             if (match) {
-                entry(col, key, fi, mfx);
+                entry(col, raw, hist, key, fi, mfx);
                 take = key >= lo;
             }
             hist_add(h_cnt, h_mass, take, (int)(fi & 2047u), mfx);
@@ -902,7 +956,7 @@ __global__ __launch_bounds__(FT) void sample_trunc_kernel(const SampleArgs A) {
             return;
         }
         if (h_cnt[b2] <= (uint32_t)CAP) {
-            gather_sort_find(b1, lo, f, f, by_mass, target, acnt, amass);
+            gather_select_find(b1, lo, f, f, by_mass, target, acnt, amass);
             return;
         }
         radix_find(b1, lo, f, by_mass, target, acnt, amass);

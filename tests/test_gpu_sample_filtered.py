@@ -310,13 +310,18 @@ def test_sample_ex_distribution_chi2():
     assert chi.pvalue > 1e-3, chi
 
 
-@pytest.mark.parametrize("case", ["tied_block", "near_equal", "wide_spread", "zero_block", "uniform_q"])
+@pytest.mark.parametrize("case", ["tied_block", "near_equal", "wide_spread", "zero_block", "uniform_q",
+                                  "flat_nucleus", "flat_topk"])
 def test_crowded_bins(case):
     """Bounds inside crowds of equal or nearly equal values: more entries
-    share one value bin than the truncation sorts at once, so its finer
+    share one value bin than the truncation gathers at once, so its finer
     histogram, its exact radix selection over the order keys, or (a top-k
     bound among weights of exactly zero) keeping the whole zero block
-    decides.  wide_spread: logits of std 68 (most of p and q underflow)."""
+    decides.  wide_spread: logits of std 68 (most of p and q underflow).
+    flat_nucleus / flat_topk: logits of std 3, where the top-p 0.95 bound
+    (resp. the 3000th entry) falls in a value bin of hundreds to thousands
+    of entries: the gathered bin is selected from by digits rather than by
+    the single-wave sort of small bins."""
     g = np.random.default_rng(sum(map(ord, case)))
     v, m_rows = (20000, 4) if case == "tied_block" else (151936, 3)
     n_exempt = 0
@@ -332,6 +337,12 @@ def test_crowded_bins(case):
         elif case == "wide_spread":
             z = g.normal(0, 68, size=(m_rows, v)).astype(np.float32)
             top_k, top_p, noise = 50, 0.9, 30.0
+        elif case == "flat_nucleus":
+            z = g.normal(0, 3, size=(m_rows, v)).astype(np.float32)
+            top_k, top_p = 0, 0.95
+        elif case == "flat_topk":
+            z = g.normal(0, 3, size=(m_rows, v)).astype(np.float32)
+            top_k, top_p = 3000, 1.0
         else:
             z = g.normal(0, 2, size=(m_rows, v)).astype(np.float32)
             top_k, top_p = 100, 1.0
@@ -343,11 +354,14 @@ def test_crowded_bins(case):
             q /= q.sum(axis=1, keepdims=True)
         if case == "uniform_q":
             q[:] = np.float32(1.0 / v)
-        # drafts near the top-k boundary of their row (both sides of it)
+        # drafts near the truncation boundary of their row (both sides of it)
         d = np.empty(m_rows - 1, np.int32)
         for j in range(m_rows - 1):
             order = np.lexsort((np.arange(v), -z[j].astype(np.float64)))
-            d[j] = order[top_k - 20 + int(g.integers(0, 40))]
+            kept = top_k
+            if case == "flat_nucleus":
+                kept = int(oracle.truncate(_softmax(z[j].astype(np.float64), 1.0), top_k, top_p).sum())
+            d[j] = order[kept - 20 + int(g.integers(0, 40))]
         if case in ("zero_block", "uniform_q", "wide_spread"):
             # drafts as drawn from the truncated q
             for j in range(m_rows - 1):
