@@ -165,13 +165,17 @@ constexpr int kDotMaxRows = 4;
 //   Qwen3-4B gate/up (1216, k 2560)  16.1 / 17.7 / 19.1 vs 18.0 / 18.7 / 20.0
 //   27B down    (320 tiles, k 17408) 26.2 / 34.6 / 43.2 vs 22.6 / 22.9 / 23.9
 //   9B gate/up  (1536 tiles, k 4096) 25.2 / 28.8 / 32.9 vs 24.6 / 24.6 / 25.7
+//     (4-wave workgroups in two rounds; as eight resident 2-wave workgroups
+//     per CU, HIP events at 1 / 4 / 8 rows: 24.2-24.7 / 25.4-25.6 / 26.7-26.8
+//     vs 26.9 / 27.5 / 26.9 us, bf16 34.3-34.8 vs 40.2-40.5 us, hence the
+//     400 KiB limit, which that launch's 384 KiB per CU fits)
 // and at 9 / 12 / 16 rows:
 //   27B q/k/v   (448 tiles, k 5120)  13.7 / 14.9 / 16.1 vs 16.7 / 16.8 / 17.1
 //   27B o       (320 tiles, k 5120)  12.7 / 13.6 / 15.4 vs 13.2 / 13.0 / 13.0
 //   Qwen3-4B down (160, k 9728)      12.1 / 13.0 / 14.4 vs 13.2 / 13.4 / 13.5
 //   9B down     (256 tiles, k 12288) 16.4 / 17.5 / 18.6 vs 15.7 / 15.1 / 15.7
 constexpr int kSlabLdsMaxRows = 16;
-constexpr int64_t kSlabAutoWeightsNarrow = 320 * 1024;
+constexpr int64_t kSlabAutoWeightsNarrow = 400 * 1024;
 constexpr int64_t kSlabAutoWeightsWide = 200 * 1024;
 constexpr int32_t kSlabAutoMaxKWide = 5120;
 int projection_variant();               // the process-wide setting (DSPK_VARIANT, or the setter)

@@ -18,11 +18,12 @@
 // plus the tile's scale/bias dwords), and the W partial tiles are added in
 // LDS in wave order.  No workspace, no cross-workgroup traffic, results
 // deterministic (the order of every sum is fixed by the shapes).  The launch
-// has one workgroup per tile; the host picks W (16, 8, 4 or 3 waves) so that
-// all of them are resident at once where they fit (one, two, four or five
-// workgroups per CU for up to 1, 2, 4 or 5 tiles per CU); with more tiles
-// than that it takes 4 waves and the rest run as a second round, which its
-// automatic choice only accepts while the weights per CU stay small.
+// has one workgroup per tile; the host picks W (16, 8, 4, 3 or 2 waves) so
+// that all of them are resident at once where they fit (one, two, four, five
+// or eight workgroups per CU for up to 1, 2, 4, 5 or 8 tiles per CU); with
+// more tiles than that it takes 4 waves and the rest run as a second round,
+// which its automatic choice only accepts while the weights per CU stay
+// small.
 //
 // The arithmetic per group is that of the stream-K kernel: exact-product bf16
 // MFMAs on the codes (8-bit codes, or 128 + q below 8 bits) and on a ones
@@ -513,6 +514,7 @@ hipError_t launch_w(const GemmLaunch &L, int waves, hipStream_t s) {
         case 8: hipLaunchKernelGGL((qgemm_slab_kernel<BITS, MT, 8>), grid, dim3(512), 0, s, L); break;
         case 4: hipLaunchKernelGGL((qgemm_slab_kernel<BITS, MT, 4>), grid, dim3(256), 0, s, L); break;
         case 3: hipLaunchKernelGGL((qgemm_slab_kernel<BITS, MT, 3>), grid, dim3(192), 0, s, L); break;
+        case 2: hipLaunchKernelGGL((qgemm_slab_kernel<BITS, MT, 2>), grid, dim3(128), 0, s, L); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -526,6 +528,7 @@ hipError_t launch_lds_w(const GemmLaunch &L, int waves, hipStream_t s) {
         case 8: hipLaunchKernelGGL((qgemm_slab_lds_kernel<BITS, 8, MR>), grid, dim3(512), 0, s, L); break;
         case 4: hipLaunchKernelGGL((qgemm_slab_lds_kernel<BITS, 4, MR>), grid, dim3(256), 0, s, L); break;
         case 3: hipLaunchKernelGGL((qgemm_slab_lds_kernel<BITS, 3, MR>), grid, dim3(192), 0, s, L); break;
+        case 2: hipLaunchKernelGGL((qgemm_slab_lds_kernel<BITS, 2, MR>), grid, dim3(128), 0, s, L); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

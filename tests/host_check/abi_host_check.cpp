@@ -86,7 +86,7 @@ hipError_t launch_lmhead(const GemmLaunch &L, int bits, int grid, hipStream_t) {
 }
 hipError_t launch_qgemm_slab(const GemmLaunch &L, int bits, int waves, hipStream_t) {
     ++g_launches;
-    CHECK(waves == 3 || waves == 4 || waves == 8 || waves == 16);
+    CHECK(waves == 2 || waves == 3 || waves == 4 || waves == 8 || waves == 16);
     CHECK(L.m >= 1 && L.m <= kMaxRows && L.count >= 1 && L.count <= kMaxGrouped);
     CHECK(L.nst == (L.k + tile_k(bits) - 1) / tile_k(bits));
     // with the automatic choice every tile of the call is resident at once
@@ -99,7 +99,7 @@ hipError_t launch_qgemm_slab(const GemmLaunch &L, int bits, int waves, hipStream
 }
 hipError_t launch_qgemm_dot(const GemmLaunch &L, int waves, hipStream_t) {
     ++g_launches;
-    CHECK(waves == 3 || waves == 4 || waves == 8 || waves == 16);
+    CHECK(waves == 2 || waves == 3 || waves == 4 || waves == 8 || waves == 16);
     CHECK(L.m >= 1 && L.m <= kDotMaxRows);
     return hipSuccess;
 }

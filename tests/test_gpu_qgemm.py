@@ -245,6 +245,24 @@ def test_qgemm_both_decompositions_match_oracle(variant, which, bits, n, k, m):
     print(f"  worst row normwise error {worst:.2e}")
 
 
+@pytest.mark.parametrize("bits", [8, 16, 4])
+@pytest.mark.parametrize("n,k", [(19456, 2560), (24576, 1024)])
+@pytest.mark.parametrize("m", [1, 5])
+def test_slab_resident_wave_counts(variant, bits, n, k, m):
+    """Forced slab launches of 4.75 and 6 tiles per CU on a 256-CU device (the
+    Qwen3-4B- and 9B-shaped gate/up widths), which run as five 3-wave and
+    eight 2-wave workgroups per CU; the oracle computes sampled columns."""
+    variant(binding.VARIANT_SLAB)
+    print(f"slab bits={bits} n={n} k={k} m={m}", flush=True)
+    g = np.random.default_rng(n + k + m + bits)
+    w = inputs.make_qweight(n, k, bits, "slab-waves", n, k)
+    x = inputs.make_activations(m, k, "slab-waves", n, k, m)
+    got = run_qgemm(w, x, m)
+    cols = np.unique(np.concatenate([[0, 15, 16, 63, 64, n - 1], g.choice(n, 186, replace=False)]))
+    ref = oracle_columns(w, x, cols)
+    assert_rows_close(got[:, cols], ref, what=f"slab bits={bits} n={n} k={k} m={m} (sampled columns)")
+
+
 def test_slab_grouped_and_deterministic(variant):
     """The slab kernel on a grouped q/k/v call (the automatic choice at this
     size): deterministic, and each weight agrees with the oracle."""
