@@ -284,6 +284,17 @@ int dspk_qgemm_verify_grouped_noalloc(int32_t count, const dspk_tiled_weight *w,
 int dspk_qgemm_prefill(const dspk_tiled_weight *w, const uint16_t *x, int64_t ldx, int32_t m,
                        void *y, int32_t y_dtype, int64_t ldy, void *stream);
 
+/*
+ * Row block of dspk_qgemm_prefill: 0 (initial) chooses per call between
+ * 128-row and 64-row output blocks from the rows, the columns and the
+ * device's CU count (64 where 128-row blocks would leave CUs idle or unevenly
+ * loaded); 64 or 128 forces one.  Both blocks produce bit-identical results;
+ * this setting is for measurement and tests.  Returns the previous setting,
+ * or DSPK_EINVAL for another value.  Not synchronised with calls in flight
+ * on other threads.
+ */
+int dspk_set_prefill_block_rows(int32_t rows);
+
 /* Workspace for dspk_lmhead_argmax (and the fused greedy head) over a
  * vocabulary of v entries: any hidden size, width 1..DSPK_MAX_ROWS and
  * format; the same contract as dspk_qgemm_workspace_bytes, and one buffer may

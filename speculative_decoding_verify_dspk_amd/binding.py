@@ -84,6 +84,7 @@ def lib() -> ctypes.CDLL:
     sig = {
         "dspk_version": (c_int32, []),
         "dspk_set_projection_variant": (c_int32, [c_int32]),
+        "dspk_set_prefill_block_rows": (c_int32, [c_int32]),
         "dspk_last_error": (ctypes.c_char_p, []),
         "dspk_tiled_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
         "dspk_qweight_pack": (c_int32, [P(QWeightDesc), c_void_p, c_size_t, c_void_p]),
@@ -333,6 +334,15 @@ VARIANT_AUTO, VARIANT_STREAMK, VARIANT_SLAB, VARIANT_DOT = 0, 1, 2, 3
 def set_projection_variant(variant: int) -> int:
     """Process-wide projection decomposition; returns the previous setting."""
     prev = lib().dspk_set_projection_variant(int(variant))
+    if prev < 0:
+        _check(prev)
+    return prev
+
+
+def set_prefill_block_rows(rows: int) -> int:
+    """Process-wide prefill row block (0 automatic, 64, 128); returns the
+    previous setting."""
+    prev = lib().dspk_set_prefill_block_rows(int(rows))
     if prev < 0:
         _check(prev)
     return prev

@@ -9,6 +9,7 @@
 
 #include "../../include/dspk.h"
 #include "dspk_internal.h"
+#include "prefill_plan.h"
 
 namespace {
 
@@ -162,6 +163,12 @@ int dspk_set_projection_variant(int32_t variant) {
     if (prev < 0)
         return fail(DSPK_EINVAL, "dspk_set_projection_variant: variant=%d (0 auto, 1 stream-K, 2 slab, 3 dot)",
                     variant);
+    return prev;
+}
+
+int dspk_set_prefill_block_rows(int32_t rows) {
+    const int prev = dspk::set_prefill_block_rows(rows);
+    if (prev < 0) return fail(DSPK_EINVAL, "dspk_set_prefill_block_rows: rows=%d (0 automatic, 64 or 128)", rows);
     return prev;
 }
 

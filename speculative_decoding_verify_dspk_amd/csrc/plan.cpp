@@ -9,6 +9,7 @@
 #include <atomic>
 
 #include "dspk_internal.h"
+#include "prefill_plan.h"
 #include "sample_layout.h"
 
 namespace dspk {
@@ -134,6 +135,43 @@ GemmPlan plan_gemm_cus(int count, const int32_t *n, int32_t k, int32_t m, int bi
 
 GemmPlan plan_gemm(int count, const int32_t *n, int32_t k, int32_t m, int bits, bool argmax) {
     return plan_gemm_cus(count, n, k, m, bits, argmax, device_cus());
+}
+
+// Rows per prefill workgroup.  Where the 128-row workgroups would not cover
+// every CU the 64-row ones are taken (the Qwen3-4B-shaped k and v projections
+// over 2048 rows: 128 workgroups, 49-60 -> 33-41 us in 2/3/4/8-bit, 50 -> 42-44
+// us in bf16).  Otherwise each CU is taken to run ceil(workgroups / CUs) of
+// them, at 16 time units per 128-row workgroup and, for the 64-row ones whose
+// decoded weights serve half as many rows, 9 units (2- and 4-bit) or 11 (3-
+// and 8-bit, whose decoding costs more per weight); the shorter estimate
+// wins, 128 rows on a tie.  bf16 keeps 128-row blocks there: its 64-row
+// blocks issue twice the weight loads per matrix instruction and ran 15-40%
+// slower per row.  (Units fitted to rocprof durations of the seven
+// Qwen3-4B-shaped projections over 2048 rows with each block forced; the o
+// and down projections, 320 128-row workgroups, 108 -> 99 and 238 -> 224 us
+// in 2-bit, 119 -> 105 and 265 -> 231 us in 4-bit.)
+int prefill_block_rows(int32_t m, int32_t nblocks, int bits, int cus) {
+    const int64_t cols = ((int64_t)nblocks + 1) / 2;
+    const int64_t w128 = ((int64_t)m + 127) / 128 * cols, w64 = ((int64_t)m + 63) / 64 * cols;
+    if (w128 <= cus) return 64;
+    if (bits == 16) return 128;
+    const int64_t c128 = 16 * ((w128 + cus - 1) / cus);
+    const int64_t c64 = (bits == 3 || bits == 8 ? 11 : 9) * ((w64 + cus - 1) / cus);
+    return c64 < c128 ? 64 : 128;
+}
+
+namespace {
+std::atomic<int> g_prefill_rows{0};   // 0: automatic, else 64 or 128
+}  // namespace
+
+int set_prefill_block_rows(int rows) {
+    if (rows != 0 && rows != 64 && rows != 128) return -1;
+    return g_prefill_rows.exchange(rows, std::memory_order_relaxed);
+}
+
+int prefill_rows_for(int32_t m, int32_t nblocks, int bits) {
+    const int r = g_prefill_rows.load(std::memory_order_relaxed);
+    return r != 0 ? r : prefill_block_rows(m, nblocks, bits, device_cus());
 }
 
 size_t tiled_bytes(int32_t n, int32_t k, int bits) {

@@ -7,10 +7,13 @@
 // With hundreds of rows the work is bound by the matrix cores and the vector
 // ALUs, not by HBM, so this kernel is tiled for MFMA reuse rather than for
 // streaming:
-// * A workgroup computes a 128-row x 128-column block of y: four waves, each
-//   64 rows (four 16-row tiles) x one 64-column weight block (four 16-column
-//   tiles), K walked in stages of 128 (a whole 8-bit unit, half of a 2/3/4-bit
-//   unit, one bf16 unit of 64).
+// * A workgroup computes a 128-row (or 64-row) x 128-column block of y: four
+//   waves, each 64 (32) rows -- four (two) 16-row tiles -- x one 64-column
+//   weight block (four 16-column tiles), K walked in stages of 128 (a whole
+//   8-bit unit, half of a 2/3/4-bit unit, one bf16 unit of 64).  The 64-row
+//   block is taken where the 128-row blocks would leave CUs idle or
+//   unevenly loaded (few or skinny column blocks); both walk K in the same
+//   order, so their results are identical.
 // * Activations reach LDS by direct global-to-LDS loads (no staging
 //   registers), double-buffered: the next stage is in flight while the
 //   current one is computed.  Each wave loads its weight codes straight from
@@ -32,18 +35,19 @@
 
 #include "decode.h"
 #include "dspk_internal.h"
+#include "prefill_plan.h"
 
 namespace dspk {
 namespace {
 
 using namespace dec;
 
-constexpr int PBM = 128;                 // rows per workgroup
 constexpr int PT = 256;                  // threads per workgroup
 
 // One stage of K: SK = min(KU, 128) (a whole unit, or half of a 256-K
-// unit) for the workgroup's 128 rows, unpadded (a row is SK bf16 = CH
-// 16-byte chunks), filled by direct global-to-LDS loads.  Such a load writes
+// unit) for the workgroup's PBM = 32 RT rows (RT 16-row tiles per wave),
+// unpadded (a row is SK bf16 = CH 16-byte chunks), filled by direct
+// global-to-LDS loads.  Such a load writes
 // 16 bytes per lane at consecutive LDS addresses, so bank spreading cannot
 // come from padding: chunk ch of row R sits at position ch ^ (R & SWM) of
 // its row instead, and the load of that position fetches that chunk.  The 16
@@ -58,11 +62,16 @@ struct SCfg {
     static constexpr int NSB = BITS == 16 ? 1 : GH;         // scale/bias loads per lane and stage
     static constexpr int CH = SK / 8;                       // 16-byte chunks per row
     static constexpr int SWM = CH >= 16 ? 15 : CH - 1;      // position swizzle mask
-    static constexpr int STAGE = PBM * SK;                  // bf16 per stage
-    static constexpr int NI = STAGE / 512;                  // 1 KiB loads per stage (512 bf16)
     static constexpr int RPI = 64 / CH;                     // rows per 1 KiB load
-    static_assert(NI % (PT / 64) == 0, "stage loads must split evenly over the waves");
     static_assert(HALVES * GH == Cfg<BITS>::GS, "stages must tile the unit's groups");
+};
+// The row-dependent sizes of a stage with RT 16-row tiles per wave.
+template <int BITS, int RT>
+struct RCfg {
+    static constexpr int PBM = 32 * RT;                     // rows per workgroup
+    static constexpr int STAGE = PBM * SCfg<BITS>::SK;      // bf16 per stage
+    static constexpr int NI = STAGE / 512;                  // 1 KiB loads per stage (512 bf16)
+    static_assert(NI % (PT / 64) == 0, "stage loads must split evenly over the waves");
 };
 // bf16 index of chunk ch of row R in a stage
 template <int BITS>
@@ -71,14 +80,14 @@ __device__ __forceinline__ int swz_index(int R, int ch) {
     return R * S::SK + 8 * (ch ^ (R & S::SWM));
 }
 
-// One stage's share of a wave: 64 rows (four 16-row tiles r) x one 64-column
+// One stage's share of a wave: 16 RT rows (RT 16-row tiles r) x one 64-column
 // weight block (four 16-column tiles t), K = the unit's groups G0..G1-1 (the
 // stage's).  xb: the stage; wv: this wave's code slots of the unit; sbv: its
 // scale/bias dwords of the stage's groups; ng: valid groups of the unit.
-template <int BITS, int G0, int G1>
+template <int BITS, int RT, int G0, int G1>
 __device__ __forceinline__ void prefill_stage(const uint16_t *__restrict__ xb, const u32x4 (&wv)[Cfg<BITS>::NS],
                                               const u32x4 (&sbv)[SCfg<BITS>::NSB], int ng, int wr, int c, int j,
-                                              f32x4 (&y)[4][4]) {
+                                              f32x4 (&y)[RT][4]) {
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const bf16x8 ones = as_bf16x8(u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 #pragma unroll
@@ -116,9 +125,9 @@ __device__ __forceinline__ void prefill_stage(const uint16_t *__restrict__ xb, c
             }
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            // lane (c, j): row 64 wr + 16 r + c, K offsets 64 g + 16 j + 0..15
-            const int R = 64 * wr + 16 * r + c;
+        for (int r = 0; r < RT; ++r) {
+            // lane (c, j): row 16 (RT wr + r) + c, K offsets 64 g + 16 j + 0..15
+            const int R = 16 * (RT * wr + r) + c;
             const u32x4 x0 = *(const u32x4 *)(xb + swz_index<BITS>(R, 8 * (g - G0) + 2 * j));
             const u32x4 x1 = *(const u32x4 *)(xb + swz_index<BITS>(R, 8 * (g - G0) + 2 * j + 1));
             bf16x8 a0, a1;
@@ -161,13 +170,13 @@ __device__ __forceinline__ void prefill_stage(const uint16_t *__restrict__ xb, c
 // fills bf16 [512 i, 512 i + 512) of the stage, lane l the 8 at 512 i + 8 l).
 // Rows past m read row m - 1 and K past k reads K offset 0: those values
 // reach only rows that are never stored and groups that are never computed.
-template <int BITS>
+template <int BITS, int RT>
 __device__ __forceinline__ void prefill_dma_x(const PrefillArgs &A, int row0, int kb, uint16_t *stage, int w,
                                               int lane) {
     using S = SCfg<BITS>;
     const int rl = lane / S::CH, pos = lane % S::CH;
 #pragma unroll
-    for (int ii = 0; ii < S::NI / (PT / 64); ++ii) {
+    for (int ii = 0; ii < RCfg<BITS, RT>::NI / (PT / 64); ++ii) {
         const int i = w + (PT / 64) * ii;
         const int R = i * S::RPI + rl;
         const int ch = pos ^ (R & S::SWM);
@@ -201,19 +210,20 @@ __device__ __forceinline__ void prefill_fetch_sb(const unsigned char *ub0, int u
     }
 }
 
-// Final values of this wave's 64 x 64 block of y.
+// Final values of this wave's 16 RT x 64 block of y.
+template <int RT>
 __device__ __forceinline__ void prefill_store(const PrefillArgs &A, int row0, int wr, int b, int c, int j,
-                                              const f32x4 (&y)[4][4]) {
+                                              const f32x4 (&y)[RT][4]) {
     // lane (c, j) of tile (r, t) holds rows 4 j .. 4 j + 3, column c
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < RT; ++r)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int col = 64 * b + 16 * t + c;
             if (col >= A.n) continue;
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                const int row = row0 + 64 * wr + 16 * r + 4 * j + r4;
+                const int row = row0 + 16 * (RT * wr + r) + 4 * j + r4;
                 if (row < A.m) {
                     if (A.y_bf16)
                         ((uint16_t *)A.y)[(int64_t)row * A.ldy + col] = f2bf16(y[r][t][r4]);
@@ -233,31 +243,32 @@ __device__ __forceinline__ void prefill_store(const PrefillArgs &A, int row0, in
 // arrays used alternately and the loop handles two units per trip, so no
 // LDS read of a stage can alias the buffer being filled and no register set
 // is ever copied.
-template <int BITS>
+template <int BITS, int RT>
 __global__ __launch_bounds__(PT, 2) void prefill_kernel(const PrefillArgs A) {
     using C = Cfg<BITS>;
     using S = SCfg<BITS>;
-    __shared__ __attribute__((aligned(1024))) uint16_t xs0[S::STAGE];
-    __shared__ __attribute__((aligned(1024))) uint16_t xs1[S::STAGE];
+    using R = RCfg<BITS, RT>;
+    __shared__ __attribute__((aligned(1024))) uint16_t xs0[R::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t xs1[R::STAGE];
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wr = w >> 1, wc = w & 1;
     const int c = lane & 15, j = lane >> 4;
-    const int row0 = blockIdx.x * PBM;
+    const int row0 = blockIdx.x * R::PBM;
     const int b = 2 * blockIdx.y + wc;                     // this wave's 64-column block
     const bool has_block = b < A.nblocks;
     const unsigned char *ub0 = (const unsigned char *)A.tiles + (size_t)b * A.nst * C::UNIT;
     const int NST = A.nst;
 
-    f32x4 y[4][4];
+    f32x4 y[RT][4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < RT; ++r)
 #pragma unroll
         for (int t = 0; t < 4; ++t) y[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     u32x4 wa[C::NS], wb[C::NS];                 // code sets: even units, odd units
     u32x4 s0[S::NSB], s1[S::NSB];               // scale/bias sets: with stage xs0, with xs1
-    prefill_dma_x<BITS>(A, row0, 0, xs0, w, lane);
+    prefill_dma_x<BITS, RT>(A, row0, 0, xs0, w, lane);
     if (has_block) {
         prefill_fetch_codes<BITS>(ub0, 0, lane, wa);
         prefill_fetch_sb<BITS>(ub0, 0, 0, c, s0);
@@ -274,15 +285,15 @@ __global__ __launch_bounds__(PT, 2) void prefill_kernel(const PrefillArgs A) {
         constexpr int h = decltype(hc)::value;
         const int nu = h + 1 < S::HALVES ? u : u + 1, nh = h + 1 < S::HALVES ? h + 1 : 0;
         if (nu < NST) {
-            prefill_dma_x<BITS>(A, row0, C::KU * nu + S::SK * nh, nxt, w, lane);
+            prefill_dma_x<BITS, RT>(A, row0, C::KU * nu + S::SK * nh, nxt, w, lane);
             if (has_block) {
                 if (h == 0 && u + 1 < NST) prefill_fetch_codes<BITS>(ub0, u + 1, lane, wnxt);
                 prefill_fetch_sb<BITS>(ub0, nu, nh, c, snxt);
             }
         }
         if (has_block)
-            prefill_stage<BITS, h * S::GH, (h + 1) * S::GH>(cur, wcur, scur, min(C::GS, (A.k - C::KU * u) / 64),
-                                                            wr, c, j, y);
+            prefill_stage<BITS, RT, h * S::GH, (h + 1) * S::GH>(cur, wcur, scur,
+                                                                min(C::GS, (A.k - C::KU * u) / 64), wr, c, j, y);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     };
@@ -306,19 +317,23 @@ __global__ __launch_bounds__(PT, 2) void prefill_kernel(const PrefillArgs A) {
     if (has_block) prefill_store(A, row0, wr, b, c, j, y);
 }
 
-}  // namespace
-
-hipError_t launch_prefill(const PrefillArgs &A, int bits, hipStream_t s) {
-    const dim3 grid((unsigned)((A.m + PBM - 1) / PBM), (unsigned)((A.nblocks + 1) / 2)), block(PT);
+template <int RT>
+hipError_t launch_rt(const PrefillArgs &A, int bits, hipStream_t s) {
+    const dim3 grid((unsigned)((A.m + 32 * RT - 1) / (32 * RT)), (unsigned)((A.nblocks + 1) / 2)), block(PT);
     switch (bits) {
-        case 2: hipLaunchKernelGGL(prefill_kernel<2>, grid, block, 0, s, A); break;
-        case 3: hipLaunchKernelGGL(prefill_kernel<3>, grid, block, 0, s, A); break;
-        case 4: hipLaunchKernelGGL(prefill_kernel<4>, grid, block, 0, s, A); break;
-        case 8: hipLaunchKernelGGL(prefill_kernel<8>, grid, block, 0, s, A); break;
-        case 16: hipLaunchKernelGGL(prefill_kernel<16>, grid, block, 0, s, A); break;
+        case 2: hipLaunchKernelGGL((prefill_kernel<2, RT>), grid, block, 0, s, A); break;
+        case 3: hipLaunchKernelGGL((prefill_kernel<3, RT>), grid, block, 0, s, A); break;
+        case 4: hipLaunchKernelGGL((prefill_kernel<4, RT>), grid, block, 0, s, A); break;
+        case 8: hipLaunchKernelGGL((prefill_kernel<8, RT>), grid, block, 0, s, A); break;
+        case 16: hipLaunchKernelGGL((prefill_kernel<16, RT>), grid, block, 0, s, A); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs &A, int bits, hipStream_t s) {
+    return prefill_rows_for(A.m, A.nblocks, bits) == 64 ? launch_rt<2>(A, bits, s) : launch_rt<4>(A, bits, s);
 }
 
 }  // namespace dspk

@@ -18,6 +18,7 @@
 
 #include "dspk.h"
 #include "dspk_internal.h"
+#include "prefill_plan.h"
 #include "sample_layout.h"
 
 static int g_fail = 0;
@@ -331,6 +332,26 @@ static void packing_and_prefill() {
     }
 }
 
+// The prefill row block: Qwen3-4B-shaped projections over 2048 rows on 256
+// CUs, a one-row call, and the override.
+static void prefill_blocks() {
+    for (int bits : {2, 3, 4, 8, 16}) {
+        CHECK(dspk::prefill_block_rows(2048, 64, bits, 256) == 128);    // q, 4096 columns: two per CU
+        CHECK(dspk::prefill_block_rows(2048, 16, bits, 256) == 64);     // k, v, 1024: 128 workgroups
+        CHECK(dspk::prefill_block_rows(2048, 152, bits, 256) == 128);   // gate, up, 9728
+        CHECK(dspk::prefill_block_rows(1, 1, bits, 256) == 64);
+        // o, down, 2560: 320 128-row workgroups load the CUs unevenly
+        CHECK(dspk::prefill_block_rows(2048, 40, bits, 256) == (bits == 2 || bits == 4 ? 64 : 128));
+    }
+    CHECK(dspk_set_prefill_block_rows(128) == 0);
+    CHECK(dspk::prefill_rows_for(2048, 16, 8) == 128);
+    CHECK(dspk_set_prefill_block_rows(64) == 128);
+    CHECK(dspk::prefill_rows_for(2048, 64, 8) == 64);
+    expect_error(dspk_set_prefill_block_rows(96), DSPK_EINVAL);
+    CHECK(dspk_set_prefill_block_rows(0) == 64);
+    CHECK(dspk::prefill_rows_for(2048, 16, 8) == 64);
+}
+
 static void sampling() {
     for (int v : {1, 100, 4096, 4097, 151936})
         for (int rows : {2, 6, 17, 32}) {
@@ -392,6 +413,7 @@ int main() {
     variants();
     rejections();
     packing_and_prefill();
+    prefill_blocks();
     sampling();
     policy();
     if (g_fail) {

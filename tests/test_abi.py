@@ -37,6 +37,14 @@ def test_exports_every_header_symbol(lib):
     assert lib.dspk_version() >= 100
 
 
+def test_prefill_block_rows_setting(lib):
+    assert binding.set_prefill_block_rows(64) == 0
+    assert binding.set_prefill_block_rows(128) == 64
+    with pytest.raises(binding.DspkError):
+        binding.set_prefill_block_rows(96)
+    assert binding.set_prefill_block_rows(0) == 128
+
+
 def _desc(n=64, k=128, bits=8, group=64, tiles=0x10000):
     return binding.TiledDesc(n, k, bits, group, tiles)
 

@@ -72,12 +72,17 @@ def test_prefill_deterministic():
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
-@pytest.mark.parametrize("bits", [8, 4, 16])
-def test_prefill_full_shape_sampled_rows(bits):
-    """Qwen3-4B gate projection (9728 x 2560) over 2048 prompt rows on the
-    device; the oracle recomputes 12 sampled rows in full."""
+@pytest.mark.parametrize("bits,n,k", [
+    (8, 9728, 2560), (4, 9728, 2560), (16, 9728, 2560),     # gate: 128-row blocks
+    (8, 1024, 2560), (4, 2560, 9728),                       # k/v and down: 64-row blocks
+])
+def test_prefill_full_shape_sampled_rows(bits, n, k):
+    """Qwen3-4B projections over 2048 prompt rows on the device, with the
+    row block chosen automatically; the oracle recomputes 12 sampled rows in
+    full."""
     t = torch()
-    n, k, m = 9728, 2560, 2048
+    m = 2048
+    print(f"prefill full shape bits={bits} n={n} k={k}", flush=True)
     w = inputs.make_qweight(n, k, bits, "prefill-full")
     x = inputs.make_activations(m, k, "prefill-full")
     got = run_prefill(w, x, m)
@@ -85,6 +90,28 @@ def test_prefill_full_shape_sampled_rows(bits):
     ref = oracle.qlinear(x[rows], w.codes, w.scales, w.biases, bits, n, k)
     assert_rows_close(got[rows], ref, what=f"bits={bits} sampled rows")
     assert np.isfinite(got).all()
+
+
+@pytest.mark.parametrize("bits", [8, 4, 3, 2, 16])
+def test_prefill_row_blocks_identical(bits):
+    """64-row and 128-row output blocks walk K in the same order, so forcing
+    either gives bit-identical results (ragged rows and columns, a short last
+    K unit); both match the oracle."""
+    n, k, m = 200, 1088, 300
+    print(f"prefill row blocks bits={bits}", flush=True)
+    w = inputs.make_qweight(n, k, bits, "prefill-blocks")
+    x = inputs.make_activations(m, k, "prefill-blocks")
+    dw = binding.DeviceQWeight.upload(w)
+    prev = binding.set_prefill_block_rows(64)
+    try:
+        a = run_prefill(w, x, m, dw=dw)
+        binding.set_prefill_block_rows(128)
+        b = run_prefill(w, x, m, dw=dw)
+    finally:
+        binding.set_prefill_block_rows(prev)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    ref = oracle.qlinear(x, w.codes, w.scales, w.biases, bits, n, k)
+    assert_rows_close(a, ref, what=f"bits={bits} row blocks")
 
 
 def test_prefill_rejects_bad_arguments():
