@@ -276,6 +276,10 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
 // ds_read_b128.  Per step: issue the next chunk's loads, then the weights DEPTH
 // - 1 steps ahead (in that order: a wait for the chunk then leaves the newer
 // weight requests in flight), compute from LDS, store the next chunk, barrier.
+// A workgroup may hold T tiles (T W waves, T = blockDim.x / 64 W, consecutive
+// tiles of the launch): every tile walks the same K steps, so one staged
+// chunk serves all of them, and a CU given T tiles stages each chunk once
+// instead of T times.
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // v_dot2_f32_bf16: c + a.x * b.x + a.y * b.y (bf16 pairs, products exact in fp32)
@@ -298,7 +302,7 @@ constexpr int lds_slab_depth(int bits) { return bits == 16 ? 4 : 2; }
 // host uses it only when forced: it exists to measure where the matrix cores
 // stop paying for padded rows.
 template <int BITS, int W, int MR>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) void qgemm_slab_lds_kernel(
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4))) void qgemm_slab_lds_kernel(
     const GemmLaunch L) {
     using C = Cfg<BITS>;
     static_assert(BITS == 8 || BITS == 16, "activations in LDS: 8-bit and bf16 units only");
@@ -306,35 +310,47 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
     constexpr int DEPTH = lds_slab_depth(BITS);
     constexpr int CK = W * C::KU;                      // K elements per step
     constexpr int ROWP = CK + kLdsPad;                 // staged row pitch (bf16)
-    constexpr int PPT = (16 * CK / 8 + 64 * W - 1) / (64 * W);   // 16-byte pieces per thread (16 rows)
-    __shared__ __attribute__((aligned(16))) uint16_t xs[2][16 * ROWP];
-    __shared__ f32x4 red[W][kWave];
+    constexpr int PPT = (16 * CK / 8) / (64 * W);      // 16-byte pieces per thread at one tile per workgroup
+    // the two chunk buffers; after the last step the same LDS holds the
+    // waves' partial tiles (at most 16 waves)
+    constexpr int XS = 2 * 16 * ROWP > 16 * kWave * 8 ? 2 * 16 * ROWP : 16 * kWave * 8;
+    __shared__ __attribute__((aligned(16))) uint16_t xs[XS];
+    f32x4 *const red = (f32x4 *)xs;
 
     (void)L;
     const GemmLaunch *KL = (const GemmLaunch *)__builtin_amdgcn_kernarg_segment_ptr();
     const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int NT = (int)blockDim.x;                     // 64 W T threads
+    const int wt = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave in the workgroup
+    const int tt = wt / W, w = wt - W * tt;             // its tile in the workgroup, its wave in the tile
     const int c = lane & 15, j = lane >> 4;
-    const int gb = (int)blockIdx.x >> 2, t = (int)blockIdx.x & 3;
+    const int tile = (int)blockIdx.x * (NT / (64 * W)) + tt;
+    const int gb = tile >> 2, t = tile & 3;
     int pi = 0;
 #pragma unroll
     for (int i = 1; i < kMaxGrouped; ++i)
         if (i < KL->count && gb >= KL->p[i].cg_begin) pi = i;
     const GemmProblem &P = KL->p[pi];
     const int cb = gb - P.cg_begin;
-    if (cb * kBlockCols + 16 * t >= P.n) return;        // the whole workgroup
+    // a tile past the last column still stages and meets every barrier
+    const bool active = cb * kBlockCols + 16 * t < P.n;
     const int NST = KL->nst, K = KL->k, G = K >> 6, M = KL->m;
     const int NSTEP = (NST + W - 1) / W;
-    const unsigned char *const base = (const unsigned char *)P.tiles + (size_t)cb * NST * C::UNIT;
+    // a tile past the last column streams block 0, tile 0 of its problem
+    // instead (never used): the weight requests stay unconditional, so the
+    // compiler's count of outstanding loads still places each wait
+    const int tl = active ? t : 0;
+    const unsigned char *const base = (const unsigned char *)P.tiles + (size_t)(active ? cb : 0) * NST * C::UNIT;
     const uint16_t *const xg = KL->x;
     const int64_t ldx = KL->ldx;
 
     // staging: thread tid copies 8 elements at column col0 of rows r0, r0 +
-    // RPP, ... (RPP rows per pass of the workgroup); rows past m and columns
-    // past k are zero
+    // RPP, ... (a pass of the workgroup covers RPP whole rows, RPP = NT / CPR
+    // = 512 T / KU); rows past m and columns past k are zero, rows past the
+    // 16 staged ones are skipped
     constexpr int CPR = CK / 8;                        // 16-byte pieces per staged row
-    constexpr int RPP = 64 * W / CPR;                  // rows per pass
-    static_assert(RPP * PPT == 16, "the passes cover the 16 staged rows");
+    static_assert((64 * W) % CPR == 0 && PPT * (64 * W / CPR) == 16, "passes of whole rows cover the 16 rows");
+    const int RPP = NT / CPR;
     const int r0 = tid / CPR, col0 = 8 * (tid % CPR);
     const uint16_t *const xt = xg + (int64_t)r0 * ldx + col0;
     u32x4 stg[PPT];
@@ -345,10 +361,11 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
             stg[q] = (r0 + RPP * q < M && kin) ? *(const u32x4 *)(xt + (int64_t)(RPP * q) * ldx + i * CK)
                                                : u32x4{0u, 0u, 0u, 0u};
     };
-    uint16_t *const xsl = &xs[0][r0 * ROWP + col0];
+    uint16_t *const xsl = xs + r0 * ROWP + col0;
     auto stage_store = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < PPT; ++q) *(u32x4 *)(xsl + buf * (16 * ROWP) + RPP * q * ROWP) = stg[q];
+        for (int q = 0; q < PPT; ++q)
+            if (r0 + RPP * q < 16) *(u32x4 *)(xsl + buf * (16 * ROWP) + RPP * q * ROWP) = stg[q];
     };
 
     struct Slot {
@@ -362,9 +379,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
         const int st = min(w + i * W, NST - 1);
         const unsigned char *ub = base + (size_t)st * C::UNIT;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) s.w[q] = load_nt(ub + (4 * q + t) * 1024 + 16 * lane);
+        for (int q = 0; q < 2; ++q) s.w[q] = load_nt(ub + (4 * q + tl) * 1024 + 16 * lane);
 #pragma unroll
-        for (int g = 0; g < C::SBQ; ++g) s.sb[g] = load4(ub + C::SBOFF + c * (16 * C::SBQ) + 16 * g + 4 * t);
+        for (int g = 0; g < C::SBQ; ++g) s.sb[g] = load4(ub + C::SBOFF + c * (16 * C::SBQ) + 16 * g + 4 * tl);
     };
     f32x4 y = {0.f, 0.f, 0.f, 0.f};
     float yd[MR > 0 ? MR : 1];
@@ -373,7 +390,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
     const int xrow = min(c, M - 1);
     auto compute = [&](int i, const Slot &s, int buf) __attribute__((always_inline)) {
         const int st = w + i * W;
-        if (st >= NST) return;
+        if (!active || st >= NST) return;
         const int ng = min(C::GS, G - st * C::GS);
         if constexpr (MR > 0) {
             const uint32_t ONES = 0x3f803f80u;          // two bf16 ones
@@ -387,7 +404,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
 #pragma unroll
                 for (int r = 0; r < MR; ++r) {
                     // rows past m are staged as zeros: they add nothing and are not stored
-                    const uint16_t *xp = &xs[buf][r * ROWP + w * C::KU + 64 * g + 16 * j];
+                    const uint16_t *xp = &xs[buf * (16 * ROWP) + r * ROWP + w * C::KU + 64 * g + 16 * j];
                     const u32x4 xa = *(const u32x4 *)xp, xb = *(const u32x4 *)(xp + 8);
                     float d = 0.f, sx = 0.f;
 #pragma unroll
@@ -408,7 +425,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
         }
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         const bf16x8 ones = as_bf16x8(u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
-        const uint16_t *xr = &xs[buf][xrow * ROWP + w * C::KU + 16 * j];
+        const uint16_t *xr = &xs[buf * (16 * ROWP) + xrow * ROWP + w * C::KU + 16 * j];
 #pragma unroll
         for (int g = 0; g < C::GS; ++g) {
             if (g >= ng) break;
@@ -465,21 +482,21 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
     const int n = cb * kBlockCols + 16 * t + c;
     if constexpr (MR > 0) {
         // the four K quarters of a column (lanes c, c + 16, c + 32, c + 48), then the waves
-        float *redf = (float *)&red[0][0];
+        float *redf = (float *)red;
 #pragma unroll
         for (int r = 0; r < MR; ++r) {
             yd[r] += __shfl_xor(yd[r], 16);
             yd[r] += __shfl_xor(yd[r], 32);
-            if (j == 0) redf[(w * MR + r) * 16 + c] = yd[r];
+            if (j == 0) redf[(wt * MR + r) * 16 + c] = yd[r];
         }
         __syncthreads();
-        if (w != 0 || j != 0 || n >= P.n) return;
+        if (!active || w != 0 || j != 0 || n >= P.n) return;
 #pragma unroll
         for (int r = 0; r < MR; ++r) {
             if (r >= M) break;
-            float z = redf[r * 16 + c];
+            float z = redf[(W * tt * MR + r) * 16 + c];
 #pragma unroll
-            for (int q = 1; q < W; ++q) z += redf[(q * MR + r) * 16 + c];
+            for (int q = 1; q < W; ++q) z += redf[((W * tt + q) * MR + r) * 16 + c];
             if (KL->y_bf16)
                 st_global_u16((uint16_t *)P.y + (int64_t)r * P.ldy + n, f2bf16(z));
             else
@@ -487,13 +504,13 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(4))) voi
         }
         return;
     }
-    red[w][lane] = y;
+    red[wt * kWave + lane] = y;
     __syncthreads();
-    if (w != 0) return;
+    if (!active || w != 0) return;
     if (n >= P.n) return;
-    f32x4 z = red[0][lane];
+    f32x4 z = red[W * tt * kWave + lane];
 #pragma unroll
-    for (int q = 1; q < W; ++q) z += red[q][lane];
+    for (int q = 1; q < W; ++q) z += red[(W * tt + q) * kWave + lane];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
         const int m = 4 * j + r4;
@@ -520,15 +537,26 @@ hipError_t launch_w(const GemmLaunch &L, int waves, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Tiles per workgroup of the LDS-staged slab kernel: a CU's whole share
+// ceil(tiles / CUs) in one workgroup of T W <= 16 waves (one workgroup per
+// CU), so that the CU stages each chunk of x once; 1 where the share does not
+// fit (the tiles then run in more than one round).
+int lds_tiles_per_workgroup(int64_t tiles, int waves, int cus) {
+    const int64_t share = (tiles + cus - 1) / cus;
+    return share >= 1 && share * waves <= 16 ? (int)share : 1;
+}
+
 template <int BITS, int MR = 0>
 hipError_t launch_lds_w(const GemmLaunch &L, int waves, hipStream_t s) {
-    const dim3 grid((unsigned)(4 * L.total_cg));
+    const int64_t tiles = 4 * (int64_t)L.total_cg;
+    const int T = lds_tiles_per_workgroup(tiles, waves, device_cus());
+    const dim3 grid((unsigned)((tiles + T - 1) / T)), block((unsigned)(64 * waves * T));
     switch (waves) {
-        case 16: hipLaunchKernelGGL((qgemm_slab_lds_kernel<BITS, 16, MR>), grid, dim3(1024), 0, s, L); break;
-        case 8: hipLaunchKernelGGL((qgemm_slab_lds_kernel<BITS, 8, MR>), grid, dim3(512), 0, s, L); break;
-        case 4: hipLaunchKernelGGL((qgemm_slab_lds_kernel<BITS, 4, MR>), grid, dim3(256), 0, s, L); break;
-        case 3: hipLaunchKernelGGL((qgemm_slab_lds_kernel<BITS, 3, MR>), grid, dim3(192), 0, s, L); break;
-        case 2: hipLaunchKernelGGL((qgemm_slab_lds_kernel<BITS, 2, MR>), grid, dim3(128), 0, s, L); break;
+        case 16: hipLaunchKernelGGL((qgemm_slab_lds_kernel<BITS, 16, MR>), grid, block, 0, s, L); break;
+        case 8: hipLaunchKernelGGL((qgemm_slab_lds_kernel<BITS, 8, MR>), grid, block, 0, s, L); break;
+        case 4: hipLaunchKernelGGL((qgemm_slab_lds_kernel<BITS, 4, MR>), grid, block, 0, s, L); break;
+        case 3: hipLaunchKernelGGL((qgemm_slab_lds_kernel<BITS, 3, MR>), grid, block, 0, s, L); break;
+        case 2: hipLaunchKernelGGL((qgemm_slab_lds_kernel<BITS, 2, MR>), grid, block, 0, s, L); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
