@@ -263,6 +263,41 @@ def test_slab_resident_wave_counts(variant, bits, n, k, m):
     assert_rows_close(got[:, cols], ref, what=f"slab bits={bits} n={n} k={k} m={m} (sampled columns)")
 
 
+@pytest.mark.parametrize("bits", [8, 16])
+@pytest.mark.parametrize("m", [3, 16])
+def test_slab_multi_tile_workgroups_ragged_grouped(variant, bits, m):
+    """Forced slab launch of a grouped call with ragged widths, 1180 tiles:
+    five tiles per workgroup on a 256-CU device, so workgroups straddle the
+    two weights and hold tiles past each weight's last column (which stage
+    and wait but store nothing).  Both outputs against the oracle on sampled
+    columns (each weight's first and last columns included), deterministic,
+    columns past n untouched."""
+    t = torch()
+    variant(binding.VARIANT_SLAB)
+    k = 2560
+    print(f"slab multi-tile bits={bits} m={m}", flush=True)
+    ws_ = [inputs.make_qweight(n, k, bits, "slab-multi", n, m) for n in (9800, 9000)]
+    x = inputs.make_activations(m, k, "slab-multi", m)
+    dws = [binding.DeviceQWeight.upload(w) for w in ws_]
+    xd = dev_act(x)
+    runs = []
+    for _ in range(2):
+        ys = [t.full((m, w.n + 8), -7.0, dtype=t.float32, device="cuda") for w in ws_]
+        binding.qgemm_verify_grouped(dws, xd, m, ys, binding.alloc_workspace(
+            sum(binding.qgemm_workspace_bytes(w.n, k, m) for w in ws_)))
+        t.cuda.synchronize()
+        runs.append([y.cpu().numpy() for y in ys])
+    for a, b in zip(*runs):
+        assert np.array_equal(a, b)
+    g = np.random.default_rng(bits + m)
+    for w, y in zip(ws_, runs[0]):
+        assert (y[:, w.n:] == -7.0).all(), "columns past n were written"
+        cols = np.unique(np.concatenate([[0, 15, 16, w.n - 41, w.n - 9, w.n - 8, w.n - 1],
+                                         g.choice(w.n, 120, replace=False)]))
+        ref = oracle_columns(w, x, cols)
+        assert_rows_close(y[:, cols], ref, what=f"slab multi-tile bits={bits} n={w.n} m={m} (sampled columns)")
+
+
 def test_slab_grouped_and_deterministic(variant):
     """The slab kernel on a grouped q/k/v call (the automatic choice at this
     size): deterministic, and each weight agrees with the oracle."""
