@@ -157,26 +157,22 @@ constexpr int kDotMaxRows = 4;
 // the activations in LDS; other calls keep them in registers.  kAuto takes
 // the slab kernel for 8-bit and bf16 calls of at most kSlabLdsMaxRows rows
 // when the weights one CU streams for its tiles (tiles per CU x 16 x k) are
-// at most kSlabAutoWeightsNarrow (<= 8 rows), or, at 9..16 rows, at most
-// kSlabAutoWeightsWide with k <= kSlabAutoMaxKWide and the tiles filling at
-// least three quarters of the CUs' last round.  Per-launch rocprof
-// durations, slab vs stream-K, 1 / 8 / 16 rows:
-//   Qwen3-4B o  (160 tiles, k 4096)   6.8 / 7.4 / 8.0  vs 10.3 / 10.5 / 11.0 us
-//   Qwen3-4B gate/up (1216, k 2560)  16.1 / 17.7 / 19.1 vs 18.0 / 18.7 / 20.0
-//   27B down    (320 tiles, k 17408) 26.2 / 34.6 / 43.2 vs 22.6 / 22.9 / 23.9
-//   9B gate/up  (1536 tiles, k 4096) 25.2 / 28.8 / 32.9 vs 24.6 / 24.6 / 25.7
-//     (4-wave workgroups in two rounds; as eight resident 2-wave workgroups
-//     per CU, HIP events at 1 / 4 / 8 rows: 24.2-24.7 / 25.4-25.6 / 26.7-26.8
-//     vs 26.9 / 27.5 / 26.9 us, bf16 34.3-34.8 vs 40.2-40.5 us, hence the
-//     400 KiB limit, which that launch's 384 KiB per CU fits)
-// and at 9 / 12 / 16 rows:
-//   27B q/k/v   (448 tiles, k 5120)  13.7 / 14.9 / 16.1 vs 16.7 / 16.8 / 17.1
-//   27B o       (320 tiles, k 5120)  12.7 / 13.6 / 15.4 vs 13.2 / 13.0 / 13.0
-//   Qwen3-4B down (160, k 9728)      12.1 / 13.0 / 14.4 vs 13.2 / 13.4 / 13.5
-//   9B down     (256 tiles, k 12288) 16.4 / 17.5 / 18.6 vs 15.7 / 15.1 / 15.7
+// at most kSlabAutoWeights and, at 9..16 rows, k <= kSlabAutoMaxKWide and the
+// tiles fill at least three quarters of the CUs' last round.  A CU's tiles
+// share one workgroup and one staged copy of x.  Launch times, slab vs
+// stream-K, 8-bit, HIP events over back-to-back launches, 8 / 9 / 12 / 16 rows:
+//   9B gate/up   (1536 tiles, k 4096)  20.2 / 21.4 / 20.6 / 21.8 vs 23.9 / 24.0 / 24.3 / 24.9 us
+//   Qwen3-4B gate/up (1216, k 2560)    12.5 / 12.7 / 13.0 / 13.7 vs 17.7 / 17.6 / 17.9 / 18.6
+//   27B o        (320 tiles, k 5120)   10.4 / 10.6 / 11.2 / 12.1 vs 11.4 / 11.4 / 11.5 / 11.7
+//   Qwen3-4B down (160, k 9728)        12.0 / 12.0 / 12.8 / 14.0 vs 12.9 / 12.9 / 13.0 / 13.0
+//   9B down      (256 tiles, k 12288)  15.5 / 15.3 / 16.4 / 17.6 vs 14.5 / 14.4 / 14.4 / 15.2
+//   27B gate/up  (2176 tiles, k 5120)  46.0 / 47.0 / 50.1 / 56.1 vs 40.8 / 41.1 / 42.0 / 43.4
+//   27B down     (320 tiles, k 17408)  28.1 / 28.8 / 30.9 / 34.1 vs 22.2 / 22.2 / 22.5 / 23.6
+// (the 27B gate/up, 8.5 tiles per CU, runs in two rounds; at 1..8 rows the
+// 9B gate/up as eight resident 2-wave tiles per CU had measured 24.2-25.6 us
+// against stream-K's 26.9-27.5, bf16 34.3-34.8 against 40.2-40.5 us).
 constexpr int kSlabLdsMaxRows = 16;
-constexpr int64_t kSlabAutoWeightsNarrow = 400 * 1024;
-constexpr int64_t kSlabAutoWeightsWide = 200 * 1024;
+constexpr int64_t kSlabAutoWeights = 400 * 1024;
 constexpr int32_t kSlabAutoMaxKWide = 5120;
 int projection_variant();               // the process-wide setting (DSPK_VARIANT, or the setter)
 int set_projection_variant(int v);      // previous setting, or -1 if v is not a Variant

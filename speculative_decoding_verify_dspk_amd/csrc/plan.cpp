@@ -80,18 +80,18 @@ static int slab_waves_for(int64_t slabs, int cus) {
 // tiles stay small -- it saves the stream-K kernel's split-block exchange and
 // most of its small loads, but a CU given two long tiles (or many) streams
 // them alone at the end.  Above 8 rows the staged activations grow with the
-// rows and with K, and a launch whose CUs hold uneven tile counts waits for
-// the fuller ones, so the slab is kept there only for K <= 5120 and tiles
-// that fill at least three quarters of the CUs' last round.  Limits from
-// per-launch rocprof durations of the 4B-, 9B- and 27B-shaped layers at 1, 8,
-// 9, 12 and 16 rows (8-bit and bf16).
+// rows and with K (a CU stages them once for all its tiles, but a long K
+// still costs), and a launch whose CUs hold uneven tile counts waits for the
+// fuller ones, so the slab is kept there only for K <= 5120 and tiles that
+// fill at least three quarters of the CUs' last round.  Limits from launch
+// durations of the 4B-, 9B- and 27B-shaped layers at 1, 8, 9, 12 and 16 rows
+// (8-bit and bf16).
 static bool slab_pays(int bits, int m, int64_t slabs, int32_t k, int cus) {
     if (!(bits == 8 || bits == 16) || m > kSlabLdsMaxRows) return false;
     const int64_t per_cu = (slabs + cus - 1) / cus;               // tiles per CU
     const int64_t weights = per_cu * 16 * (int64_t)k;             // weights one CU streams
-    if (m <= 8) return weights <= kSlabAutoWeightsNarrow;
-    return weights <= kSlabAutoWeightsWide && k <= kSlabAutoMaxKWide &&
-           (per_cu == 1 || 4 * slabs >= 3 * (int64_t)cus * per_cu);
+    if (weights > kSlabAutoWeights) return false;
+    return m <= 8 || (k <= kSlabAutoMaxKWide && (per_cu == 1 || 4 * slabs >= 3 * (int64_t)cus * per_cu));
 }
 
 GemmPlan plan_gemm_cus(int count, const int32_t *n, int32_t k, int32_t m, int bits, bool argmax, int cus) {

@@ -94,7 +94,7 @@ hipError_t launch_qgemm_slab(const GemmLaunch &L, int bits, int waves, hipStream
     if (projection_variant() == kAuto) {
         CHECK((bits == 8 || bits == 16) && L.m <= kSlabLdsMaxRows);
         const int64_t per_cu = (4 * (int64_t)L.total_cg + 255) / 256;
-        CHECK(per_cu * 16 * L.k <= (L.m <= 8 ? kSlabAutoWeightsNarrow : kSlabAutoWeightsWide));
+        CHECK(per_cu * 16 * L.k <= kSlabAutoWeights);
     }
     return hipSuccess;
 }
