@@ -179,7 +179,7 @@ int set_projection_variant(int v);      // previous setting, or -1 if v is not a
 
 struct GemmPlan {
     int32_t nst, nq, quads, grid, total_cg;
-    int32_t slab_waves;       // > 0: slab kernel with this many waves per workgroup (grid = 4 * total_cg)
+    int32_t slab_waves;       // > 0: slab kernel with this many waves per 16-column tile (4 * total_cg tiles)
     int32_t dot;              // with slab_waves: the dot-product form of the slab kernel
     int32_t pairs;            // see GemmLaunch::pairs
     bool fits;                // quads * grid < 2^31 (the kernel's index range)

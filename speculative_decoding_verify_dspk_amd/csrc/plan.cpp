@@ -56,13 +56,13 @@ int set_projection_variant(int v) {
     return prev;
 }
 
-// Waves per workgroup of the slab kernel for `slabs` tiles, or 0 when the
-// tiles would not all be resident at once (a slab launch then takes 4 waves
-// per workgroup and runs its tiles in more than one round).  At most 128
-// VGPRs per lane, a CU holds 16 waves: one workgroup of 16, two of 8, four
-// of 4, five of 3 or eight of 2; the most waves per tile that still fit all
-// tiles are taken, for the most loads in flight per tile.  (Resident 3- or
-// 2-wave workgroups rather than a second round of 4-wave ones: Qwen3-4B-
+// Waves per tile of the slab kernel for `slabs` tiles, or 0 when the tiles
+// would not all be resident at once (a slab launch then takes 4 waves per
+// tile and runs its tiles in more than one round).  At most 128 VGPRs per
+// lane, a CU holds 16 waves: one tile of 16, two of 8, four of 4, five of 3
+// or eight of 2; the most waves per tile that still fit all tiles are taken,
+// for the most loads in flight per tile.  (Resident 3- or 2-wave tiles
+// rather than a second round of 4-wave ones: Qwen3-4B-
 // shaped gate/up, 4.75 tiles per CU, 18.4-19.7 -> 15.4-17.0 us at 1-8 rows;
 // 9B-shaped gate/up, 6 tiles per CU, once the automatic choice takes it,
 // 26.9-27.5 -> 24.2-25.6 us at 1-4 rows and bf16 40.2-40.5 -> 34.3-34.8 us.)

@@ -1,5 +1,6 @@
-// Verify-pass projection for launches with few output columns: one workgroup
-// per 16-column tile ("slab") over the whole K range, for gfx950 (MI355X).
+// Verify-pass projection for launches with few output columns: each
+// 16-column tile ("slab") over the whole K range is the work of W waves of
+// one workgroup, for gfx950 (MI355X).
 //
 // What is computed is the projection of qgemm.hip, y[i][c] = sum_r x[i][r] *
 // (s[c][r/64] * q[c][r] + b[c][r/64]) ("mlx-dspark" wiki summary, sections
@@ -12,18 +13,18 @@
 // round trips (partial stores, arrival ticket, piece loads) at the end of the
 // launch.  For the small launches of a decoder layer (2560-column o and down,
 // 6144-column q/k/v) that exchange and the cold start are most of the launch.
-// Here a workgroup owns one 16-column MFMA tile of one 64-column block: its
-// W waves take the block's K units round-robin (unit w, w + W, ...), each
-// wave streams only its tile's code slots of each unit (2 KiB of the 8 KiB,
-// plus the tile's scale/bias dwords), and the W partial tiles are added in
-// LDS in wave order.  No workspace, no cross-workgroup traffic, results
-// deterministic (the order of every sum is fixed by the shapes).  The launch
-// has one workgroup per tile; the host picks W (16, 8, 4, 3 or 2 waves) so
-// that all of them are resident at once where they fit (one, two, four, five
-// or eight workgroups per CU for up to 1, 2, 4, 5 or 8 tiles per CU); with
-// more tiles than that it takes 4 waves and the rest run as a second round,
-// which its automatic choice only accepts while the weights per CU stay
-// small.
+// Here W waves own one 16-column MFMA tile of one 64-column block: they take
+// the block's K units round-robin (unit w, w + W, ...), each wave streams
+// only its tile's code slots of each unit (2 KiB of the 8 KiB, plus the
+// tile's scale/bias dwords), and the W partial tiles are added in LDS in
+// wave order.  No workspace, no cross-workgroup traffic, results
+// deterministic (the order of every sum is fixed by the shapes).  The host
+// picks W (16, 8, 4, 3 or 2 waves) so that all tiles are resident at once
+// where they fit (up to 1, 2, 4, 5 or 8 tiles per CU); with more tiles than
+// that it takes 4 waves and the rest run as a second round, which its
+// automatic choice only accepts while the weights per CU stay small.  The
+// register-staged kernel runs one tile per workgroup; the LDS-staged one
+// puts a CU's whole share of tiles in one workgroup (see there).
 //
 // The arithmetic per group is that of the stream-K kernel: exact-product bf16
 // MFMAs on the codes (8-bit codes, or 128 + q below 8 bits) and on a ones
@@ -73,7 +74,7 @@ __device__ __forceinline__ void st_global_u16(uint16_t *p, uint32_t v) {
 }
 
 // Every W runs at most four waves per SIMD (16 per CU): the plan assumes
-// floor(16 / W) workgroups per CU.
+// floor(16 / W) tiles of W waves per CU.
 //
 // The register ring of a wave's n units: requests run DEPTH - 1 units ahead
 // of the computation.  The steady-state loop issues without a condition, so
