@@ -229,12 +229,15 @@ def prefill_bench(args):
     projs = [("q", Q, H), ("k", KV, H), ("v", KV, H), ("o", H, Q), ("gate", F, H), ("up", F, H), ("down", H, F)]
     calls, ev_pairs, flops = [], [], 0
     keep = []
+    # one workspace for every projection (calls ordered on one stream): the
+    # launches with few output blocks split K through it
+    wsp = binding.alloc_workspace(max(binding.prefill_workspace_bytes(n, k, P, args.bits) for _, n, k in projs))
     for name, n, k in projs:
         c, sc, bi = inputs.make_qweight_device(n, k, args.bits, args.config, "prefill", name)
         w = binding.DeviceQWeight(n, k, args.bits, c, sc, bi)
         x = inputs.make_activations_rowmajor_device(P, k, args.config, "prefill", name)
         y = torch.empty((P, n), dtype=torch.float32, device="cuda")
-        calls.append((name, binding.prepare_qgemm_prefill(w, x, P, y)))
+        calls.append((name, binding.prepare_qgemm_prefill(w, x, P, y, wsp)))
         keep += [w, x, y, c, sc, bi]
         flops += 2 * P * n * k
     c, sc, bi = inputs.make_qweight_device(V, H, args.bits, args.config, "prefill", "head")

@@ -268,21 +268,39 @@ int dspk_qgemm_verify_grouped_noalloc(int32_t count, const dspk_tiled_weight *w,
  * Prefill projection: the same y = x . deq(W)^T for many rows at once -- a
  * prompt's tokens, the wide-row form of the pass ("mlx-dspark" wiki summary,
  * "Key techniques": a weight group dequantised once and reused for all rows).
- * Tiled for the matrix cores (128 x 128 output blocks); exact like the verify
- * projection (codes contracted exactly, fp32 accumulation, one scale/bias
- * update per group).  For a prompt's last row only, call dspk_lmhead_argmax
- * with m = 1 on that row.
+ * Tiled for the matrix cores (128 x 128 or 64 x 128 output blocks); exact
+ * like the verify projection (codes contracted exactly, fp32 accumulation,
+ * one scale/bias update per group).  For a prompt's last row only, call
+ * dspk_lmhead_argmax with m = 1 on that row.
  *
- *   w   : tiled weight (any format).
- *   x   : bf16 activations, ROW-major [m][ldx]: ldx >= k, ldx % 8 == 0,
- *         16-byte aligned.
- *   m   : rows, >= 1.
- *   y   : output [m][ldy], y_dtype (DSPK_F32 | DSPK_BF16), ldy >= n.
- * No workspace; deterministic.  Errors: DSPK_EINVAL (pointers, alignment,
- * ldx/ldy, m < 1), DSPK_EUNSUPPORTED (bits, group), DSPK_EDEVICE.
+ *   w         : tiled weight (any format).
+ *   x         : bf16 activations, ROW-major [m][ldx]: ldx >= k, ldx % 8 == 0,
+ *               16-byte aligned.
+ *   m         : rows, >= 1.
+ *   y         : output [m][ldy], y_dtype (DSPK_F32 | DSPK_BF16), ldy >= n.
+ *   workspace : NULL, or >= dspk_prefill_workspace_bytes(n, k, m, bits)
+ *               bytes, 256-byte aligned, zero-filled before its first use;
+ *               every call leaves its counters zero again, so one buffer
+ *               serves any sequence of prefill calls ordered on one stream
+ *               (calls that overlap must not share it).  With a workspace,
+ *               launches with fewer output blocks than the CUs hold at once
+ *               split K over several workgroups; the last of a block's
+ *               workgroups adds their partial sums in a fixed order.
+ * Deterministic for a given call shape and workspace choice (a K split
+ * changes the summation order, so results with and without a workspace
+ * may differ by rounding).  Errors: DSPK_EINVAL (pointers, alignment,
+ * ldx/ldy, m < 1, a workspace that is too small), DSPK_EUNSUPPORTED (bits,
+ * group), DSPK_EDEVICE.
  */
 int dspk_qgemm_prefill(const dspk_tiled_weight *w, const uint16_t *x, int64_t ldx, int32_t m,
-                       void *y, int32_t y_dtype, int64_t ldy, void *stream);
+                       void *y, int32_t y_dtype, int64_t ldy, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/* Workspace for dspk_qgemm_prefill over an n x k weight of `bits` and m
+ * rows: 0 when no launch of that shape splits K (a NULL workspace then
+ * serves), else the bytes the split needs.  It depends on the device's CU
+ * count and on dspk_set_prefill_block_rows. */
+size_t dspk_prefill_workspace_bytes(int32_t n, int32_t k, int32_t m, int32_t bits);
 
 /*
  * Row block of dspk_qgemm_prefill: 0 (initial) chooses per call between

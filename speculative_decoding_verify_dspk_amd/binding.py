@@ -97,7 +97,8 @@ def lib() -> ctypes.CDLL:
         "dspk_qgemm_verify_grouped_noalloc": (c_int32, [c_int32, P(TiledDesc), c_void_p, c_int64, c_int32,
                                                         P(c_void_p), c_int32, P(c_int64), c_void_p]),
         "dspk_qgemm_prefill": (c_int32, [P(TiledDesc), c_void_p, c_int64, c_int32, c_void_p, c_int32, c_int64,
-                                         c_void_p]),
+                                         c_void_p, c_size_t, c_void_p]),
+        "dspk_prefill_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32]),
         "dspk_lmhead_workspace_bytes": (c_size_t, [c_int32, c_int32]),
         "dspk_lmhead_argmax": (c_int32, [P(TiledDesc), c_void_p, c_int64, c_int32, c_void_p, c_void_p,
                                          c_int64, c_void_p, c_size_t, c_void_p]),
@@ -397,17 +398,24 @@ def qgemm_verify_grouped_noalloc(ws: list, x, m: int, ys: list, stream=None) -> 
                                                    _stream(stream)))
 
 
-def qgemm_prefill(w: DeviceQWeight, x, m: int, y, stream=None) -> None:
-    """x: ROW-major bf16 activations [m][ldx] (int16 bit patterns or bfloat16)."""
+def prefill_workspace_bytes(n: int, k: int, m: int, bits: int) -> int:
+    return lib().dspk_prefill_workspace_bytes(n, k, m, bits)
+
+
+def qgemm_prefill(w: DeviceQWeight, x, m: int, y, workspace=None, stream=None) -> None:
+    """x: ROW-major bf16 activations [m][ldx] (int16 bit patterns or bfloat16).
+    workspace: None, or a zero-filled buffer of prefill_workspace_bytes."""
     dt = DSPK_BF16 if y.element_size() == 2 else DSPK_F32
     _check(lib().dspk_qgemm_prefill(ctypes.byref(w.desc), x.data_ptr(), _rows(x, "x"), m, y.data_ptr(), dt,
-                                    _rows(y, "y"), _stream(stream)))
+                                    _rows(y, "y"), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                    _stream(stream)))
 
 
-def prepare_qgemm_prefill(w: DeviceQWeight, x, m: int, y, stream=None) -> Prepared:
+def prepare_qgemm_prefill(w: DeviceQWeight, x, m: int, y, workspace=None, stream=None) -> Prepared:
     dt = DSPK_BF16 if y.element_size() == 2 else DSPK_F32
     return Prepared("dspk_qgemm_prefill", ctypes.byref(w.desc), x.data_ptr(), _rows(x, "x"), m, y.data_ptr(), dt,
-                    _rows(y, "y"), _stream(stream))
+                    _rows(y, "y"), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                    _stream(stream))
 
 
 def lmhead_argmax(w: DeviceQWeight, h, m: int, argmax, logits=None, workspace=None, stream=None) -> None:

@@ -174,8 +174,14 @@ int dspk_set_prefill_block_rows(int32_t rows) {
 
 const char *dspk_last_error(void) { return g_err.c_str(); }
 
+size_t dspk_prefill_workspace_bytes(int32_t n, int32_t k, int32_t m, int32_t bits) {
+    if (n < 1 || k < 64 || k % 64 || m < 1 || !dspk::supported_bits(bits)) return 0;
+    const int32_t nst = (k + dspk::tile_k(bits) - 1) / dspk::tile_k(bits);
+    return dspk::prefill_plan(m, (n + dspk::kBlockCols - 1) / dspk::kBlockCols, nst, bits, true).ws_bytes;
+}
+
 int dspk_qgemm_prefill(const dspk_tiled_weight *w, const uint16_t *x, int64_t ldx, int32_t m, void *y,
-                       int32_t y_dtype, int64_t ldy, void *stream) {
+                       int32_t y_dtype, int64_t ldy, void *workspace, size_t workspace_bytes, void *stream) {
     const char *who = "dspk_qgemm_prefill";
     int rc = check_tiled(w, who);
     if (rc) return rc;
@@ -199,6 +205,16 @@ int dspk_qgemm_prefill(const dspk_tiled_weight *w, const uint16_t *x, int64_t ld
     A.y = y;
     A.ldy = ldy;
     A.y_bf16 = y_dtype == DSPK_BF16;
+    if (workspace != nullptr && !aligned(workspace, 256))
+        return fail(DSPK_EINVAL, "%s: workspace must be 256-byte aligned", who);
+    const dspk::PrefillPlan pl = dspk::prefill_plan(m, A.nblocks, A.nst, w->bits, workspace != nullptr);
+    if (pl.ks > 1 && workspace_bytes < pl.ws_bytes)
+        return fail(DSPK_EINVAL, "%s: workspace of %zu bytes, %zu needed (dspk_prefill_workspace_bytes)", who,
+                    workspace_bytes, pl.ws_bytes);
+    A.block_rows = pl.rows;
+    A.ks = pl.ks;
+    A.ctr = pl.ks > 1 ? (uint32_t *)workspace : nullptr;
+    A.part = pl.ks > 1 ? (float *)((char *)workspace + pl.off_part) : nullptr;
     return launch_result(dspk::launch_prefill(A, w->bits, (hipStream_t)stream), who);
 }
 

@@ -116,6 +116,10 @@ struct PrefillArgs {
     void *y;                  // [m][ldy], fp32 or bf16
     int64_t ldy;
     int32_t y_bf16;
+    int32_t block_rows;       // rows per workgroup: 64 or 128
+    int32_t ks;               // K splits; > 1 needs the two regions below
+    float *part;              // partial tiles [tile][wave][split][row tile][column tile][2][64][2]
+    uint32_t *ctr;            // arrival counters [tile][wave], zero between calls
 };
 hipError_t launch_prefill(const PrefillArgs &a, int bits, hipStream_t s);
 

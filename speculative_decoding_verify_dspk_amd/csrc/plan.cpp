@@ -174,6 +174,48 @@ int prefill_rows_for(int32_t m, int32_t nblocks, int bits) {
     return r != 0 ? r : prefill_block_rows(m, nblocks, bits, device_cus());
 }
 
+// A launch with fewer workgroups than the CUs hold at once leaves CUs idle or
+// running one workgroup alone for the whole launch (the Qwen3-4B-shaped o and
+// down projections over 2048 rows: 320 128-row workgroups for 512 slots).
+// Splitting K into ks ranges, each workgroup summing one and the last of a
+// tile's ks workgroups adding their partial tiles in split order, makes ks
+// times as many shorter workgroups.  The estimate is ceil(ks wgs / slots)
+// rounds of nst / ks units; the split with the lowest one is taken when it
+// promises at least 30% over the single partial round, and every split keeps
+// at least two units.
+int prefill_splits(int64_t wgs, int32_t nst, int occ, int cus) {
+    const int64_t slots = (int64_t)occ * cus;
+    if (wgs >= slots) return 1;
+    int best = 1;
+    int64_t best_rounds = 7, best_ks = 10;        // rounds / ks to beat: 0.7
+    for (int ks = 2; ks <= 4 && 2 * ks <= nst; ++ks) {
+        const int64_t rounds = (wgs * ks + slots - 1) / slots;
+        if (rounds * best_ks < best_rounds * ks) {
+            best = ks;
+            best_rounds = rounds;
+            best_ks = ks;
+        }
+    }
+    return best;
+}
+
+PrefillPlan prefill_plan(int32_t m, int32_t nblocks, int32_t nst, int bits, bool may_split) {
+    PrefillPlan p{};
+    p.rows = prefill_rows_for(m, nblocks, bits);
+    const int64_t tiles = ((int64_t)m + p.rows - 1) / p.rows * (((int64_t)nblocks + 1) / 2);
+    // two workgroups per CU (64 KiB of LDS, 184-256 VGPRs).  bf16 fits
+    // three at 128 rows, but its 512-workgroup q launch already runs as a
+    // full grid (65-67 us unsplit, 85 us split three ways), so it is planned
+    // as two as well
+    p.ks = may_split ? prefill_splits(tiles, nst, 2, device_cus()) : 1;
+    if (p.ks > 1) {
+        p.off_part = ((size_t)tiles * 4 * sizeof(uint32_t) + 255) / 256 * 256;
+        // per wave and split: (rows / 32) x 4 tiles of 64 lanes x 16 bytes
+        p.ws_bytes = p.off_part + (size_t)tiles * 4 * p.ks * (p.rows / 32) * 4 * 1024;
+    }
+    return p;
+}
+
 size_t tiled_bytes(int32_t n, int32_t k, int bits) {
     if (n < 1 || k < 64 || k % 64 || !supported_bits(bits)) return 0;
     const size_t nb = ((size_t)n + 63) / 64, nst = ((size_t)k + tile_k(bits) - 1) / tile_k(bits);

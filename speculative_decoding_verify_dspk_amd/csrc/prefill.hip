@@ -29,6 +29,11 @@
 // * Two workgroups per CU (64 KiB of LDS each, 32 KiB for bf16).  Row blocks
 //   vary fastest in the grid, so the workgroups that run together share their
 //   weight units in L2.
+// * With a caller's workspace, a launch with fewer output blocks than the
+//   CUs hold at once splits K into ks contiguous unit ranges (grid z): each
+//   workgroup publishes its partial block, counts itself in per wave, and the
+//   last of a block's ks arrivals adds the partials in split order and
+//   stores y, so the result does not depend on which arrives last.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -210,6 +215,27 @@ __device__ __forceinline__ void prefill_fetch_sb(const unsigned char *ub0, int u
     }
 }
 
+// K split: a lane's four partial sums of one 16 x 16 tile as two
+// device-scope 64-bit accesses, laid out [half][lane][2] (each wave-wide
+// access covers 512 contiguous bytes).  Device-scope atomic accesses reach
+// the other workgroups of the tile without a cache flush.
+__device__ __forceinline__ void part_store(float *tile, int lane, f32x4 v) {
+    unsigned long long *q = (unsigned long long *)tile;
+    const unsigned long long lo = (unsigned long long)__float_as_uint(v[0]) |
+                                  ((unsigned long long)__float_as_uint(v[1]) << 32);
+    const unsigned long long hi = (unsigned long long)__float_as_uint(v[2]) |
+                                  ((unsigned long long)__float_as_uint(v[3]) << 32);
+    __hip_atomic_store(q + lane, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 64 + lane, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x4 part_load(const float *tile, int lane) {
+    unsigned long long *q = (unsigned long long *)tile;
+    const unsigned long long lo = __hip_atomic_load(q + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long hi = __hip_atomic_load(q + 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return f32x4{__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)), __uint_as_float((uint32_t)hi),
+                 __uint_as_float((uint32_t)(hi >> 32))};
+}
+
 // Final values of this wave's 16 RT x 64 block of y.
 template <int RT>
 __device__ __forceinline__ void prefill_store(const PrefillArgs &A, int row0, int wr, int b, int c, int j,
@@ -258,7 +284,9 @@ __global__ __launch_bounds__(PT, 2) void prefill_kernel(const PrefillArgs A) {
     const int b = 2 * blockIdx.y + wc;                     // this wave's 64-column block
     const bool has_block = b < A.nblocks;
     const unsigned char *ub0 = (const unsigned char *)A.tiles + (size_t)b * A.nst * C::UNIT;
-    const int NST = A.nst;
+    // K split blockIdx.z of A.ks: units [U0, U1) of the block's A.nst
+    const int ks = A.ks, sp = blockIdx.z;
+    const int U0 = (int)((int64_t)A.nst * sp / ks), U1 = (int)((int64_t)A.nst * (sp + 1) / ks);
 
     f32x4 y[RT][4];
 #pragma unroll
@@ -268,10 +296,10 @@ __global__ __launch_bounds__(PT, 2) void prefill_kernel(const PrefillArgs A) {
 
     u32x4 wa[C::NS], wb[C::NS];                 // code sets: even units, odd units
     u32x4 s0[S::NSB], s1[S::NSB];               // scale/bias sets: with stage xs0, with xs1
-    prefill_dma_x<BITS, RT>(A, row0, 0, xs0, w, lane);
+    prefill_dma_x<BITS, RT>(A, row0, C::KU * U0, xs0, w, lane);
     if (has_block) {
-        prefill_fetch_codes<BITS>(ub0, 0, lane, wa);
-        prefill_fetch_sb<BITS>(ub0, 0, 0, c, s0);
+        prefill_fetch_codes<BITS>(ub0, U0, lane, wa);
+        prefill_fetch_sb<BITS>(ub0, U0, 0, c, s0);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -284,10 +312,10 @@ __global__ __launch_bounds__(PT, 2) void prefill_kernel(const PrefillArgs A) {
         __attribute__((always_inline)) {
         constexpr int h = decltype(hc)::value;
         const int nu = h + 1 < S::HALVES ? u : u + 1, nh = h + 1 < S::HALVES ? h + 1 : 0;
-        if (nu < NST) {
+        if (nu < U1) {
             prefill_dma_x<BITS, RT>(A, row0, C::KU * nu + S::SK * nh, nxt, w, lane);
             if (has_block) {
-                if (h == 0 && u + 1 < NST) prefill_fetch_codes<BITS>(ub0, u + 1, lane, wnxt);
+                if (h == 0 && u + 1 < U1) prefill_fetch_codes<BITS>(ub0, u + 1, lane, wnxt);
                 prefill_fetch_sb<BITS>(ub0, nu, nh, c, snxt);
             }
         }
@@ -299,27 +327,56 @@ __global__ __launch_bounds__(PT, 2) void prefill_kernel(const PrefillArgs A) {
     };
     using H0 = std::integral_constant<int, 0>;
     using H1 = std::integral_constant<int, 1>;
-    for (int u = 0; u < NST; u += 2) {
+    for (int u = U0; u < U1; u += 2) {
         if constexpr (S::HALVES == 1) {
             // one stage per unit: unit u on xs0, unit u + 1 on xs1
             stage(H0{}, u, xs0, xs1, wa, wb, s0, s1);
-            if (u + 1 < NST) stage(H0{}, u + 1, xs1, xs0, wb, wa, s1, s0);
+            if (u + 1 < U1) stage(H0{}, u + 1, xs1, xs0, wb, wa, s1, s0);
         } else {
             // two stages per unit: every unit starts on xs0
             stage(H0{}, u, xs0, xs1, wa, wb, s0, s1);
             stage(H1{}, u, xs1, xs0, wa, wb, s1, s0);
-            if (u + 1 < NST) {
+            if (u + 1 < U1) {
                 stage(H0{}, u + 1, xs0, xs1, wb, wa, s0, s1);
                 stage(H1{}, u + 1, xs1, xs0, wb, wa, s1, s0);
             }
         }
     }
-    if (has_block) prefill_store(A, row0, wr, b, c, j, y);
+    if (!has_block) return;
+    if (ks > 1) {
+        // publish this split's partial block, count in; the last of the
+        // tile's ks arrivals adds the partials in split order (so the result
+        // does not depend on the arrival order) and stores y
+        const int64_t tile = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+        constexpr int PW = RT * 4 * 256;                 // floats per wave and split
+        float *const pw = A.part + (tile * 4 + w) * ks * PW;
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) part_store(pw + sp * PW + (4 * r + t) * 256, lane, y[r][t]);
+        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0): the partials are performed
+        uint32_t *const ctr = A.ctr + tile * 4 + w;
+        uint32_t ticket = 0;
+        if (lane == 0) ticket = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ticket = __shfl(ticket, 0);
+        if (ticket != (uint32_t)(ks - 1)) return;
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                f32x4 z = sp == 0 ? y[r][t] : part_load(pw + (4 * r + t) * 256, lane);
+                for (int q = 1; q < ks; ++q) z += q == sp ? y[r][t] : part_load(pw + q * PW + (4 * r + t) * 256, lane);
+                y[r][t] = z;
+            }
+        if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    prefill_store(A, row0, wr, b, c, j, y);
 }
 
 template <int RT>
 hipError_t launch_rt(const PrefillArgs &A, int bits, hipStream_t s) {
-    const dim3 grid((unsigned)((A.m + 32 * RT - 1) / (32 * RT)), (unsigned)((A.nblocks + 1) / 2)), block(PT);
+    const dim3 grid((unsigned)((A.m + 32 * RT - 1) / (32 * RT)), (unsigned)((A.nblocks + 1) / 2), (unsigned)A.ks),
+        block(PT);
     switch (bits) {
         case 2: hipLaunchKernelGGL((prefill_kernel<2, RT>), grid, block, 0, s, A); break;
         case 3: hipLaunchKernelGGL((prefill_kernel<3, RT>), grid, block, 0, s, A); break;
@@ -333,7 +390,7 @@ hipError_t launch_rt(const PrefillArgs &A, int bits, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs &A, int bits, hipStream_t s) {
-    return prefill_rows_for(A.m, A.nblocks, bits) == 64 ? launch_rt<2>(A, bits, s) : launch_rt<4>(A, bits, s);
+    return A.block_rows == 64 ? launch_rt<2>(A, bits, s) : launch_rt<4>(A, bits, s);
 }
 
 }  // namespace dspk

@@ -17,4 +17,17 @@ int prefill_rows_for(int32_t m, int32_t nblocks, int bits);
 // setting, or -1 for another value.
 int set_prefill_block_rows(int rows);
 
+// K splits of a launch of `wgs` workgroups over nst units of K, on a device
+// of `cus` CUs holding `occ` workgroups each (planning only).
+int prefill_splits(int64_t wgs, int32_t nst, int occ, int cus);
+
+// The whole plan of one prefill call: rows per workgroup, K splits (1 unless
+// a workspace may be used) and the workspace it needs (0 for one split):
+// arrival counters at offset 0, partial tiles at off_part.
+struct PrefillPlan {
+    int rows, ks;
+    size_t off_part, ws_bytes;
+};
+PrefillPlan prefill_plan(int32_t m, int32_t nblocks, int32_t nst, int bits, bool may_split);
+
 }  // namespace dspk

@@ -33,6 +33,7 @@ static int g_fail = 0;
 static const int kCus = 256;
 
 // ------------------------------------------------------------------ recorders
+static int g_prefill_splits = 0;    // prefill launches that split K
 static uintptr_t g_ws = 0;
 static size_t g_ws_bytes = 0;
 static int g_launches = 0;
@@ -108,6 +109,19 @@ hipError_t launch_prefill(const PrefillArgs &a, int bits, hipStream_t) {
     ++g_launches;
     CHECK(supported_bits(bits) && a.m >= 1 && a.ldx >= a.k && a.ldy >= a.n);
     CHECK(a.nblocks == (a.n + 63) / 64 && a.nst == (a.k + tile_k(bits) - 1) / tile_k(bits));
+    CHECK(a.block_rows == 64 || a.block_rows == 128);
+    CHECK(a.ks >= 1 && a.ks <= 4);
+    if (a.ks > 1) {
+        // counters, then the partial tiles, inside the caller's buffer
+        const int64_t tiles = (int64_t)(a.m + a.block_rows - 1) / a.block_rows * ((a.nblocks + 1) / 2);
+        CHECK(2 * a.ks <= a.nst);
+        CHECK((uintptr_t)a.ctr == g_ws && inside(a.ctr, (size_t)tiles * 4 * 4));
+        CHECK(inside(a.part, (size_t)tiles * 4 * a.ks * (a.block_rows / 32) * 4 * 1024));
+        CHECK((uintptr_t)a.part >= (uintptr_t)a.ctr + (uintptr_t)tiles * 16 && (uintptr_t)a.part % 256 == 0);
+        ++g_prefill_splits;
+    } else {
+        CHECK(a.part == nullptr && a.ctr == nullptr);
+    }
     return hipSuccess;
 }
 hipError_t launch_pack(int32_t n, int32_t k, int bits, const void *, const uint16_t *, const uint16_t *, void *,
@@ -326,10 +340,33 @@ static void packing_and_prefill() {
         CHECK(dspk_qweight_pack(&q, fake(W), tb, nullptr) == DSPK_OK);
         expect_error(dspk_qweight_pack(&q, fake(W), tb - 1, nullptr), DSPK_EINVAL);
         dspk_tiled_weight w = tiled(130, 320, bits);
-        CHECK(dspk_qgemm_prefill(&w, (const uint16_t *)fake(X), 320, 2048, fake(Y), 0, 130, nullptr) == DSPK_OK);
-        expect_error(dspk_qgemm_prefill(&w, (const uint16_t *)fake(X), 316, 2048, fake(Y), 0, 130, nullptr),
+        CHECK(dspk_qgemm_prefill(&w, (const uint16_t *)fake(X), 320, 2048, fake(Y), 0, 130, nullptr, 0, nullptr) ==
+              DSPK_OK);
+        expect_error(dspk_qgemm_prefill(&w, (const uint16_t *)fake(X), 316, 2048, fake(Y), 0, 130, nullptr, 0, nullptr),
                      DSPK_EINVAL);
     }
+    // prefill with a workspace: shapes whose launches split K and one that
+    // does not; a short or misaligned buffer is refused
+    for (int bits : {2, 3, 4, 8, 16})
+        for (int n : {130, 2560, 9728})
+            for (int m : {1, 300, 2048}) {
+                const int k = 4096;
+                const size_t need = dspk_prefill_workspace_bytes(n, k, m, bits);
+                dspk_tiled_weight w = tiled(n, k, bits);
+                use_ws(need > 0 ? need : 256);
+                const int before = g_prefill_splits;
+                CHECK(dspk_qgemm_prefill(&w, (const uint16_t *)fake(X), k, m, fake(Y), 0, n, fake(g_ws), need,
+                                         nullptr) == DSPK_OK);
+                CHECK((g_prefill_splits > before) == (need > 0));
+                if (need > 0) {
+                    expect_error(dspk_qgemm_prefill(&w, (const uint16_t *)fake(X), k, m, fake(Y), 0, n, fake(g_ws),
+                                                    need - 1, nullptr),
+                                 DSPK_EINVAL);
+                    expect_error(dspk_qgemm_prefill(&w, (const uint16_t *)fake(X), k, m, fake(Y), 0, n,
+                                                    fake(g_ws + 16), need, nullptr),
+                                 DSPK_EINVAL);
+                }
+            }
 }
 
 // The prefill row block: Qwen3-4B-shaped projections over 2048 rows on 256
@@ -342,6 +379,19 @@ static void prefill_blocks() {
         CHECK(dspk::prefill_block_rows(1, 1, bits, 256) == 64);
         // o, down, 2560: 320 128-row workgroups load the CUs unevenly
         CHECK(dspk::prefill_block_rows(2048, 40, bits, 256) == (bits == 2 || bits == 4 ? 64 : 128));
+    }
+    // K splits: o and down (320 workgroups of 128 rows, 512 slots) three,
+    // k and v at 64 rows (256 workgroups) two, full grids none
+    CHECK(dspk::prefill_splits(320, 32, 2, 256) == 3);
+    CHECK(dspk::prefill_splits(320, 76, 2, 256) == 3);
+    CHECK(dspk::prefill_splits(256, 20, 2, 256) == 2);
+    CHECK(dspk::prefill_splits(512, 20, 2, 256) == 1);
+    CHECK(dspk::prefill_splits(1216, 20, 2, 256) == 1);
+    CHECK(dspk::prefill_splits(2, 3, 2, 256) == 1);       // too few units to split
+    for (int bits : {2, 3, 4, 8, 16}) {
+        const int32_t nst32 = 4096 / dspk::tile_k(bits);   // o: K = 4096
+        CHECK(dspk::prefill_plan(2048, 64, 2560 / dspk::tile_k(bits), bits, true).ks == 1);   // q: a full grid
+        CHECK(dspk::prefill_plan(2048, 40, nst32, bits, false).ks == 1);                // no workspace
     }
     CHECK(dspk_set_prefill_block_rows(128) == 0);
     CHECK(dspk::prefill_rows_for(2048, 16, 8) == 128);

@@ -17,7 +17,7 @@ from gpuutil import assert_rows_close, dev_u16, torch
 pytestmark = pytest.mark.gpu
 
 
-def run_prefill(w, x_bits, m, ldx=None, ldy=None, out_bf16=False, dw=None):
+def run_prefill(w, x_bits, m, ldx=None, ldy=None, out_bf16=False, dw=None, workspace=None):
     t = torch()
     dw = dw or binding.DeviceQWeight.upload(w)
     k = w.k
@@ -27,7 +27,7 @@ def run_prefill(w, x_bits, m, ldx=None, ldy=None, out_bf16=False, dw=None):
     x = dev_u16(xp)
     ldy = ldy or w.n
     y = t.full((m, ldy), -7, dtype=t.int16 if out_bf16 else t.float32, device="cuda")
-    binding.qgemm_prefill(dw, x, m, y)
+    binding.qgemm_prefill(dw, x, m, y, workspace=workspace)
     t.cuda.synchronize()
     r = y.cpu().numpy()
     assert (r[:, w.n:] == -7).all(), "columns past n were written"
@@ -114,6 +114,62 @@ def test_prefill_row_blocks_identical(bits):
     assert_rows_close(a, ref, what=f"bits={bits} row blocks")
 
 
+def _workspace(n, k, m, bits):
+    need = binding.prefill_workspace_bytes(n, k, m, bits)
+    assert need > 0, "this shape is expected to split K"
+    return binding.alloc_workspace(need)
+
+
+@pytest.mark.parametrize("bits", [8, 4, 3, 2, 16])
+@pytest.mark.parametrize("n,k,m", [(200, 1088, 300), (130, 2560, 129), (64, 1024, 1), (520, 4160, 64)])
+def test_prefill_split_k_matches_oracle(bits, n, k, m):
+    """With a workspace, launches with few output blocks split K over up to
+    four workgroups and the last arrival adds the partial blocks in split
+    order: matches the oracle, deterministic, and the counters are left
+    zero (the same buffer serves the next call)."""
+    print(f"prefill split-K bits={bits} n={n} k={k} m={m}", flush=True)
+    w = inputs.make_qweight(n, k, bits, "prefill-split", n, k)
+    x = inputs.make_activations(m, k, "prefill-split", m, k)
+    dw = binding.DeviceQWeight.upload(w)
+    ws = _workspace(n, k, m, bits)
+    a = run_prefill(w, x, m, dw=dw, workspace=ws)
+    b = run_prefill(w, x, m, dw=dw, workspace=ws)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    ref = oracle.qlinear(x, w.codes, w.scales, w.biases, bits, n, k)
+    assert_rows_close(a, ref, what=f"split-K bits={bits} n={n} k={k} m={m}")
+
+
+def test_prefill_split_k_workspace_shared_across_shapes():
+    """One zero-filled buffer, sized for the largest call, serves calls of
+    different shapes in a row (each leaves its arrival counters zero); bf16
+    output included."""
+    shapes = [(200, 1088, 300, 8), (130, 2560, 129, 4), (64, 512, 1, 16), (200, 1088, 300, 8)]
+    ws = binding.alloc_workspace(max(binding.prefill_workspace_bytes(n, k, m, b) for n, k, m, b in shapes))
+    for i, (n, k, m, bits) in enumerate(shapes):
+        w = inputs.make_qweight(n, k, bits, "prefill-share", i)
+        x = inputs.make_activations(m, k, "prefill-share", i)
+        ref = oracle.qlinear(x, w.codes, w.scales, w.biases, bits, n, k)
+        assert_rows_close(run_prefill(w, x, m, workspace=ws), ref, what=f"shared workspace call {i}")
+        got = run_prefill(w, x, m, workspace=ws, out_bf16=True)
+        assert_rows_close(got, ref, rtol=2e-3 + 2 ** -8, what=f"shared workspace call {i}, bf16 out", design=None)
+
+
+@pytest.mark.parametrize("bits,n,k", [(8, 2560, 4096), (16, 2560, 9728), (3, 2560, 4096)])
+def test_prefill_split_k_full_shape_sampled_rows(bits, n, k):
+    """Qwen3-4B o and down projections over 2048 rows with a workspace: 320
+    output blocks, K split three ways (two for bf16); the oracle recomputes
+    sampled rows."""
+    m = 2048
+    print(f"prefill split-K full shape bits={bits} n={n} k={k}", flush=True)
+    w = inputs.make_qweight(n, k, bits, "prefill-split-full")
+    x = inputs.make_activations(m, k, "prefill-split-full")
+    got = run_prefill(w, x, m, workspace=_workspace(n, k, m, bits))
+    rows = np.unique(np.concatenate([[0, 127, 128, m - 1], np.random.default_rng(5).integers(0, m, 8)]))
+    ref = oracle.qlinear(x[rows], w.codes, w.scales, w.biases, bits, n, k)
+    assert_rows_close(got[rows], ref, what=f"split-K bits={bits} sampled rows")
+    assert np.isfinite(got).all()
+
+
 def test_prefill_rejects_bad_arguments():
     t = torch()
     w = inputs.make_qweight(64, 128, 8, "prefill-bad")
@@ -126,3 +182,11 @@ def test_prefill_rejects_bad_arguments():
         binding.qgemm_prefill(dw, t.zeros((4, 120), dtype=t.int16, device="cuda"), 4, y)   # ldx < k
     with pytest.raises(binding.DspkError):
         binding.qgemm_prefill(dw, t.zeros((4, 132), dtype=t.int16, device="cuda"), 4, y)   # ldx % 8
+    # a workspace shorter than the K split needs
+    w2 = inputs.make_qweight(64, 1024, 8, "prefill-bad-ws")
+    dw2 = binding.DeviceQWeight.upload(w2)
+    x2 = t.zeros((4, 1024), dtype=t.int16, device="cuda")
+    need = binding.prefill_workspace_bytes(64, 1024, 4, 8)
+    assert need > 0
+    with pytest.raises(binding.DspkError):
+        binding.qgemm_prefill(dw2, x2, 4, y, workspace=binding.alloc_workspace(need)[: need - 1])
