@@ -182,13 +182,16 @@ int prefill_rows_for(int32_t m, int32_t nblocks, int bits) {
 // times as many shorter workgroups.  The estimate is ceil(ks wgs / slots)
 // rounds of nst / ks units; the split with the lowest one is taken when it
 // promises at least 30% over the single partial round, and every split keeps
-// at least two units.
+// at least eight units (shorter ones did not pay for their pipeline start
+// and exchange: the 4-bit o projection, 16 units, 91-93 us as 64-row blocks
+// against 97-98 us as 128-row blocks split three ways; the 4-bit k and v,
+// 10 units, 32-33 us either way).
 int prefill_splits(int64_t wgs, int32_t nst, int occ, int cus) {
     const int64_t slots = (int64_t)occ * cus;
     if (wgs >= slots) return 1;
     int best = 1;
     int64_t best_rounds = 7, best_ks = 10;        // rounds / ks to beat: 0.7
-    for (int ks = 2; ks <= 4 && 2 * ks <= nst; ++ks) {
+    for (int ks = 2; ks <= 4 && 8 * ks <= nst; ++ks) {
         const int64_t rounds = (wgs * ks + slots - 1) / slots;
         if (rounds * best_ks < best_rounds * ks) {
             best = ks;
@@ -202,14 +205,29 @@ int prefill_splits(int64_t wgs, int32_t nst, int occ, int cus) {
 PrefillPlan prefill_plan(int32_t m, int32_t nblocks, int32_t nst, int bits, bool may_split) {
     PrefillPlan p{};
     p.rows = prefill_rows_for(m, nblocks, bits);
+    // With a workspace, a 128-row grid that covers the CUs but not two per CU
+    // splits K rather than halving the rows, where the split pays: the 2- and
+    // 4-bit down projections (320 128-row blocks, 38 units) 200-202 -> 184-186
+    // us.  Grids that do not cover the CUs keep 64-row blocks (k and v: 35-37
+    // us at 64 rows, 49-54 us split four ways at 128).
+    const int cus = device_cus();
+    if (may_split && g_prefill_rows.load(std::memory_order_relaxed) == 0) {
+        const int64_t w128 = ((int64_t)m + 127) / 128 * (((int64_t)nblocks + 1) / 2);
+        if (w128 > cus && w128 < 2 * (int64_t)cus && prefill_splits(w128, nst, 2, cus) > 1) p.rows = 128;
+    }
     const int64_t tiles = ((int64_t)m + p.rows - 1) / p.rows * (((int64_t)nblocks + 1) / 2);
     // two workgroups per CU (64 KiB of LDS, 184-256 VGPRs).  bf16 fits
     // three at 128 rows, but its 512-workgroup q launch already runs as a
     // full grid (65-67 us unsplit, 85 us split three ways), so it is planned
     // as two as well
-    p.ks = may_split ? prefill_splits(tiles, nst, 2, device_cus()) : 1;
+    p.ks = may_split ? prefill_splits(tiles, nst, 2, cus) : 1;
     if (p.ks > 1) {
-        p.off_part = ((size_t)tiles * 4 * sizeof(uint32_t) + 255) / 256 * 256;
+        // the counters of the largest launch that splits (fewer than two
+        // blocks per CU, four waves each) at a fixed place, so that calls
+        // of any shape sharing one buffer find them zero: a region sized
+        // by this call's blocks would overlap the partials of a call with
+        // fewer blocks
+        p.off_part = ((size_t)2 * cus * 4 * sizeof(uint32_t) + 255) / 256 * 256;
         // per wave and split: (rows / 32) x 4 tiles of 64 lanes x 16 bytes
         p.ws_bytes = p.off_part + (size_t)tiles * 4 * p.ks * (p.rows / 32) * 4 * 1024;
     }

@@ -118,6 +118,8 @@ hipError_t launch_prefill(const PrefillArgs &a, int bits, hipStream_t) {
         CHECK((uintptr_t)a.ctr == g_ws && inside(a.ctr, (size_t)tiles * 4 * 4));
         CHECK(inside(a.part, (size_t)tiles * 4 * a.ks * (a.block_rows / 32) * 4 * 1024));
         CHECK((uintptr_t)a.part >= (uintptr_t)a.ctr + (uintptr_t)tiles * 16 && (uintptr_t)a.part % 256 == 0);
+        // the partials start at a place that does not depend on the call
+        CHECK((uintptr_t)a.part == g_ws + (2 * kCus * 16 + 255) / 256 * 256);
         ++g_prefill_splits;
     } else {
         CHECK(a.part == nullptr && a.ctr == nullptr);
@@ -387,11 +389,25 @@ static void prefill_blocks() {
     CHECK(dspk::prefill_splits(256, 20, 2, 256) == 2);
     CHECK(dspk::prefill_splits(512, 20, 2, 256) == 1);
     CHECK(dspk::prefill_splits(1216, 20, 2, 256) == 1);
-    CHECK(dspk::prefill_splits(2, 3, 2, 256) == 1);       // too few units to split
+    CHECK(dspk::prefill_splits(256, 10, 2, 256) == 1);    // 4-bit k/v: splits would be under 8 units
+    CHECK(dspk::prefill_splits(320, 16, 2, 256) == 1);    // 4-bit o at 128 rows: likewise
+    CHECK(dspk::prefill_splits(320, 38, 2, 256) == 3);    // 4-bit down
     for (int bits : {2, 3, 4, 8, 16}) {
-        const int32_t nst32 = 4096 / dspk::tile_k(bits);   // o: K = 4096
-        CHECK(dspk::prefill_plan(2048, 64, 2560 / dspk::tile_k(bits), bits, true).ks == 1);   // q: a full grid
-        CHECK(dspk::prefill_plan(2048, 40, nst32, bits, false).ks == 1);                // no workspace
+        const int32_t ku = dspk::tile_k(bits);
+        CHECK(dspk::prefill_plan(2048, 64, 2560 / ku, bits, true).ks == 1);      // q: a full grid
+        CHECK(dspk::prefill_plan(2048, 40, 4096 / ku, bits, false).ks == 1);     // no workspace
+        // down with a workspace: 128-row blocks, K split three ways
+        const dspk::PrefillPlan pd = dspk::prefill_plan(2048, 40, 9728 / ku, bits, true);
+        CHECK(pd.rows == 128 && pd.ks == 3 && pd.ws_bytes > pd.off_part);
+        // o and k/v: split where each split keeps 8 units (8-bit and bf16)
+        const dspk::PrefillPlan po = dspk::prefill_plan(2048, 40, 4096 / ku, bits, true);
+        const dspk::PrefillPlan pk = dspk::prefill_plan(2048, 16, 2560 / ku, bits, true);
+        if (bits >= 8) {
+            CHECK(po.rows == 128 && po.ks == 3);
+            CHECK(pk.rows == 64 && pk.ks == 2);
+        } else {
+            CHECK(po.ks == 1 && pk.ks == 1 && pk.rows == 64);
+        }
     }
     CHECK(dspk_set_prefill_block_rows(128) == 0);
     CHECK(dspk::prefill_rows_for(2048, 16, 8) == 128);

@@ -121,7 +121,7 @@ def _workspace(n, k, m, bits):
 
 
 @pytest.mark.parametrize("bits", [8, 4, 3, 2, 16])
-@pytest.mark.parametrize("n,k,m", [(200, 1088, 300), (130, 2560, 129), (64, 1024, 1), (520, 4160, 64)])
+@pytest.mark.parametrize("n,k,m", [(200, 4160, 300), (130, 4096, 129), (64, 4096, 1), (520, 8256, 64)])
 def test_prefill_split_k_matches_oracle(bits, n, k, m):
     """With a workspace, launches with few output blocks split K over up to
     four workgroups and the last arrival adds the partial blocks in split
@@ -143,7 +143,7 @@ def test_prefill_split_k_workspace_shared_across_shapes():
     """One zero-filled buffer, sized for the largest call, serves calls of
     different shapes in a row (each leaves its arrival counters zero); bf16
     output included."""
-    shapes = [(200, 1088, 300, 8), (130, 2560, 129, 4), (64, 512, 1, 16), (200, 1088, 300, 8)]
+    shapes = [(200, 2176, 300, 8), (130, 4096, 129, 4), (64, 1024, 1, 16), (200, 2176, 300, 8)]
     ws = binding.alloc_workspace(max(binding.prefill_workspace_bytes(n, k, m, b) for n, k, m, b in shapes))
     for i, (n, k, m, bits) in enumerate(shapes):
         w = inputs.make_qweight(n, k, bits, "prefill-share", i)
@@ -154,11 +154,27 @@ def test_prefill_split_k_workspace_shared_across_shapes():
         assert_rows_close(got, ref, rtol=2e-3 + 2 ** -8, what=f"shared workspace call {i}, bf16 out", design=None)
 
 
-@pytest.mark.parametrize("bits,n,k", [(8, 2560, 4096), (16, 2560, 9728), (3, 2560, 4096)])
+def test_prefill_split_k_counters_stay_put_across_block_counts():
+    """Calls of 40, 60 and again 40 split output blocks share one buffer:
+    the arrival counters sit at a place that does not depend on the call,
+    so a call with more blocks never counts on the partial sums an earlier
+    call with fewer blocks left behind (a counter region sized per call
+    overlapped them)."""
+    k, m, bits = 2176, 300, 8
+    ns = (1000, 1500, 1000)
+    ws = binding.alloc_workspace(max(binding.prefill_workspace_bytes(n, k, m, bits) for n in ns))
+    for i, n in enumerate(ns):
+        w = inputs.make_qweight(n, k, bits, "prefill-ctr", n)
+        x = inputs.make_activations(m, k, "prefill-ctr", i)
+        ref = oracle.qlinear(x, w.codes, w.scales, w.biases, bits, n, k)
+        assert_rows_close(run_prefill(w, x, m, workspace=ws), ref, what=f"call {i} (n={n})")
+
+
+@pytest.mark.parametrize("bits,n,k", [(8, 2560, 4096), (16, 2560, 9728), (3, 2560, 9728), (4, 2560, 9728)])
 def test_prefill_split_k_full_shape_sampled_rows(bits, n, k):
     """Qwen3-4B o and down projections over 2048 rows with a workspace: 320
-    output blocks, K split three ways (two for bf16); the oracle recomputes
-    sampled rows."""
+    128-row output blocks, K split three ways; the oracle recomputes sampled
+    rows."""
     m = 2048
     print(f"prefill split-K full shape bits={bits} n={n} k={k}", flush=True)
     w = inputs.make_qweight(n, k, bits, "prefill-split-full")
@@ -183,10 +199,10 @@ def test_prefill_rejects_bad_arguments():
     with pytest.raises(binding.DspkError):
         binding.qgemm_prefill(dw, t.zeros((4, 132), dtype=t.int16, device="cuda"), 4, y)   # ldx % 8
     # a workspace shorter than the K split needs
-    w2 = inputs.make_qweight(64, 1024, 8, "prefill-bad-ws")
+    w2 = inputs.make_qweight(64, 2048, 8, "prefill-bad-ws")
     dw2 = binding.DeviceQWeight.upload(w2)
-    x2 = t.zeros((4, 1024), dtype=t.int16, device="cuda")
-    need = binding.prefill_workspace_bytes(64, 1024, 4, 8)
+    x2 = t.zeros((4, 2048), dtype=t.int16, device="cuda")
+    need = binding.prefill_workspace_bytes(64, 2048, 4, 8)
     assert need > 0
     with pytest.raises(binding.DspkError):
         binding.qgemm_prefill(dw2, x2, 4, y, workspace=binding.alloc_workspace(need)[: need - 1])
