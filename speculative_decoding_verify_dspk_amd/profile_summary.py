@@ -59,13 +59,14 @@ def stats(stats_csv: str, trace_csv: str, out: str, cmd: str) -> None:
     per = collections.defaultdict(list)
     for r in csv.DictReader(open(trace_csv)):
         if "qgemm" in r["Kernel_Name"] or "prefill_kernel" in r["Kernel_Name"]:
-            per[(short(r["Kernel_Name"]), r["Grid_Size_X"], r.get("Grid_Size_Y", "1"))].append(
-                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    lines += ["", "Projection launches by grid (threads in x, workgroups in y; 256 threads per workgroup):", "",
-              "| kernel | grid x | grid y | launches | median us |", "|---|---|---|---|---|"]
-    for (k, gx, gy), v in sorted(per.items()):
+            per[(short(r["Kernel_Name"]), r["Grid_Size_X"], r.get("Grid_Size_Y", "1"),
+                 r.get("Grid_Size_Z", "1"))].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines += ["", "Projection launches by grid (threads in x, workgroups in y and z; the prefill kernel's z is "
+              "its K split):", "",
+              "| kernel | grid x | grid y | grid z | launches | median us |", "|---|---|---|---|---|---|"]
+    for (k, gx, gy, gz), v in sorted(per.items()):
         v.sort()
-        lines.append(f"| {k} | {gx} | {gy} | {len(v)} | {v[len(v) // 2]:.1f} |")
+        lines.append(f"| {k} | {gx} | {gy} | {gz} | {len(v)} | {v[len(v) // 2]:.1f} |")
     open(out, "w").write("\n".join(lines) + "\n")
 
 
